@@ -1,0 +1,361 @@
+"""Benchmark of the TQ4_1S decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extended]
+
+A *step* is one batch-1 decode pass over a Llama-3-8B-shaped model stored in
+TQ4_1S: for each of the 32 layers and each activation group (q|k|v, o,
+gate|up, down) the activation is rotated once (tq_rotate) and the fused GEMV
+(tq_gemv) streams that group's packed weights from HBM.  ``value`` is the
+whole step's algorithmic bytes (0.625 B per weight + activations + outputs)
+divided by the step time, with every input already resident in HBM.
+
+The same run also measures, outside the timed step: the quantizer over the
+whole model, the small-batch GEMM at M in {1, 4, 16, 32, 64}, dequantization,
+and NVFP4 / MXFP6 quantize + GEMV on 27B-shaped layers (a few layers by
+default, all 64 plus the 70B quantize with --extended).  ``roofline``
+reports the fused GEMV kernel alone (per-launch HIP event pairs on the
+launch stream); ``cpu_baseline`` times the CPU oracle on a bounded sample.
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+WEIGHT_BYTES_PER_ELEM = 0.625      # 16 B nibbles + 4 B fp16 scales per 32 weights
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extended", action="store_true", help="all 64 27B layers and the 80-layer 70B quantize")
+    ap.add_argument("--fused-rotation", action="store_true", help="rotate inside the GEMV instead of tq_rotate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def gemv_bytes(n, k):
+    return WEIGHT_BYTES_PER_ELEM * n * k + 4 * k + 4 * n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
+                                   "multi-GPU sharding is described in the design notes but not built"}))
+        sys.exit(2)
+
+    import torch
+    import dequant_gemv_tq_amd as tqa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ setup
+    groups = wl.LLAMA8B_GROUPS                       # name -> (N, K)
+    members = {"qkv": ["q", "k", "v"], "o": ["o"], "gate_up": ["gate", "up"], "down": ["down"]}
+    L = wl.LLAMA8B_LAYERS
+    model = []                                        # per layer: name -> (packed, scales)
+    xs = []                                           # per layer: name -> bf16 activation
+    q_bytes = 0.0
+    q_ms = 0.0
+    for layer in range(L):
+        variant = wl.layer_variant(layer)
+        entry = {}
+        for gname, (n, k) in groups.items():
+            W = torch.cat([wl.llama8b_weight(t, layer, dev, variant) for t in members[gname]], dim=0)
+            assert W.shape == (n, k)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            packed, scales = tqa.quantize(W)
+            e1.record(stream)
+            e1.synchronize()
+            q_ms += e0.elapsed_time(e1)
+            q_bytes += (2.0 + WEIGHT_BYTES_PER_ELEM) * n * k
+            entry[gname] = (packed, scales)
+            del W
+        model.append(entry)
+        g = wl.generator(wl.seed_of(2, layer, 50), dev)
+        xs.append({gname: wl.activation(1, k, g, dev, torch.bfloat16)[0].contiguous()
+                   for gname, (n, k) in groups.items()})
+    torch.cuda.synchronize()
+    xr_buf = {gname: torch.empty(k, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
+    y_buf = {gname: torch.empty(n, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
+
+    step_bytes = 0.0
+    for gname, (n, k) in groups.items():
+        step_bytes += L * (gemv_bytes(n, k) + (0 if args.fused_rotation else 6 * k))
+
+    def step(events=None):
+        for layer in range(L):
+            for gname in groups:
+                packed, scales = model[layer][gname]
+                x = xs[layer][gname]
+                if args.fused_rotation:
+                    if events is not None:
+                        events.append((gname, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                        events[-1][1].record(stream)
+                    tqa.gemv(packed, scales, x, out=y_buf[gname])
+                else:
+                    xr = tqa.rotate(x, out=xr_buf[gname])
+                    if events is not None:
+                        events.append((gname, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                        events[-1][1].record(stream)
+                    tqa.gemv(packed, scales, xr, rotated=True, out=y_buf[gname])
+                if events is not None:
+                    events[-1][2].record(stream)
+
+    # --------------------------------------------------------------- timed
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ------------------------------------------------- per-launch GEMV timing
+    per = {g: [] for g in groups}
+    for _ in range(3):
+        ev = []
+        step(ev)
+        torch.cuda.synchronize()
+        for gname, a, b in ev:
+            per[gname].append(a.elapsed_time(b))
+    gemv_launch_bytes = 0.0
+    gemv_launch_ms = 0.0
+    per_group = {}
+    for gname, (n, k) in groups.items():
+        ms = sum(per[gname]) / len(per[gname])
+        per_group[gname] = {"N": n, "K": k, "us": round(ms * 1e3, 2),
+                            "GB_s": round(gemv_bytes(n, k) / (ms * 1e-3) / 1e9, 1)}
+        gemv_launch_bytes += gemv_bytes(n, k)
+        gemv_launch_ms += ms
+    achieved = gemv_launch_bytes / (gemv_launch_ms * 1e-3) / 1e9
+    layer_kernel_ms = gemv_launch_ms          # the four group launches of one layer
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "gemv_kernel (fused TQ4_1S GEMV)", "launches_per_step": 4 * L,
+                "bytes_per_launch_avg": round(gemv_launch_bytes / 4), "avg_launch_us": round(gemv_launch_ms / 4 * 1e3, 2)}
+
+    out = {
+        "metric": "fused TQ4_1S GEMV achieved HBM GB/s (% of peak) at batch 1; quantize GB/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "Llama-3-8B-shaped 32-layer batch-1 decode, TQ4_1S weights, fused GEMV stream",
+                   "layers": L, "groups": {g: list(v) for g, v in groups.items()},
+                   "weights": "bf16 N(0,1/K) even layers, Student-t(4) odd layers, quantized on device",
+                   "activation": "bf16 [K] N(0,1), rotated once per group",
+                   "rotation": "fused in GEMV" if args.fused_rotation else "tq_rotate + tq_gemv",
+                   "step_bytes": int(step_bytes)},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "tokens_equiv_layers_per_s": round(1e3 / layer_kernel_ms, 1),
+        "tokens_per_s_32_layers": round(1e3 / ms_per_step, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "per_group": per_group,
+        "quantize": {"GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms_total": round(q_ms, 3),
+                     "weights": int(q_bytes / (2.0 + WEIGHT_BYTES_PER_ELEM)),
+                     "bytes": "2 B bf16 in + 0.625 B out per weight"},
+    }
+
+    # ----------------------------------------------------- secondary rows
+    out["gemm"] = bench_gemm(torch, tqa, wl, model, groups, dev, stream)
+    out["dequantize"] = bench_dequant(torch, tqa, model, groups, dev, stream)
+    out["blockfp"] = bench_blockfp(torch, tqa, wl, dev, stream, layers=64 if args.extended else 4)
+    if args.extended:
+        del model, xs
+        torch.cuda.empty_cache()
+        out["llama70b"] = bench_70b(torch, tqa, wl, dev, stream)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(model, groups, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _time(torch, stream, fn, reps):
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def bench_gemm(torch, tqa, wl, model, groups, dev, stream):
+    """Small-batch GEMM over the 32-layer stream (bf16 pre-rotated activations)."""
+    res = {}
+    L = len(model)
+    for m in (1, 4, 16, 32, 64):
+        xr = {}
+        for gi, (gname, (n, k)) in enumerate(groups.items()):
+            g = wl.generator(wl.seed_of(3, m, gi), dev)
+            X = wl.activation(m, k, g, dev, torch.bfloat16)
+            xr[gname] = tqa.rotate(X, dtype=torch.bfloat16)
+        ys = {gname: torch.empty((m, n), dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
+
+        def run():
+            for layer in range(L):
+                for gname in groups:
+                    p, s = model[layer][gname]
+                    tqa.gemm(p, s, xr[gname], out=ys[gname])
+
+        ms = _time(torch, stream, run, 3)
+        byts = sum(L * (WEIGHT_BYTES_PER_ELEM * n * k + 2 * m * k + 4 * m * n) for n, k in groups.values())
+        flops = sum(L * 2.0 * m * n * k for n, k in groups.values())
+        res[f"M{m}"] = {"ms_32_layers": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
+                        "TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 2),
+                        "path": "VALU fp32" if m < 16 else "MFMA bf16"}
+    return res
+
+
+def bench_dequant(torch, tqa, model, groups, dev, stream):
+    n, k = groups["gate_up"]
+    p, s = model[0]["gate_up"]
+    out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    ms = _time(torch, stream, lambda: tqa.dequantize(p, s, dtype=torch.bfloat16, out=out), 5)
+    byts = (WEIGHT_BYTES_PER_ELEM + 2.0) * n * k
+    return {"shape": [n, k], "out": "bf16", "us": round(ms * 1e3, 1), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1)}
+
+
+def bench_blockfp(torch, tqa, wl, dev, stream, layers):
+    """27B-shaped layers: per-tensor NVFP4 or MXFP6 (seeded, ~10% MXFP6); quantize and GEMV at M = 1, 8."""
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    store = []
+    q_ms = 0.0
+    q_bytes = 0.0
+    fmt_count = {"nvfp4": 0, "mxfp6": 0}
+    for layer in range(layers):
+        for t in names:
+            fmt = wl.qwen27b_format(layer, t)
+            fmt_count[fmt] += 1
+            W = wl.qwen27b_weight(t, layer, dev)
+            n, k = W.shape
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            codes, bs, ts = tqa.blockfp_quantize(fmt, W)
+            b.record(stream)
+            b.synchronize()
+            q_ms += a.elapsed_time(b)
+            reads = 2 if fmt == "nvfp4" else 1          # NVFP4 reads W twice (amax, encode)
+            q_bytes += (2.0 * reads + (0.5625 if fmt == "nvfp4" else 0.78125)) * n * k
+            store.append((fmt, codes, bs, ts, n, k))
+            del W
+    res = {"layers": layers, "tensors": fmt_count, "quantize_GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}
+    for m in (1, 8):
+        xsv = {}
+        for (fmt, codes, bs, ts, n, k) in store:
+            if k not in xsv:
+                g = wl.generator(wl.seed_of(4, m, k), dev)
+                xsv[k] = wl.activation(m, k, g, dev, torch.bfloat16)
+        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for (_, _, _, _, n, _) in store]
+
+        def run():
+            for i, (fmt, codes, bs, ts, n, k) in enumerate(store):
+                tqa.blockfp_gemm(fmt, codes, bs, ts, xsv[k], out=ys[i])
+
+        ms = _time(torch, stream, run, 3)
+        byts = sum(((0.5625 if f == "nvfp4" else 0.78125) * n * k + 2 * m * k + 4 * m * n)
+                   for (f, _, _, _, n, k) in store)
+        res[f"gemv_M{m}"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1)}
+    return res
+
+
+def bench_70b(torch, tqa, wl, dev, stream):
+    """Full 80-layer 70B-shaped quantize (generated one tensor at a time) and the FFN-trio GEMV."""
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    q_ms, weights = 0.0, 0
+    keep = None
+    for layer in range(wl.LLAMA70B_LAYERS):
+        for t in names:
+            W = wl.llama70b_weight(t, layer, dev)
+            n, k = W.shape
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            p, s = tqa.quantize(W)
+            b.record(stream)
+            b.synchronize()
+            q_ms += a.elapsed_time(b)
+            weights += n * k
+            if layer == 0 and t in ("gate", "up", "down"):
+                keep = (keep or {})
+                keep[t] = (p, s, n, k)
+            del W, p, s
+    res = {"weights": weights, "quantize_ms": round(q_ms, 1),
+           "quantize_GB_s": round((2.0 + WEIGHT_BYTES_PER_ELEM) * weights / (q_ms * 1e-3) / 1e9, 1)}
+    xr = {}
+    for t, (p, s, n, k) in keep.items():
+        g = wl.generator(wl.seed_of(5, 0, 77), dev)
+        xr[t] = tqa.rotate(wl.activation(1, k, g, dev, torch.bfloat16)[0].contiguous())
+    ys = {t: torch.empty(n, dtype=torch.float32, device=dev) for t, (p, s, n, k) in keep.items()}
+
+    def run():
+        for t, (p, s, n, k) in keep.items():
+            tqa.gemv(p, s, xr[t], rotated=True, out=ys[t])
+
+    ms = _time(torch, stream, run, 10)
+    byts = sum(gemv_bytes(n, k) for (p, s, n, k) in keep.values())
+    res["ffn_trio_gemv"] = {"packed_GB": round(sum(WEIGHT_BYTES_PER_ELEM * n * k for (_, _, n, k) in keep.values()) / 1e9, 3),
+                            "us": round(ms * 1e3, 1), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1)}
+    return res
+
+
+def cpu_baseline(model, groups, seconds):
+    """The CPU oracle's float64 GEMV on sampled rows of the same packed weights, scaled to GB/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import tq4_1s as otq
+
+    rows = 256
+    samples = []
+    for it, gname in enumerate(list(groups) * 2):
+        n, k = groups[gname]
+        p, s = model[it % len(model)][gname]
+        r0 = (it * 997) % (n - rows)
+        x = np.random.default_rng(it).standard_normal(k).astype(np.float32)
+        samples.append((p[r0:r0 + rows].cpu().numpy(), s[r0:r0 + rows].cpu().numpy().view(np.uint16), x, k))
+    done_bytes = 0.0
+    elapsed = 0.0
+    it = 0
+    while elapsed < seconds:
+        pk, sc, x, k = samples[it % len(samples)]
+        t = time.perf_counter()
+        otq.gemv_rows_o64(pk, sc, x)
+        elapsed += time.perf_counter() - t
+        done_bytes += gemv_bytes(rows, k)
+        it += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{it} oracle float64 GEMV calls on {rows}-row slices of the 8B decode groups "
+                      f"(q|k|v, o, gate|up, down; {elapsed:.1f} s of oracle time)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

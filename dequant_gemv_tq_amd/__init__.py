@@ -1,0 +1,245 @@
+"""Python binding of libtq (include/tq.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of ``libtq.so``; this module checks
+tensors, allocates outputs with torch (device memory and streams are the only
+things torch provides here) and passes raw pointers plus torch's current HIP
+stream to the C ABI.  There is no CPU fallback: if the library is not built
+or a tensor is not on the GPU, the call raises.
+
+The names follow the C ABI: quantize, dequantize, rotate, gemv, gemm,
+blockfp_quantize, blockfp_gemm, codebook, sign_mask_from_seed.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported before libtq so both bind to the same HIP runtime
+
+__all__ = [
+    "TQError", "lib", "codebook", "sign_mask_from_seed", "DEFAULT_SIGN_MASK",
+    "quantize", "dequantize", "rotate", "gemv", "gemm",
+    "blockfp_quantize", "blockfp_gemm", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+FORMATS = {"nvfp4": 1, "mxfp6": 2}
+_STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EALIGN", 4: "TQ_EDTYPE", 5: "TQ_EDEVICE"}
+
+EXPORTED = [
+    "tq_abi_version", "tq_status_str", "tq_codebook", "tq_sign_mask_from_seed", "tq_default_sign_mask",
+    "tq_quantize", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
+    "tq_blockfp_quantize", "tq_blockfp_gemm",
+]
+
+
+class TQError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dequant_gemv_tq_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, u32, p, c_int = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    L.tq_abi_version.restype = c_int
+    L.tq_status_str.restype = ctypes.c_char_p
+    L.tq_status_str.argtypes = [c_int]
+    L.tq_codebook.restype = c_int
+    L.tq_codebook.argtypes = [p, p]
+    L.tq_sign_mask_from_seed.restype = u32
+    L.tq_sign_mask_from_seed.argtypes = [ctypes.c_uint64]
+    L.tq_default_sign_mask.restype = u32
+    L.tq_quantize.argtypes = [p, c_int, i64, i64, i64, u32, p, p, p]
+    L.tq_dequantize.argtypes = [p, p, i64, i64, u32, p, c_int, i64, p]
+    L.tq_rotate.argtypes = [p, c_int, i64, i64, i64, u32, p, c_int, i64, p]
+    L.tq_gemv.argtypes = [p, p, i64, i64, u32, p, c_int, c_int, p, p]
+    L.tq_gemm.argtypes = [p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
+    L.tq_blockfp_quantize.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p]
+    L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
+    for name in ("tq_quantize", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
+                 "tq_blockfp_quantize", "tq_blockfp_gemm"):
+        getattr(L, name).restype = c_int
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TQError(fn, status, lib().tq_status_str(status).decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU fallback)")
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ----------------------------------------------------------------------------
+# host constants
+# ----------------------------------------------------------------------------
+
+def codebook():
+    """(centroids float32[16], thresholds float32[15]) as the kernels use them."""
+    import numpy as np
+    c = (ctypes.c_float * 16)()
+    m = (ctypes.c_float * 15)()
+    _check("tq_codebook", lib().tq_codebook(c, m))
+    return np.frombuffer(c, dtype=np.float32).copy(), np.frombuffer(m, dtype=np.float32).copy()
+
+
+def sign_mask_from_seed(seed: int) -> int:
+    return int(lib().tq_sign_mask_from_seed(seed))
+
+
+def default_sign_mask() -> int:
+    return int(lib().tq_default_sign_mask())
+
+
+DEFAULT_SIGN_MASK = 0x7B1DCDAF
+
+
+# ----------------------------------------------------------------------------
+# TQ4_1S
+# ----------------------------------------------------------------------------
+
+def quantize(W: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None):
+    """W [N, K] (fp32/bf16, row stride may exceed K) -> (packed uint8 [N, K/2], scales int16 [N, K/16]).
+
+    ``scales`` holds the fp16 bit patterns of d0, d1 per block (view as float16).
+    """
+    _dev(W, "W")
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be a 2-D tensor with unit column stride")
+    N, K = W.shape
+    if out is None:
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        scales = torch.empty((N, K // 16), dtype=torch.int16, device=W.device)
+    else:
+        packed, scales = out
+    st = lib().tq_quantize(_ptr(W), _dtype_code(W, "W"), N, K, W.stride(0), sign_mask & 0xFFFFFFFF,
+                           _ptr(packed), _ptr(scales), _stream())
+    _check("tq_quantize", st)
+    return packed, scales
+
+
+def dequantize(packed: torch.Tensor, scales: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK,
+               dtype=torch.float32, out=None):
+    _dev(packed, "packed")
+    N, K = packed.shape[0], packed.shape[1] * 2
+    W = torch.empty((N, K), dtype=dtype, device=packed.device) if out is None else out
+    st = lib().tq_dequantize(_ptr(packed), _ptr(scales), N, K, sign_mask & 0xFFFFFFFF, _ptr(W),
+                             _dtype_code(W, "out"), W.stride(0), _stream())
+    _check("tq_dequantize", st)
+    return W
+
+
+def rotate(x: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, dtype=torch.float32, out=None):
+    """x [M, K] or [K] -> x' of the same shape (dtype fp32 or bf16)."""
+    _dev(x, "x")
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    M, K = x2.shape
+    xr = torch.empty((M, K), dtype=dtype, device=x.device) if out is None else out.reshape(M, K)
+    st = lib().tq_rotate(_ptr(x2), _dtype_code(x2, "x"), M, K, x2.stride(0), sign_mask & 0xFFFFFFFF,
+                         _ptr(xr), _dtype_code(xr, "out"), xr.stride(0), _stream())
+    _check("tq_rotate", st)
+    return xr if x.dim() == 2 else xr.reshape(-1)
+
+
+def gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, rotated: bool = False,
+         sign_mask: int = DEFAULT_SIGN_MASK, out=None):
+    """y [N] float32 = W_deq x.  x: [K] raw (fp32/bf16) or, with rotated=True, x' fp32."""
+    _dev(packed, "packed")
+    _dev(x, "x")
+    N, K = packed.shape[0], packed.shape[1] * 2
+    if x.numel() != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous vector of length K")
+    y = torch.empty(N, dtype=torch.float32, device=packed.device) if out is None else out
+    st = lib().tq_gemv(_ptr(packed), _ptr(scales), N, K, sign_mask & 0xFFFFFFFF, _ptr(x), _dtype_code(x, "x"),
+                       1 if rotated else 0, _ptr(y), _stream())
+    _check("tq_gemv", st)
+    return y
+
+
+def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=None):
+    """Y [M, N] float32 = X' Q^T with pre-rotated activations x_rot [M, K] (bf16, or fp32 for M < 16)."""
+    _dev(packed, "packed")
+    _dev(x_rot, "x_rot")
+    N, K = packed.shape[0], packed.shape[1] * 2
+    M = x_rot.shape[0]
+    if x_rot.dim() != 2 or x_rot.shape[1] != K or x_rot.stride(1) != 1:
+        raise ValueError("x_rot must be [M, K] with unit column stride")
+    y = torch.empty((M, N), dtype=torch.float32, device=packed.device) if out is None else out
+    st = lib().tq_gemm(_ptr(packed), _ptr(scales), N, K, M, _ptr(x_rot), _dtype_code(x_rot, "x_rot"),
+                       x_rot.stride(0), _ptr(y), y.stride(0), _stream())
+    _check("tq_gemm", st)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# NVFP4 / MXFP6
+# ----------------------------------------------------------------------------
+
+def blockfp_quantize(fmt: str, W: torch.Tensor):
+    """-> (codes uint8, block_scales uint8, tensor_scale float32[1] or None)."""
+    _dev(W, "W")
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous")
+    f = FORMATS[fmt]
+    N, K = W.shape
+    if fmt == "nvfp4":
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+        bs = torch.empty((N, K // 16), dtype=torch.uint8, device=W.device)
+        ts = torch.empty(1, dtype=torch.float32, device=W.device)
+    else:
+        codes = torch.empty((N, 3 * K // 4), dtype=torch.uint8, device=W.device)
+        bs = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
+        ts = None
+    st = lib().tq_blockfp_quantize(f, _ptr(W), _dtype_code(W, "W"), N, K, _ptr(codes), _ptr(bs), _ptr(ts),
+                                   _stream())
+    _check("tq_blockfp_quantize", st)
+    return codes, bs, ts
+
+
+def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale, x: torch.Tensor,
+                 out=None):
+    """Y [M, N] float32 = X W_deq^T (x: [M, K] or [K], fp32/bf16)."""
+    _dev(codes, "codes")
+    _dev(x, "x")
+    f = FORMATS[fmt]
+    N = codes.shape[0]
+    K = codes.shape[1] * 2 if fmt == "nvfp4" else codes.shape[1] * 4 // 3
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    M = x2.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=codes.device) if out is None else out
+    st = lib().tq_blockfp_gemm(f, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), N, K, M, _ptr(x2),
+                               _dtype_code(x2, "x"), x2.stride(0), _ptr(y), y.stride(0), _stream())
+    _check("tq_blockfp_gemm", st)
+    return y if x.dim() == 2 else y.reshape(-1)

@@ -1,0 +1,134 @@
+// C ABI of libtq: argument validation and dispatch to the HIP launchers.
+// Every check runs before anything is enqueued, so a call that returns an
+// error has not touched the stream.
+#include <cstdint>
+
+#include "tq_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t dtype_size(tq_dtype t) {
+  switch (t) {
+    case TQ_F32: return 4;
+    case TQ_BF16: return 2;
+    case TQ_F16: return 2;
+  }
+  return 0;
+}
+
+bool float_or_bf16(tq_dtype t) { return t == TQ_F32 || t == TQ_BF16; }
+
+tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
+
+// Common checks for a TQ4_1S weight pair.
+tq_status check_weights(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K) {
+  if (!packed || !scales) return TQ_EINVAL;
+  if (N <= 0 || K <= 0) return TQ_EINVAL;
+  if (K % tq::kBlock) return TQ_ESHAPE;
+  if (!aligned(packed, 16) || !aligned(scales, 4)) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument (null pointer, non-positive size, bad flag or format)";
+    case TQ_ESHAPE: return "unsupported shape (K not a multiple of the block, or a size limit exceeded)";
+    case TQ_EALIGN: return "misaligned pointer or leading dimension";
+    case TQ_EDTYPE: return "dtype not accepted by this call";
+    case TQ_EDEVICE: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+tq_status tq_quantize(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t ldw, uint32_t sign_mask,
+                      uint8_t* packed, uint16_t* scales, hipStream_t stream) {
+  if (!W) return TQ_EINVAL;
+  if (tq_status st = check_weights(packed, scales, N, K)) return st;
+  if (ldw < K) return TQ_EINVAL;
+  if (!float_or_bf16(wt)) return TQ_EDTYPE;
+  if (!aligned(W, 16) || (ldw * dtype_size(wt)) % 16) return TQ_EALIGN;
+  return from_hip(tq::launch_quantize(W, wt == TQ_BF16, N, K, ldw, sign_mask, packed, scales, stream));
+}
+
+tq_status tq_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t sign_mask,
+                        void* W_out, tq_dtype ot, int64_t ldo, hipStream_t stream) {
+  if (!W_out) return TQ_EINVAL;
+  if (tq_status st = check_weights(packed, scales, N, K)) return st;
+  if (ldo < K) return TQ_EINVAL;
+  if (!float_or_bf16(ot)) return TQ_EDTYPE;
+  if (!aligned(W_out, 16) || (ldo * dtype_size(ot)) % 16) return TQ_EALIGN;
+  return from_hip(tq::launch_dequantize(packed, scales, N, K, sign_mask, W_out, ot == TQ_BF16, ldo, stream));
+}
+
+tq_status tq_rotate(const void* x, tq_dtype xt, int64_t M, int64_t K, int64_t ldx, uint32_t sign_mask,
+                    void* x_rot, tq_dtype rt, int64_t ldr, hipStream_t stream) {
+  if (!x || !x_rot || M <= 0 || K <= 0) return TQ_EINVAL;
+  if (K % tq::kBlock) return TQ_ESHAPE;
+  if (ldx < K || ldr < K) return TQ_EINVAL;
+  if (!float_or_bf16(xt) || !float_or_bf16(rt)) return TQ_EDTYPE;
+  if (!aligned(x, 16) || !aligned(x_rot, 16) || (ldx * dtype_size(xt)) % 16 || (ldr * dtype_size(rt)) % 16)
+    return TQ_EALIGN;
+  return from_hip(tq::launch_rotate(x, xt == TQ_BF16, M, K, ldx, sign_mask, x_rot, rt == TQ_BF16, ldr, stream));
+}
+
+tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t sign_mask,
+                  const void* x, tq_dtype xt, int x_is_rotated, float* y, hipStream_t stream) {
+  if (!x || !y) return TQ_EINVAL;
+  if (tq_status st = check_weights(packed, scales, N, K)) return st;
+  if (K > 131072 || N > 0x7fffffff) return TQ_ESHAPE;
+  if (x_is_rotated ? xt != TQ_F32 : !float_or_bf16(xt)) return TQ_EDTYPE;
+  if (!aligned(x, 16) || !aligned(y, 4)) return TQ_EALIGN;
+  return from_hip(tq::launch_gemv(packed, scales, N, K, sign_mask, x, xt == TQ_BF16, x_is_rotated != 0, y, stream));
+}
+
+tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
+                  const void* x_rot, tq_dtype xt, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+  if (!x_rot || !y || M <= 0) return TQ_EINVAL;
+  if (tq_status st = check_weights(packed, scales, N, K)) return st;
+  if (ldx < K || ldy < N) return TQ_EINVAL;
+  if (M > 256 || K > 131072 || N > 0x7fffffff) return TQ_ESHAPE;
+  if (!float_or_bf16(xt)) return TQ_EDTYPE;
+  if (!aligned(x_rot, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4)) return TQ_EALIGN;
+  return from_hip(tq::launch_gemm(packed, scales, N, K, M, x_rot, xt == TQ_BF16, ldx, y, ldy, stream));
+}
+
+tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
+                              uint8_t* block_scales, float* tensor_scale, hipStream_t stream) {
+  if (f != TQ_FMT_NVFP4 && f != TQ_FMT_MXFP6) return TQ_EINVAL;
+  if (!W || !codes || !block_scales || N <= 0 || K <= 0) return TQ_EINVAL;
+  if (f == TQ_FMT_NVFP4 && !tensor_scale) return TQ_EINVAL;
+  if (K % (f == TQ_FMT_NVFP4 ? 16 : 32)) return TQ_ESHAPE;
+  if (N > 0x7fffffff) return TQ_ESHAPE;
+  if (!float_or_bf16(wt)) return TQ_EDTYPE;
+  if (!aligned(W, 16) || (K * dtype_size(wt)) % 16 || !aligned(codes, 8)) return TQ_EALIGN;
+  if (f == TQ_FMT_NVFP4 && !aligned(tensor_scale, 4)) return TQ_EALIGN;
+  return from_hip(tq::launch_blockfp_quantize((int)f, W, wt == TQ_BF16, N, K, codes, block_scales, tensor_scale,
+                                              stream));
+}
+
+tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale,
+                          int64_t N, int64_t K, int64_t M, const void* x, tq_dtype xt, int64_t ldx, float* y,
+                          int64_t ldy, hipStream_t stream) {
+  if (f != TQ_FMT_NVFP4 && f != TQ_FMT_MXFP6) return TQ_EINVAL;
+  if (!codes || !block_scales || !x || !y || N <= 0 || K <= 0 || M <= 0) return TQ_EINVAL;
+  if (f == TQ_FMT_NVFP4 && !tensor_scale) return TQ_EINVAL;
+  if (ldx < K || ldy < N) return TQ_EINVAL;
+  if (K % 32) return TQ_ESHAPE;
+  if (M > 16 || K > 32768 || N > 0x7fffffff) return TQ_ESHAPE;
+  if (!float_or_bf16(xt)) return TQ_EDTYPE;
+  if (!aligned(codes, 8) || !aligned(x, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4)) return TQ_EALIGN;
+  if (f == TQ_FMT_NVFP4 && (!aligned(block_scales, 2) || !aligned(tensor_scale, 4))) return TQ_EALIGN;
+  return from_hip(tq::launch_blockfp_gemm((int)f, codes, block_scales, tensor_scale, N, K, M, x, xt == TQ_BF16, ldx,
+                                          y, ldy, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Internal declarations shared by the libtq translation units.
+//
+// Every kernel is written for gfx950 (CDNA4): 64-lane wavefronts, 160 KB of
+// LDS per CU, 256 CUs in 8 XCDs.  The host entry points in tq_api.cpp
+// validate arguments and call the launch_* functions declared here.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kBlock = 32;           // TQ4_1S block length
+constexpr int kHalf = 16;            // elements per scale (d0: 0-15, d1: 16-31)
+constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;   // float32(1/sqrt(32)) = 0x3E3504F3
+
+// Codebook handed to kernels by value (kernel-argument segment, read through
+// the scalar cache): 16 ascending centroids and the 15 midpoint thresholds.
+struct Codebook {
+  float c[16];
+  float m[15];
+};
+
+// Host side (tq_codebook.cpp).
+const Codebook& host_codebook();
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// float32 -> fp16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__half_as_ushort(__float2half_rn(f));
+}
+
+// Non-negative finite float32 -> fp16 bits with round-to-nearest-even and
+// saturation at 65504, in integer arithmetic (independent of the FP mode
+// register, keeps fp16 subnormals).
+__device__ __forceinline__ uint32_t f32_to_f16_sat_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u >= 0x477fe000u) return 0x7bffu;              // >= 65504 -> max finite
+  int e = (int)(u >> 23) - 127;
+  uint32_t m = (u & 0x7fffffu) | 0x800000u;
+  if (e >= -14) {                                    // normal half
+    uint32_t h = ((uint32_t)(e + 15) << 10) | ((m >> 13) & 0x3ffu);
+    uint32_t rem = m & 0x1fffu;
+    h += (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ? 1u : 0u;
+    return h;                                        // carry may round up to the next binade
+  }
+  if (u == 0u) return 0u;
+  int s = -e - 1;                                    // value / 2^-24 = m >> s
+  if (s >= 32) return 0u;
+  uint32_t q = m >> s;
+  uint32_t rem = m & ((1u << s) - 1u);
+  uint32_t half = 1u << (s - 1);
+  q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+  return q;
+}
+
+// fp16 bits -> float32, exact, in integer arithmetic (finite inputs).
+__device__ __forceinline__ float f16_bits_to_f32_exact(uint32_t h) {
+  uint32_t e = (h >> 10) & 0x1fu;
+  uint32_t m = h & 0x3ffu;
+  uint32_t s = (h & 0x8000u) << 16;
+  if (e == 0u) {
+    float v = (float)m * 0x1p-24f;                   // exact: m < 2^10
+    return __uint_as_float(__float_as_uint(v) | s);
+  }
+  return __uint_as_float(s | ((e + 112u) << 23) | (m << 13));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return __half2float(__ushort_as_half((unsigned short)(h & 0xffffu)));
+}
+
+// Unnormalised 32-point Walsh-Hadamard transform in registers, Sylvester
+// order: stages h = 1, 2, 4, 8, 16; pair (i, i+h) -> (v_i + v_{i+h}, v_i - v_{i+h}).
+__device__ __forceinline__ void fwht32(float (&v)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Flip the sign of element i when bit i of mask is set (exact).
+__device__ __forceinline__ void apply_signs(float (&v)[32], uint32_t mask) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
+}
+
+// Load one 32-element block (fp32 or bf16) into registers; p is 16-byte aligned.
+template <bool kBf16>
+__device__ __forceinline__ void load_block(const void* p, float (&v)[32]) {
+  if constexpr (kBf16) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint4 u = q[t];
+      v[8 * t + 0] = bf16_lo(u.x); v[8 * t + 1] = bf16_hi(u.x);
+      v[8 * t + 2] = bf16_lo(u.y); v[8 * t + 3] = bf16_hi(u.y);
+      v[8 * t + 4] = bf16_lo(u.z); v[8 * t + 5] = bf16_hi(u.z);
+      v[8 * t + 6] = bf16_lo(u.w); v[8 * t + 7] = bf16_hi(u.w);
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float4 u = q[t];
+      v[4 * t + 0] = u.x; v[4 * t + 1] = u.y; v[4 * t + 2] = u.z; v[4 * t + 3] = u.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipGetLastError() after its launches)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_quantize(const void* W, bool bf16, int64_t N, int64_t K, int64_t ldw, uint32_t mask,
+                           uint8_t* packed, uint16_t* scales, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                             uint32_t mask, void* out, bool bf16, int64_t ldo, hipStream_t s);
+hipError_t launch_rotate(const void* x, bool xbf16, int64_t M, int64_t K, int64_t ldx, uint32_t mask,
+                         void* xr, bool rbf16, int64_t ldr, hipStream_t s);
+hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t mask,
+                       const void* x, bool xbf16, bool rotated, float* y, hipStream_t s);
+hipError_t launch_gemm_valu(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
+                            const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
+                       const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K,
+                                   uint8_t* codes, uint8_t* bscales, float* tscale, hipStream_t s);
+hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
+                               int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
+                               float* y, int64_t ldy, hipStream_t s);
+
+}  // namespace tq

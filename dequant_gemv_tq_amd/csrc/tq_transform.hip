@@ -1,0 +1,251 @@
+// Per-block TQ4_1S transforms on gfx950: quantize (weights -> nibbles + fp16
+// scales), rotate (activations -> rotated activations) and dequantize.
+//
+// TQ4 page ("企业官网建设流程全解析", hotelren.com/news/5458160), "格式原理":
+//   1. each 32-element block is rotated by a randomized Walsh-Hadamard
+//      transform with sign flips;
+//   2. every rotated value maps to the nearest of 16 Lloyd-Max N(0,1)
+//      centroids;
+//   3. elements 0-15 and 16-31 keep separate scales d0, d1.
+// The decode-speed section's "rotate the activation once" is tq_rotate.
+//
+// One thread owns one block: the 32 values live in VGPRs, the FWHT is five
+// register butterfly stages with no cross-lane traffic, and each thread
+// writes 16 contiguous bytes of nibbles and one 32-bit scale pair, so
+// consecutive lanes produce fully coalesced 16-byte and 4-byte stores.
+//
+// Bit-exact float32 order (shared definition with any CPU reference):
+//   v = D w; u = FWHT32(v) in stages h = 1, 2, 4, 8, 16; w' = u * fl(1/sqrt 32);
+//   per half: sq_i = w'_i * w'_i; ss = pairwise tree in index order;
+//   rms = sqrt(ss * 0.0625) correctly rounded; d = fp16_rne_sat(rms);
+//   idx = #{k : w' > fl(d * m_k)}.
+// FMA contraction would change these roundings, so it is off in this file.
+#pragma clang fp contract(off)
+
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Index of the nearest centroid: #{k in 0..14 : w > U_k} with U_k = fl(dd * m_k).
+// The thresholds are antisymmetric (U_k = -U_{14-k}, U_7 = +0), so only the
+// seven positive ones are kept.  For w > 0 the count is 8 + #{r : |w| > U_{8+r}};
+// for w <= 0 it is 7 - #{r : |w| >= U_{8+r}}.  Non-negative floats order like
+// their bit patterns, and |w| >= U  <=>  bits(|w|) + 1 > bits(U), so both
+// cases become one unsigned 3-level binary search over U_8..U_14.
+__device__ __forceinline__ uint32_t nearest_index(float w, const uint32_t (&U)[7]) {
+  uint32_t bits = __float_as_uint(w);
+  bool pos = (int32_t)bits > 0;                      // strictly positive (subnormals too)
+  uint32_t key = (bits & 0x7fffffffu) + (pos ? 0u : 1u);
+  bool c2 = key > U[3];
+  uint32_t t1 = c2 ? U[5] : U[1];
+  bool c1 = key > t1;
+  uint32_t ta = c2 ? U[4] : U[0];
+  uint32_t tb = c2 ? U[6] : U[2];
+  bool c0 = key > (c1 ? tb : ta);
+  uint32_t j = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
+  return pos ? 8u + j : 7u - j;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ W, int64_t ldw_bytes,
+                                                            uint32_t nb, uint32_t total, uint32_t mask,
+                                                            Codebook cb, uint4* __restrict__ packed,
+                                                            uint32_t* __restrict__ scales) {
+  uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  uint32_t row = g / nb;
+  uint32_t b = g - row * nb;
+  const uint8_t* src = W + (int64_t)row * ldw_bytes + (int64_t)b * (kBf16 ? 64 : 128);
+
+  float v[32];
+  load_block<kBf16>(src, v);
+  apply_signs(v, mask);
+  fwht32(v);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = v[i] * kInvSqrt32;
+
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  uint32_t dbits[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = v[16 * h + i] * v[16 * h + i];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+      for (int i = 0; i < w; ++i) s[i] = s[2 * i] + s[2 * i + 1];
+    }
+    float rms = __builtin_sqrtf(s[0] * 0.0625f);
+    dbits[h] = f32_to_f16_sat_rne(rms);
+    float dd = f16_bits_to_f32_exact(dbits[h]);
+    uint32_t U[7];
+#pragma unroll
+    for (int r = 0; r < 7; ++r) U[r] = __float_as_uint(dd * cb.m[8 + r]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int e = 16 * h + i;
+      words[e >> 3] |= nearest_index(v[e], U) << (4 * (e & 7));
+    }
+  }
+  packed[g] = make_uint4(words[0], words[1], words[2], words[3]);
+  scales[g] = dbits[0] | (dbits[1] << 16);
+}
+
+template <bool kInBf16, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void rotate_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes,
+                                                          uint32_t nb, uint32_t total, uint32_t mask,
+                                                          uint8_t* __restrict__ xr, int64_t ldr_bytes) {
+  uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  uint32_t row = g / nb;
+  uint32_t b = g - row * nb;
+  float v[32];
+  load_block<kInBf16>(x + (int64_t)row * ldx_bytes + (int64_t)b * (kInBf16 ? 64 : 128), v);
+  apply_signs(v, mask);
+  fwht32(v);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = v[i] * kInvSqrt32;
+  uint8_t* dst = xr + (int64_t)row * ldr_bytes + (int64_t)b * (kOutBf16 ? 64 : 128);
+  if constexpr (kOutBf16) {
+    uint4* q = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        w[u] = f32_to_bf16_rne(v[8 * t + 2 * u]) | (f32_to_bf16_rne(v[8 * t + 2 * u + 1]) << 16);
+      q[t] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    float4* q = reinterpret_cast<float4*>(dst);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = make_float4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]);
+  }
+}
+
+// Dequantize: q_i = d_h * c[idx_i], then the inverse rotation
+// w = fl(1/sqrt 32) * D * FWHT32(q)   (H32 is symmetric and H32^2 = 32 I).
+template <bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint4* __restrict__ packed,
+                                                              const uint32_t* __restrict__ scales,
+                                                              uint32_t nb, uint32_t total, uint32_t mask,
+                                                              Codebook cb, uint8_t* __restrict__ out,
+                                                              int64_t ldo_bytes) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = cb.c[threadIdx.x];
+  __syncthreads();
+  uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  uint32_t row = g / nb;
+  uint32_t b = g - row * nb;
+  uint4 p = packed[g];
+  uint32_t sc = scales[g];
+  float d0 = f16_bits_to_f32_exact(sc & 0xffffu);
+  float d1 = f16_bits_to_f32_exact(sc >> 16);
+  uint32_t words[4] = {p.x, p.y, p.z, p.w};
+  float v[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    uint32_t n = (words[e >> 3] >> (4 * (e & 7))) & 15u;
+    v[e] = (e < 16 ? d0 : d1) * lut[n];
+  }
+  fwht32(v);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = v[i] * kInvSqrt32;
+  apply_signs(v, mask);
+  uint8_t* dst = out + (int64_t)row * ldo_bytes + (int64_t)b * (kOutBf16 ? 64 : 128);
+  if constexpr (kOutBf16) {
+    uint4* q = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        w[u] = f32_to_bf16_rne(v[8 * t + 2 * u]) | (f32_to_bf16_rne(v[8 * t + 2 * u + 1]) << 16);
+      q[t] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    float4* q = reinterpret_cast<float4*>(dst);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = make_float4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]);
+  }
+}
+
+inline uint32_t grid_for(uint32_t total) { return (total + kThreads - 1) / kThreads; }
+
+}  // namespace
+
+// The flat block index g = row * nb + b is kept in 32 bits; callers split
+// larger tensors into row chunks so that each launch stays below 2^31 blocks.
+hipError_t launch_quantize(const void* W, bool bf16, int64_t N, int64_t K, int64_t ldw, uint32_t mask,
+                           uint8_t* packed, uint16_t* scales, hipStream_t s) {
+  const Codebook& cb = host_codebook();
+  const uint32_t nb = (uint32_t)(K / kBlock);
+  const int64_t esz = bf16 ? 2 : 4;
+  const int64_t rows_per_launch = ((int64_t)1 << 30) / nb;
+  for (int64_t r0 = 0; r0 < N; r0 += rows_per_launch) {
+    int64_t rows = (N - r0 < rows_per_launch) ? N - r0 : rows_per_launch;
+    uint32_t total = (uint32_t)(rows * nb);
+    const uint8_t* w = static_cast<const uint8_t*>(W) + r0 * ldw * esz;
+    uint4* pk = reinterpret_cast<uint4*>(packed + r0 * (K / 2));
+    uint32_t* sc = reinterpret_cast<uint32_t*>(scales + r0 * (K / 16));
+    if (bf16)
+      hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, s, w, ldw * esz, nb,
+                         total, mask, cb, pk, sc);
+    else
+      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, s, w, ldw * esz, nb,
+                         total, mask, cb, pk, sc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate(const void* x, bool xbf16, int64_t M, int64_t K, int64_t ldx, uint32_t mask,
+                         void* xr, bool rbf16, int64_t ldr, hipStream_t s) {
+  const uint32_t nb = (uint32_t)(K / kBlock);
+  const int64_t rows_per_launch = ((int64_t)1 << 30) / nb;
+  const int64_t xs = xbf16 ? 2 : 4, rs = rbf16 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < M; r0 += rows_per_launch) {
+    int64_t rows = (M - r0 < rows_per_launch) ? M - r0 : rows_per_launch;
+    uint32_t total = (uint32_t)(rows * nb);
+    const uint8_t* xi = static_cast<const uint8_t*>(x) + r0 * ldx * xs;
+    uint8_t* xo = static_cast<uint8_t*>(xr) + r0 * ldr * rs;
+    dim3 grid(grid_for(total)), block(kThreads);
+    if (xbf16 && rbf16)
+      hipLaunchKernelGGL((rotate_kernel<true, true>), grid, block, 0, s, xi, ldx * xs, nb, total, mask, xo, ldr * rs);
+    else if (xbf16)
+      hipLaunchKernelGGL((rotate_kernel<true, false>), grid, block, 0, s, xi, ldx * xs, nb, total, mask, xo, ldr * rs);
+    else if (rbf16)
+      hipLaunchKernelGGL((rotate_kernel<false, true>), grid, block, 0, s, xi, ldx * xs, nb, total, mask, xo, ldr * rs);
+    else
+      hipLaunchKernelGGL((rotate_kernel<false, false>), grid, block, 0, s, xi, ldx * xs, nb, total, mask, xo, ldr * rs);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t mask,
+                             void* out, bool bf16, int64_t ldo, hipStream_t s) {
+  const Codebook& cb = host_codebook();
+  const uint32_t nb = (uint32_t)(K / kBlock);
+  const int64_t esz = bf16 ? 2 : 4;
+  const int64_t rows_per_launch = ((int64_t)1 << 30) / nb;
+  for (int64_t r0 = 0; r0 < N; r0 += rows_per_launch) {
+    int64_t rows = (N - r0 < rows_per_launch) ? N - r0 : rows_per_launch;
+    uint32_t total = (uint32_t)(rows * nb);
+    const uint4* pk = reinterpret_cast<const uint4*>(packed + r0 * (K / 2));
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales + r0 * (K / 16));
+    uint8_t* o = static_cast<uint8_t*>(out) + r0 * ldo * esz;
+    if (bf16)
+      hipLaunchKernelGGL(dequantize_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, s, pk, sc, nb, total,
+                         mask, cb, o, ldo * esz);
+    else
+      hipLaunchKernelGGL(dequantize_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, s, pk, sc, nb, total,
+                         mask, cb, o, ldo * esz);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tq

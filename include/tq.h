@@ -1,0 +1,193 @@
+/*
+ * tq.h -- C ABI of libtq: TQ4_1S block quantization and fused
+ * dequantize-times-activation GEMV/GEMM on AMD Instinct MI355X (gfx950),
+ * plus NVFP4 / MXFP6 block formats.
+ *
+ * Sources (five web pages; cited by title and section):
+ *   TQ4 page  -- "企业官网建设流程全解析" (hotelren.com/news/5458160), a
+ *                summary of community results for TQ4_1S weight compression.
+ *                Section "TQ4_1S 是什么", sub-list "格式原理" items 1-3 and the
+ *                paragraph after it define the encoding; the decode-speed
+ *                section ("解码速度：分硬件汇总", paragraph on why CUDA differs)
+ *                describes rotating the activation once so that
+ *                dequantization becomes a centroid lookup times a scale;
+ *                "适用前提与边界" notes that the attention tensors of a layer
+ *                share one in-place rotation.
+ *   Quantizer-tool page -- "这是我的 llama.cpp NVFP4/MXFP6 GGUF 量化工具"
+ *                (bittide.aicompass.dev): NVFP4 weight and tensor scales,
+ *                MXFP6 ("目前能实现的部分功能", "MXFP6 的未来").
+ *
+ * Conventions for every call below
+ *   - W is [N, K] row-major and y = W x; K is split into blocks of 32
+ *     contiguous elements (16 for NVFP4).
+ *   - Buffer pointers are DEVICE pointers unless marked [host].  The caller
+ *     allocates and frees every buffer; the library never allocates device
+ *     memory and keeps no state other than its host-side constant tables,
+ *     built once on first use (thread-safe).
+ *   - Inputs are never modified.  Outputs must not alias inputs.
+ *   - All work is enqueued asynchronously on `stream` (NULL = the null
+ *     stream); a call returns once its kernels are launched.
+ *   - Arguments are validated before anything is launched; on any error
+ *     nothing is enqueued.  TQ_EDEVICE reports a failed launch.
+ *   - NaN or Inf inputs give unspecified (but memory-safe) outputs.
+ *
+ * TQ4_1S storage (one 32-element block of row n, block b):
+ *   packed[n][16b .. 16b+15]   (uint8, K/2 bytes per row): byte j of the
+ *                              block holds element 2j in its low nibble and
+ *                              element 2j+1 in its high nibble; a nibble is
+ *                              the index (0 = most negative) of one of the
+ *                              16 Lloyd-Max centroids of N(0,1).
+ *   scales[n][2b], [2b+1]      (fp16 bits, K/16 per row): d0 for elements
+ *                              0-15 and d1 for elements 16-31 of the block.
+ *   5.0 bits per weight.
+ * Rotation: w' = (1/sqrt 32) * H32 * D * w per block, H32 the Sylvester
+ * Hadamard matrix in natural order and D = diag(+-1) with D_i = -1 when bit
+ * i of `sign_mask` is set.  The same mask must be used for the weights and
+ * the activations they multiply.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,      /* null pointer, non-positive size, bad flag or format   */
+  TQ_ESHAPE = 2,      /* K not a multiple of the block, size beyond a limit    */
+  TQ_EALIGN = 3,      /* a pointer or leading dimension breaks an alignment rule */
+  TQ_EDTYPE = 4,      /* dtype not accepted by this call                         */
+  TQ_EDEVICE = 5      /* the HIP runtime reported an error at launch             */
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+typedef enum tq_format { TQ_FMT_NVFP4 = 1, TQ_FMT_MXFP6 = 2 } tq_format;
+
+/* Version of this ABI (TQ_ABI_VERSION). */
+int tq_abi_version(void);
+
+/* Static English text for a status code. */
+const char* tq_status_str(int status);
+
+/* [host] The 16 centroids (ascending) of the 16-level Lloyd-Max quantizer of
+ * N(0,1) and the 15 decision thresholds m_k = float32((c_k + c_{k+1}) / 2),
+ * as the kernels use them (TQ4 page, "格式原理" item 2 and the paragraph after
+ * it: Lloyd's algorithm on the rotated-coordinate law).  The library computes
+ * them once, in double precision, to a fixed point and rounds to float32.
+ * Either pointer may be NULL.  Returns TQ_OK. */
+tq_status tq_codebook(float centroids[16], float thresholds[15]);
+
+/* [host] Sign mask from a seed: low 32 bits of the first splitmix64 output
+ * (state advanced by the 64-bit golden-ratio constant 0x9E3779B97F4A7C15).
+ * This is the reading taken of the TQ4 page's "golden-ratio sign flips"
+ * ("格式原理" item 1). */
+uint32_t tq_sign_mask_from_seed(uint64_t seed);
+
+/* [host] tq_sign_mask_from_seed(0) = 0x7B1DCDAF, the default mask. */
+uint32_t tq_default_sign_mask(void);
+
+/* Quantize W to TQ4_1S (TQ4 page, "格式原理" items 1-3).
+ *   W       [N, K] with row stride `ldw` elements; dtype `wt` = TQ_F32 or
+ *           TQ_BF16.  16-byte aligned; ldw * sizeof(wt) a multiple of 16.
+ *   packed  [N, K/2] uint8, 16-byte aligned (output).
+ *   scales  [N, K/16] fp16 bits, 4-byte aligned (output).
+ * Per block and half h: d_h = fp16(RMS of the 16 rotated values), rounded to
+ * nearest even and saturated at 65504; index = number of thresholds
+ * float32(d_h * m_k) the rotated value exceeds.  The float32 operation order
+ * is fixed (see the oracle), so the output is bit-reproducible.
+ * Errors: TQ_EINVAL (null, N or K <= 0, ldw < K), TQ_ESHAPE (K % 32),
+ * TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_quantize(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t ldw,
+                      uint32_t sign_mask, uint8_t* packed, uint16_t* scales,
+                      hipStream_t stream);
+
+/* Dequantize TQ4_1S back to the original (unrotated) domain: per block
+ * W_out = (1/sqrt 32) * D * H32 * (d_h * c[index]) (TQ4 page, paragraph after
+ * "格式原理": the reference dequantizes by inverse rotation and rescaling).
+ *   W_out   [N, K] with row stride `ldo`; `ot` = TQ_F32 or TQ_BF16 (RNE);
+ *           16-byte aligned, ldo * sizeof(ot) a multiple of 16.
+ * Errors as tq_quantize. */
+tq_status tq_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                        uint32_t sign_mask, void* W_out, tq_dtype ot, int64_t ldo,
+                        hipStream_t stream);
+
+/* Pre-rotate activations once: x_rot = (1/sqrt 32) * H32 * D * x per
+ * 32-block (TQ4 page, decode-speed section: rotate the activation instead of
+ * inverse-rotating every weight block).  The float32 order is the same
+ * butterfly order as tq_quantize.
+ *   x       [M, K], row stride ldx; `xt` = TQ_F32 or TQ_BF16; 16-byte aligned.
+ *   x_rot   [M, K], row stride ldr; `rt` = TQ_F32 or TQ_BF16 (RNE).
+ * Errors: TQ_EINVAL, TQ_ESHAPE (K % 32), TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_rotate(const void* x, tq_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                    uint32_t sign_mask, void* x_rot, tq_dtype rt, int64_t ldr,
+                    hipStream_t stream);
+
+/* Fused batch-1 GEMV y = W_deq x on TQ4_1S weights, computed in the rotated
+ * domain: y_n = sum_b [ d0 * sum_{i<16} c[idx_i] x'_i + d1 * sum_{i>=16} ... ]
+ * with float32 accumulation (TQ4 page, decode-speed section).
+ *   x            [K]; if x_is_rotated != 0 it is x' from tq_rotate and must
+ *                be TQ_F32; otherwise it is the raw activation (TQ_F32 or
+ *                TQ_BF16) and the kernel rotates it itself (sign_mask used).
+ *   y            [N] float32 (output).
+ * Limits: K <= 131072.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN (x 16-byte
+ * aligned, y 4-byte aligned), TQ_EDTYPE. */
+tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                  uint32_t sign_mask, const void* x, tq_dtype xt, int x_is_rotated,
+                  float* y, hipStream_t stream);
+
+/* Small-batch fused GEMM Y = X' Q^T with Q = d * c[idx] in the rotated
+ * domain (the same identity as tq_gemv, M activations at once).
+ *   x_rot   [M, K] pre-rotated activations (tq_rotate), row stride ldx,
+ *           TQ_BF16 or TQ_F32, 16-byte aligned.
+ *   y       [M, N] float32, row stride ldy (output).
+ * M < 16 runs a VALU kernel with float32 FMAs.  M >= 16 runs bf16 MFMA with
+ * float32 accumulation, dequantizing each weight once: one pass for bf16
+ * activations (operand rounding about 2^-9, inside 1e-3 * sum|w x| once K is
+ * in the hundreds), three hi/lo-split passes for float32 activations (about
+ * 16 significant bits per product, any K).
+ * Limits: M <= 256, K <= 131072.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN,
+ * TQ_EDTYPE. */
+tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
+                  const void* x_rot, tq_dtype xt, int64_t ldx, float* y, int64_t ldy,
+                  hipStream_t stream);
+
+/* Quantize W [N, K] (TQ_F32 or TQ_BF16, dense rows) to a block float format
+ * (quantizer-tool page, "目前能实现的部分功能" / "MXFP6 的未来"):
+ *   TQ_FMT_NVFP4: codes [N, K/2] (E2M1, element 2j in the low nibble of byte
+ *     j), block_scales [N, K/16] (E4M3fn), *tensor_scale = amax|W| / 2688
+ *     (one float32, device memory; also used as the amax accumulator while
+ *     the call runs).  K % 16 == 0.
+ *   TQ_FMT_MXFP6: codes [N, 3K/4] (E3M2, 4 codes per little-endian 24-bit
+ *     word), block_scales [N, K/32] (E8M0); tensor_scale ignored (may be
+ *     NULL).  K % 32 == 0.
+ * Rounding is to nearest even with saturation; the sign of a value that
+ * rounds to zero is kept.  W 16-byte aligned, codes 8-byte aligned.
+ * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K,
+                              uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                              hipStream_t stream);
+
+/* Y[m, n] = sum_k W_deq[n, k] X[m, k] for a block-float weight (fused
+ * decode, float32 accumulation).  X [M, K] row stride ldx, TQ_F32 or
+ * TQ_BF16, 16-byte aligned; Y [M, N] float32, row stride ldy.  K % 32 == 0,
+ * K <= 32768, M <= 16; NVFP4 block_scales 2-byte aligned.
+ * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales,
+                          const float* tensor_scale, int64_t N, int64_t K, int64_t M,
+                          const void* x, tq_dtype xt, int64_t ldx, float* y, int64_t ldy,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,117 @@
+"""The C ABI library loads, exports every symbol include/tq.h declares, and
+rejects bad arguments before launching anything (CPU only: no compute calls)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dequant_gemv_tq_amd as tqa
+from oracle import codebook as cb
+from oracle import tq4_1s as otq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+EINVAL, ESHAPE, EALIGN, EDTYPE = 1, 2, 3, 4
+F32, BF16, F16 = 0, 1, 2
+GOOD = 0x10000          # a 64 KiB-aligned fake device address: never dereferenced by a rejected call
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_knows():
+    assert sorted(tqa.EXPORTED) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    L = tqa.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    L = tqa.lib()
+    assert L.tq_abi_version() == 1
+    for s in range(6):
+        assert L.tq_status_str(s)
+    assert b"unknown" in L.tq_status_str(99)
+
+
+def test_codebook_matches_oracle_bit_exactly():
+    c, m = tqa.codebook()
+    np.testing.assert_array_equal(c, cb.tq4_codebook_f32())
+    np.testing.assert_array_equal(m, cb.tq4_midpoints_f32())
+
+
+def test_sign_mask_matches_oracle_splitmix():
+    for seed in (0, 1, 42, 2 ** 63 + 5):
+        assert tqa.sign_mask_from_seed(seed) == otq.sign_mask_from_seed(seed)
+    assert tqa.default_sign_mask() == otq.DEFAULT_SIGN_MASK == tqa.DEFAULT_SIGN_MASK
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, F32, 4, 64, 64, 0, _p(GOOD), _p(GOOD), None), EINVAL),          # null W
+    ((_p(GOOD), F32, 4, 64, 64, 0, None, _p(GOOD), None), EINVAL),          # null packed
+    ((_p(GOOD), F32, 0, 64, 64, 0, _p(GOOD), _p(GOOD), None), EINVAL),      # N = 0
+    ((_p(GOOD), F32, 4, -32, 64, 0, _p(GOOD), _p(GOOD), None), EINVAL),     # K < 0
+    ((_p(GOOD), F32, 4, 48, 48, 0, _p(GOOD), _p(GOOD), None), ESHAPE),      # K % 32
+    ((_p(GOOD), F32, 4, 64, 32, 0, _p(GOOD), _p(GOOD), None), EINVAL),      # ldw < K
+    ((_p(GOOD), F16, 4, 64, 64, 0, _p(GOOD), _p(GOOD), None), EDTYPE),      # fp16 weights
+    ((_p(GOOD + 4), F32, 4, 64, 64, 0, _p(GOOD), _p(GOOD), None), EALIGN),  # W misaligned
+    ((_p(GOOD), F32, 4, 64, 66, 0, _p(GOOD), _p(GOOD), None), EALIGN),      # ldw*4 % 16
+    ((_p(GOOD), F32, 4, 64, 64, 0, _p(GOOD + 8), _p(GOOD), None), EALIGN),  # packed misaligned
+    ((_p(GOOD), F32, 4, 64, 64, 0, _p(GOOD), _p(GOOD + 2), None), EALIGN),  # scales misaligned
+])
+def test_quantize_rejects(args, expect):
+    assert tqa.lib().tq_quantize(*args) == expect
+
+
+def test_other_calls_reject_before_launch():
+    L = tqa.lib()
+    g = _p(GOOD)
+    # gemv
+    assert L.tq_gemv(g, g, 8, 64, 0, None, F32, 1, g, None) == EINVAL
+    assert L.tq_gemv(g, g, 8, 50, 0, g, F32, 1, g, None) == ESHAPE
+    assert L.tq_gemv(g, g, 8, 131072 + 32, 0, g, F32, 1, g, None) == ESHAPE
+    assert L.tq_gemv(g, g, 8, 64, 0, g, BF16, 1, g, None) == EDTYPE          # rotated x must be fp32
+    assert L.tq_gemv(g, g, 8, 64, 0, g, F16, 0, g, None) == EDTYPE
+    assert L.tq_gemv(g, g, 8, 64, 0, _p(GOOD + 4), F32, 1, g, None) == EALIGN
+    assert L.tq_gemv(g, g, 8, 64, 0, g, F32, 1, _p(GOOD + 2), None) == EALIGN
+    # gemm
+    assert L.tq_gemm(g, g, 8, 64, 0, g, BF16, 64, g, 8, None) == EINVAL
+    assert L.tq_gemm(g, g, 8, 64, 257, g, BF16, 64, g, 8, None) == ESHAPE
+    assert L.tq_gemm(g, g, 8, 64, 16, g, F16, 64, g, 8, None) == EDTYPE
+    assert L.tq_gemm(g, g, 8, 64, 4, g, BF16, 60, g, 8, None) == EINVAL     # ldx < K
+    assert L.tq_gemm(g, g, 8, 64, 4, g, BF16, 64, g, 4, None) == EINVAL     # ldy < N
+    # rotate / dequantize
+    assert L.tq_rotate(g, F32, 2, 40, 40, 0, g, F32, 40, None) == ESHAPE
+    assert L.tq_rotate(g, F16, 2, 64, 64, 0, g, F32, 64, None) == EDTYPE
+    assert L.tq_dequantize(g, g, 2, 64, 0, None, F32, 64, None) == EINVAL
+    assert L.tq_dequantize(g, g, 2, 64, 0, g, F16, 64, None) == EDTYPE
+    # block float
+    assert L.tq_blockfp_quantize(3, g, F32, 2, 64, g, g, g, None) == EINVAL
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 64, g, g, None, None) == EINVAL   # NVFP4 needs tensor_scale
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 40, g, g, g, None) == ESHAPE
+    assert L.tq_blockfp_quantize(2, g, F32, 2, 48, g, g, None, None) == ESHAPE   # MXFP6 needs K % 32
+    assert L.tq_blockfp_quantize(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
+    assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 17, g, F32, 64, g, 8, None) == ESHAPE
+    assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None) == EDTYPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        tqa.quantize(w)
+    with pytest.raises(ValueError):
+        tqa.gemv(torch.zeros(4, 32, dtype=torch.uint8), torch.zeros(4, 4, dtype=torch.int16), torch.zeros(64))

@@ -1,0 +1,76 @@
+"""GPU parity of the NVFP4 / MXFP6 path against the CPU oracle (through the C ABI):
+codes, block scales and the tensor scale bit-exact; decode GEMV/GEMM within
+|dy| <= 1e-3 * sum |W_deq x|."""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_tq_amd as tqa
+from oracle import blockfp as obf
+import workloads
+from gpu_helpers import say, f32np, assert_within
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _check(fmt, W):
+    say(f"[{fmt} quantize] shape={tuple(W.shape)} dtype={W.dtype}")
+    codes, bs, ts = tqa.blockfp_quantize(fmt, W)
+    torch.cuda.synchronize()
+    Wh = W.float().cpu().numpy()
+    if fmt == "nvfp4":
+        oc, osb, ost = obf.nvfp4_quantize_o32(Wh)
+        assert np.float32(ts.cpu().numpy()[0]).view(np.uint32) == np.float32(ost).view(np.uint32)
+        Wd = obf.nvfp4_dequantize_o64(oc, osb, ost)
+    else:
+        oc, osb = obf.mxfp6_quantize_o32(Wh)
+        Wd = obf.mxfp6_dequantize_o64(oc, osb)
+    np.testing.assert_array_equal(bs.cpu().numpy(), osb, err_msg=f"{fmt} block scales")
+    np.testing.assert_array_equal(codes.cpu().numpy(), oc, err_msg=f"{fmt} codes")
+    return codes, bs, ts, Wd
+
+
+def _outlier_weight(n, k, seed, dtype):
+    g = workloads.generator(seed, DEV)
+    w = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.float32)
+    return workloads.add_outliers(w, 0.001, 20.0, g).to(dtype)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+@pytest.mark.parametrize("n,k,dt", [(1, 32, torch.float32), (13, 512, torch.bfloat16), (64, 5120, torch.bfloat16),
+                                    (7, 17408, torch.bfloat16), (33, 96, torch.float32)])
+def test_blockfp_quantize_bit_exact(fmt, n, k, dt):
+    _check(fmt, _outlier_weight(n, k, n * 31 + k, dt))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+def test_blockfp_edge_values(fmt):
+    W = torch.zeros(6, 64)
+    W[1, :] = -0.0
+    W[2, 3] = 1e-40                       # subnormal amax
+    W[3, :32] = torch.linspace(-1, 1, 32)
+    W[3, 40] = 3e4                        # huge tensor amax
+    W[4, :] = 2.0 ** -126
+    W[5, ::2] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0] * 4)   # E2M1 midpoints
+    _check(fmt, W.to(DEV))
+    _check(fmt, torch.zeros(3, 32, device=DEV))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 16])
+def test_blockfp_gemm(fmt, m):
+    n, k = 96, 5120
+    W = _outlier_weight(n, k, 500 + m, torch.bfloat16)
+    codes, bs, ts, Wd = _check(fmt, W)
+    g = workloads.generator(900 + m, DEV)
+    X = workloads.activation(m, k, g, DEV, torch.bfloat16)
+    say(f"[{fmt} gemm] M={m}")
+    Y = tqa.blockfp_gemm(fmt, codes, bs, ts, X)
+    yr, a = obf.gemm_deq_o64(Wd, X.float().cpu().numpy())
+    worst = assert_within(f32np(Y), yr, a, what=f"{fmt} M={m}")
+    assert worst < 1e-4
+    if m == 1:
+        y1 = tqa.blockfp_gemm(fmt, codes, bs, ts, X[0].contiguous())
+        assert torch.equal(y1, Y[0])
