@@ -40,14 +40,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extended", action="store_true", help="all 64 27B layers and the 80-layer 70B quantize")
-    ap.add_argument("--fused-rotation", action="store_true", help="rotate inside the GEMV instead of tq_rotate")
+    ap.add_argument("--prerotate", action="store_true",
+                    help="rotate each activation with tq_rotate before the GEMV instead of inside it")
+    ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
 
 
-def gemv_bytes(n, k):
-    return WEIGHT_BYTES_PER_ELEM * n * k + 4 * k + 4 * n
+def gemv_bytes(n, k, x_elem_bytes=4):
+    """Algorithmic bytes of one GEMV: packed weights + activation + float32 output."""
+    return WEIGHT_BYTES_PER_ELEM * n * k + x_elem_bytes * k + 4 * n
 
 
 def main():
@@ -98,14 +101,16 @@ def main():
 
     step_bytes = 0.0
     for gname, (n, k) in groups.items():
-        step_bytes += L * (gemv_bytes(n, k) + (0 if args.fused_rotation else 6 * k))
+        # fused: the GEMV reads the bf16 activation; prerotated: tq_rotate reads
+        # 2K and writes 4K bytes, then the GEMV reads the 4K-byte x'
+        step_bytes += L * (gemv_bytes(n, k, 2) if not args.prerotate else gemv_bytes(n, k, 4) + 6 * k)
 
     def step(events=None):
         for layer in range(L):
             for gname in groups:
                 packed, scales = model[layer][gname]
                 x = xs[layer][gname]
-                if args.fused_rotation:
+                if (not args.prerotate):
                     if events is not None:
                         events.append((gname, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
                         events[-1][1].record(stream)
@@ -120,15 +125,34 @@ def main():
                     events[-1][2].record(stream)
 
     # --------------------------------------------------------------- timed
+    # The step's launches are captured once into a HIP graph (torch.cuda.graph
+    # records on its capture stream, which is the current stream the library
+    # launches on) and replayed; --no-graph launches them eagerly.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run_step = step
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        for _ in range(max(1, args.warmup)):
+            run_step()
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     wall0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run_step()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -146,11 +170,12 @@ def main():
     gemv_launch_bytes = 0.0
     gemv_launch_ms = 0.0
     per_group = {}
+    xb = 2 if not args.prerotate else 4
     for gname, (n, k) in groups.items():
         ms = sum(per[gname]) / len(per[gname])
         per_group[gname] = {"N": n, "K": k, "us": round(ms * 1e3, 2),
-                            "GB_s": round(gemv_bytes(n, k) / (ms * 1e-3) / 1e9, 1)}
-        gemv_launch_bytes += gemv_bytes(n, k)
+                            "GB_s": round(gemv_bytes(n, k, xb) / (ms * 1e-3) / 1e9, 1)}
+        gemv_launch_bytes += gemv_bytes(n, k, xb)
         gemv_launch_ms += ms
     achieved = gemv_launch_bytes / (gemv_launch_ms * 1e-3) / 1e9
     layer_kernel_ms = gemv_launch_ms          # the four group launches of one layer
@@ -168,7 +193,8 @@ def main():
                    "layers": L, "groups": {g: list(v) for g, v in groups.items()},
                    "weights": "bf16 N(0,1/K) even layers, Student-t(4) odd layers, quantized on device",
                    "activation": "bf16 [K] N(0,1), rotated once per group",
-                   "rotation": "fused in GEMV" if args.fused_rotation else "tq_rotate + tq_gemv",
+                   "rotation": "fused in GEMV" if (not args.prerotate) else "tq_rotate + tq_gemv",
+                   "launch": "eager" if args.no_graph else "HIP graph replay",
                    "step_bytes": int(step_bytes)},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "tokens_equiv_layers_per_s": round(1e3 / layer_kernel_ms, 1),

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint4* __restrict_
   const int wave = tid >> 6;
   const int nl = lane & 15;
   const int g = lane >> 4;
-  if (tid < 16) lut[tid] = cb.c[tid];
+  stage_centroids(cb, lut);
   __syncthreads();
 
   const uint32_t n0 = blockIdx.x * 16u;

@@ -27,6 +27,9 @@ struct Codebook {
 // Host side (tq_codebook.cpp).
 const Codebook& host_codebook();
 
+// Number of compute units of the current device (queried once per device).
+int device_cu_count();
+
 // ---------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------
@@ -106,6 +109,17 @@ __device__ __forceinline__ void fwht32(float (&v)[32]) {
 __device__ __forceinline__ void apply_signs(float (&v)[32], uint32_t mask) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
+}
+
+// Copy the 16 centroids into LDS.  Compile-time indices keep the reads of the
+// by-value codebook argument on the scalar unit (a runtime index would turn
+// every read into a dependent vector load from the argument segment).  The
+// caller synchronizes before reading lut16.
+__device__ __forceinline__ void stage_centroids(const Codebook& cb, float* lut16) {
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lut16[k] = cb.c[k];
+  }
 }
 
 // Load one 32-element block (fp32 or bf16) into registers; p is 16-byte aligned.

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint4* __res
                                                               Codebook cb, uint8_t* __restrict__ out,
                                                               int64_t ldo_bytes) {
   __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = cb.c[threadIdx.x];
+  stage_centroids(cb, lut);
   __syncthreads();
   uint32_t g = blockIdx.x * kThreads + threadIdx.x;
   if (g >= total) return;
