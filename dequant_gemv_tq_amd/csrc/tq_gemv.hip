@@ -142,10 +142,131 @@ __device__ __forceinline__ void decode_block(const uint4& p, uint32_t sc, const 
   for (int m = 0; m < MC; ++m) acc[m] = __builtin_fmaf(d0, a[m][0], __builtin_fmaf(d1, a[m][1], acc[m]));
 }
 
+// Pair table fill straight from the codebook argument (scalar registers): no
+// staging through LDS and no barrier before it.  Wavefront w (of 16 virtual
+// ones) writes entries e = 16 w + 4 u + lane / 16 (u < 4), copies
+// 2 (lane % 16) and 2 (lane % 16) + 1, so the high centroid c[e / 16] =
+// c[w] is a wavefront-uniform choice and the low one c[e % 16] = c[4 u +
+// lane / 16] a per-lane choice of four.  Consecutive lanes
+// store consecutive 16-byte chunks of the table (no bank conflicts).
+__device__ __forceinline__ void fill_pair_lut(const Codebook& cb, uint8_t* lut, int tid, int nthreads) {
+  // readfirstlane makes each centroid an opaque register value, so the
+  // selects below stay selects (a select between two argument loads is
+  // otherwise folded into one load from a selected address, which copies
+  // the argument to scratch memory).
+  float c[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) c[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cb.c[k])));
+  const int lane = tid & 63, g = lane >> 4;
+  for (int w = tid >> 6; w < 16; w += nthreads >> 6) {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    float hi = c[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) hi = wu == k ? c[k] : hi;
+    uint8_t* base = lut + ((16 * wu + g) << 8) + 16 * (lane & 15);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float lo = g == 0 ? c[4 * u] : g == 1 ? c[4 * u + 1] : g == 2 ? c[4 * u + 2] : c[4 * u + 3];
+      *reinterpret_cast<float4*>(base + (u << 10)) = make_float4(lo, hi, lo, hi);
+    }
+  }
+}
+
+// One cross-lane stage of the 32-point FWHT when 8 consecutive lanes hold a
+// block, 4 consecutive elements each: elements i and i + 4d sit in lanes
+// l and l ^ d at the same position.  The lower lane forms a + b, the upper
+// one a - b (a the lower lane's value), each with one rounding, exactly as
+// the in-register butterfly does.
+template <int D>
+__device__ __forceinline__ void fwht_lane_stage(float (&v)[4], int lane) {
+  const float sgn = (lane & D) ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float p;
+    if constexpr (D == 1) p = dpp<kQuadXor1>(v[e]);
+    else if constexpr (D == 2) p = dpp<kQuadXor2>(v[e]);
+    else p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[e]), 0x101F));   // lane ^ 4 in 32
+    v[e] = __builtin_fmaf(sgn, v[e], p);
+  }
+}
+
+// Stage the activation of one GEMV in LDS as fp32 x' (rotated when kMode >=
+// 2), once per workgroup.  Consecutive threads load consecutive 4-element
+// groups, P groups per thread (coalesced: one request per cache line per
+// workgroup instead of one per lane), all issued up front; the loads of a
+// thread's unused groups are clamped to the tensor and discarded.  Once they
+// arrive, the groups are rotated cooperatively (8 lanes per block, the
+// butterfly stages in the same order as the per-lane transform) and block
+// b, 16-byte chunk q is stored at float offset 32 b + 4 (q ^ (b % 8)):
+// lanes that later read consecutive blocks then hit distinct banks.  The
+// 1/sqrt(32) factor is left to the row sums.
+template <int kMode, int P>
+struct ActivationStage {
+  static constexpr bool kBf16 = kMode == 1 || kMode == 3;
+  uint32_t raw[P][kBf16 ? 2 : 4];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ x, uint32_t K, int tid, int nthreads) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t e0 = min(4u * (uint32_t)(tid + p * nthreads), K - 4);
+      if constexpr (kBf16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(x + 2 * (size_t)e0);
+        raw[p][0] = u.x; raw[p][1] = u.y;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + 4 * (size_t)e0);
+        raw[p][0] = u.x; raw[p][1] = u.y; raw[p][2] = u.z; raw[p][3] = u.w;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint32_t K, uint32_t mask, float* xs, int tid, int nthreads) const {
+    const int lane = tid & 63;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t e0 = 4u * (uint32_t)(tid + p * nthreads);
+      if (e0 >= K) break;                // whole 8-lane groups leave together (K % 32 == 0)
+      float v[4];
+      if constexpr (kBf16) {
+        v[0] = bf16_lo(raw[p][0]); v[1] = bf16_hi(raw[p][0]); v[2] = bf16_lo(raw[p][1]); v[3] = bf16_hi(raw[p][1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(raw[p][e]);
+      }
+      if constexpr (kMode >= 2) {
+        const uint32_t i0 = e0 & 31;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((mask >> (i0 + e)) & 1u) << 31));
+        float a = v[0], b = v[1];        // h = 1
+        v[0] = a + b; v[1] = a - b;
+        a = v[2]; b = v[3];
+        v[2] = a + b; v[3] = a - b;
+        a = v[0]; b = v[2];              // h = 2
+        v[0] = a + b; v[2] = a - b;
+        a = v[1]; b = v[3];
+        v[1] = a + b; v[3] = a - b;
+        fwht_lane_stage<1>(v, lane);     // h = 4
+        fwht_lane_stage<2>(v, lane);     // h = 8
+        fwht_lane_stage<4>(v, lane);     // h = 16
+      }
+      const uint32_t b = e0 >> 5, q = (e0 >> 2) & 7;
+      *reinterpret_cast<float4*>(xs + 32 * b + 4 * (q ^ (b & 7))) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+};
+
+// Largest K whose x' a workgroup stages in LDS next to the 64 KiB pair table.
+constexpr int kStageFloats = 20480;
+// Tiles whose cross-wavefront partial sums wait in LDS before being combined.
+constexpr int kRing = 32;
+
 // kMode: 0 = x' fp32, 1 = x' bf16, 2 = raw fp32 x, 3 = raw bf16 x (rotated in the prologue).
-// kPrefetch: keep the next tile's loads in flight while the current one is
-// computed (two register sets), otherwise rely on other wavefronts.
-template <int J, int R, int MC, int kMode, int kMaxT, bool kPrefetch>
+// kStage: stage x' in LDS once per workgroup with kStage groups of 4
+// elements per thread (MC == 1, K <= kStageFloats); 0: every lane loads and
+// rotates its own blocks.
+// kDepth: tiles whose loads a wavefront keeps in flight (register sets): 1
+// = load, wait, compute; 2 and 3 issue the loads of the tiles one and two
+// steps ahead before the current tile is computed.
+template <int J, int R, int MC, int kMode, int kMaxT, int kDepth, int kStage>
 __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ packed,
                                                      const uint32_t* __restrict__ scales, uint32_t N, uint32_t nb,
                                                      uint32_t mask, const uint8_t* __restrict__ x, int64_t ldx,
@@ -154,13 +275,24 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   constexpr int V = R * MC;
   static_assert(V == 1 || V == 2 || V == 4 || V == 8, "R * MC must be 1, 2, 4 or 8");
   constexpr bool kXbf16 = kMode == 1 || kMode == 3;
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  __shared__ float red[2][kMaxT / 64][V];
-  __shared__ float c16[16];
+  static_assert(!kStage || MC == 1, "staged activations serve one row");
+  // One LDS allocation with the pair table at offset 0, so a table address
+  // is the v_perm result itself (a base above 64 KiB would not fit the
+  // ds_read immediate and cost an add per lookup), then the staged x' and
+  // the cross-wavefront partial sums.
+  constexpr int kXsBytes = kStage ? kStageFloats * 4 : 0;
+  constexpr int kRedBytes = kRing * (kMaxT / 64) * V * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLutBytes + kXsBytes + kRedBytes];
+  uint8_t* const lut = smem;
+  float* const xs = reinterpret_cast<float*>(smem + kLutBytes);
+  float (*const red)[kMaxT / 64][V] = reinterpret_cast<float (*)[kMaxT / 64][V]>(smem + kLutBytes + kXsBytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int slot = tid / TK;                  // row slot of this thread
+  // TK is a multiple of 64, so the row slot and the wavefront's place along
+  // K are wavefront-uniform: readfirstlane lets the row addressing run on
+  // the scalar unit.
+  const int slot = __builtin_amdgcn_readfirstlane(tid / TK);   // row slot of this thread
   const int lk = tid - slot * TK;             // lane index along K
   const int wk = lk >> 6;                     // wavefront index along K within the slot
   const int WK = TK >> 6;
@@ -170,70 +302,114 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   // Loads are branch-free: indices are clamped into the tensor, so a lane
   // past the last block or row reads valid memory whose contribution is
   // discarded (x' is zero past the last block; rows past N are not written).
-  uint4 pa[R][J], pb[kPrefetch ? R : 1][kPrefetch ? J : 1];
-  uint32_t sa[R][J], sb[kPrefetch ? R : 1][kPrefetch ? J : 1];
+  static_assert(kDepth >= 1 && kDepth <= 3, "kDepth must be 1, 2 or 3");
+  constexpr int RB = kDepth >= 2 ? R : 1, RC = kDepth >= 3 ? R : 1;
+  uint4 pa[R][J], pb[RB][J], pc[RC][J];
+  uint32_t sa[R][J], sb[RB][J], sc[RC][J];
   auto load_tile = [&](uint32_t t, auto& p, auto& s) {
     const uint32_t row0 = (t * S + slot) * R;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t row = min(row0 + r, N - 1);
+      const uint4* prow = packed + (size_t)row * nb;
+      const uint32_t* srow = scales + (size_t)row * nb;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const uint32_t b = min((uint32_t)(lk + j * TK), nb - 1);
-        const size_t g = (size_t)row * nb + b;
-        p[r][j] = packed[g];
-        s[r][j] = scales[g];
+        p[r][j] = prow[b];
+        s[r][j] = srow[b];
       }
     }
   };
 
-  // The first tile's weights and the activation are requested before
+  // The first kDepth tiles' weights and the activation are requested before
   // anything else so that their latency overlaps the table fill.
   const uint32_t G = gridDim.x;
   uint32_t t = blockIdx.x;
-  load_tile(t, pa, sa);
+  const uint32_t last = t + (tiles - 1 - t) / G * G;   // this workgroup's last tile
+  const uint32_t n = (last - t) / G + 1;               // and its tile count
 
   float xr[J][MC][32];
+  ActivationStage<kMode, kStage ? kStage : 1> xst;
+  if constexpr (kStage) {
+    xst.load(x, nb * 32, tid, blockDim.x);
+  } else {
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const uint32_t b = min((uint32_t)(lk + j * TK), nb - 1);
+    for (int j = 0; j < J; ++j) {
+      const uint32_t b = min((uint32_t)(lk + j * TK), nb - 1);
 #pragma unroll
-    for (int m = 0; m < MC; ++m) load_block<kXbf16>(x + m * ldx + (size_t)b * (kXbf16 ? 64 : 128), xr[j][m]);
-  }
-
-  // Pair table: entry e, copy c -> (c[e & 15], c[e >> 4]).  Item i writes
-  // copies 2 (i % 16) and 2 (i % 16) + 1 of entry i / 16 with one 16-byte
-  // store, so consecutive lanes fill consecutive bytes of a 256-byte table
-  // row (no bank conflicts; a lane stride of 256 B would put every lane of a
-  // wavefront on one bank).
-  stage_centroids(cb, c16);
-  __syncthreads();
-  for (int i = tid; i < 256 * (kCopies / 2); i += blockDim.x) {
-    const int e = i >> 4, c = 2 * (i & 15);
-    const float lo = c16[e & 15], hi = c16[e >> 4];
-    *reinterpret_cast<float4*>(lut + (e << 8) + c * 8) = make_float4(lo, hi, lo, hi);
-  }
-
-  // Unrotated activations are rotated per lane while the first tile's loads
-  // are in flight: x' = FWHT32(D x); the 1/sqrt(32) is applied once to each
-  // finished row sum instead of to every element.
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const bool inside = (uint32_t)(lk + j * TK) < nb;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      if constexpr (kMode >= 2) {
-        apply_signs(xr[j][m], mask);
-        fwht32(xr[j][m]);
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) xr[j][m][i] = inside ? xr[j][m][i] : 0.f;
+      for (int m = 0; m < MC; ++m) load_block<kXbf16>(x + m * ldx + (size_t)b * (kXbf16 ? 64 : 128), xr[j][m]);
     }
   }
-  __syncthreads();
+  load_tile(t, pa, sa);
+  if constexpr (kDepth >= 2) load_tile(min(t + G, last), pb, sb);
+  if constexpr (kDepth >= 3) load_tile(min(t + 2 * G, last), pc, sc);
+
+  fill_pair_lut(cb, lut, tid, blockDim.x);
+
+  if constexpr (kStage) {
+    xst.store(nb * 32, mask, xs, tid, blockDim.x);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t b0 = (uint32_t)(lk + j * TK);
+      const bool inside = b0 < nb;
+      const uint32_t b = min(b0, nb - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 u = *reinterpret_cast<const float4*>(xs + 32 * b + 4 * (q ^ (b & 7)));
+        xr[j][0][4 * q + 0] = inside ? u.x : 0.f;
+        xr[j][0][4 * q + 1] = inside ? u.y : 0.f;
+        xr[j][0][4 * q + 2] = inside ? u.z : 0.f;
+        xr[j][0][4 * q + 3] = inside ? u.w : 0.f;
+      }
+    }
+  } else {
+    // Unrotated activations are rotated per lane while the first tile's
+    // loads are in flight: x' = FWHT32(D x); the 1/sqrt(32) is applied once
+    // to each finished row sum instead of to every element.
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const bool inside = (uint32_t)(lk + j * TK) < nb;
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        if constexpr (kMode >= 2) {
+          apply_signs(xr[j][m], mask);
+          fwht32(xr[j][m]);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xr[j][m][i] = inside ? xr[j][m][i] : 0.f;
+      }
+    }
+    __syncthreads();
+  }
   constexpr float kOutScale = kMode >= 2 ? kInvSqrt32 : 1.0f;
 
-  int parity = 0;
+  // Rows split over WK > 1 wavefronts: each wavefront leaves its partial
+  // sums for tile number i (of this workgroup) in ring slot i % kRing and
+  // runs on; the partials are combined and y written once per kRing tiles
+  // and after the last tile.  Wavefronts thus never wait for each other per
+  // tile (a per-tile barrier would pace every tile by the slowest of the
+  // workgroup's loads).  The tile count is uniform over the workgroup, so
+  // every wavefront reaches the same barriers.
+  const uint32_t t0 = t;
+  uint32_t ti = 0;
+  auto flush = [&](uint32_t first, uint32_t cnt) {
+    __syncthreads();
+    for (uint32_t e = tid; e < cnt * (uint32_t)(S * V); e += blockDim.x) {
+      const uint32_t jl = e / (uint32_t)(S * V), rem = e - jl * (uint32_t)(S * V);
+      const int s2 = (int)rem / V, v2 = (int)rem % V;
+      const uint32_t li = first + jl;
+      const uint32_t row = ((t0 + li * G) * S + s2) * R + v2 / MC;
+      if (row < N) {
+        float sum = 0.f;
+        for (int w = 0; w < WK; ++w) sum += red[li % kRing][s2 * WK + w][v2];
+        y[(v2 % MC) * ldy + row] = sum * kOutScale;
+      }
+    }
+    __syncthreads();                        // the ring slots are rewritten next
+  };
+
   auto do_tile = [&](uint32_t tt, const auto& p, const auto& s) {
     float v[V];
 #pragma unroll
@@ -256,45 +432,62 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
         if (row < N) y[(vi % MC) * ldy + row] = v[0] * kOutScale;
       }
     } else {
-      if (writer) red[parity][slot * WK + wk][vi] = v[0];
-      __syncthreads();
-      if (tid < S * V) {
-        const int s2 = tid / V, v2 = tid % V;
-        const uint32_t row = (tt * S + s2) * R + v2 / MC;
-        if (row < N) {
-          float sum = 0.f;
-          for (int w = 0; w < WK; ++w) sum += red[parity][s2 * WK + w][v2];
-          y[(v2 % MC) * ldy + row] = sum * kOutScale;
-        }
-      }
-      parity ^= 1;
+      if (writer) red[ti % kRing][slot * WK + wk][vi] = v[0];
+      ++ti;
+      if (ti % kRing == 0) flush(ti - kRing, kRing);
     }
   };
 
-  if constexpr (kPrefetch) {
-    // Two tiles in flight per wavefront: ping-pong between register sets (no
-    // copies, which would force a wait on the loads still in flight).
-    // The prefetch is skipped (uniform branch) past the last tile: a wave
-    // cannot retire while loads it issued are still in flight.
-    while (t < tiles) {
-      if (t + G < tiles) load_tile(t + G, pb, sb);
-      __builtin_amdgcn_sched_barrier(0);      // keep the prefetch ahead of this tile's math
+  // Every wavefront walks its n tiles t0, t0 + G, ..., last and keeps the
+  // loads of the next kDepth - 1 tiles in flight: a register set is
+  // reloaded as soon as its tile has been computed.  The loads are
+  // unconditional, with the tile index clamped to `last`, and the loop runs a
+  // trip count fixed up front with the remainder after it (no exit from the
+  // middle of the body): every path that reaches a use of a register set then
+  // carries the same loads, so the compiler's wait counts stay exact.  (A
+  // conditional load or a mid-body exit makes it wait for every outstanding
+  // load, the prefetches included.)  The clamped loads at the end re-read the
+  // last tile (cache hits) and are discarded.
+  if constexpr (kDepth == 1) {
+    for (uint32_t i = 1; i < n; ++i) {
       do_tile(t, pa, sa);
       t += G;
-      if (t >= tiles) break;
-      if (t + G < tiles) load_tile(t + G, pa, sa);
-      __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, pb, sb);
-      t += G;
-    }
-  } else {
-    while (true) {
-      do_tile(t, pa, sa);
-      t += G;
-      if (t >= tiles) break;
       load_tile(t, pa, sa);
     }
+    do_tile(t, pa, sa);
+  } else if constexpr (kDepth == 2) {
+    uint32_t i = 0;
+    for (; i + 2 <= n; i += 2) {
+      do_tile(t, pa, sa);
+      load_tile(min(t + 2 * G, last), pa, sa);
+      __builtin_amdgcn_sched_barrier(0);     // keep the reload ahead of the next tile's math
+      t += G;
+      do_tile(t, pb, sb);
+      load_tile(min(t + 2 * G, last), pb, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      t += G;
+    }
+    if (i < n) do_tile(t, pa, sa);
+  } else {
+    uint32_t i = 0;
+    for (; i + 3 <= n; i += 3) {
+      do_tile(t, pa, sa);
+      load_tile(min(t + 3 * G, last), pa, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      t += G;
+      do_tile(t, pb, sb);
+      load_tile(min(t + 3 * G, last), pb, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      t += G;
+      do_tile(t, pc, sc);
+      load_tile(min(t + 3 * G, last), pc, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      t += G;
+    }
+    if (i < n) do_tile(t, pa, sa);
+    if (i + 1 < n) do_tile(t + G, pb, sb);
   }
+  if (WK > 1 && ti % kRing != 0) flush(ti - ti % kRing, ti % kRing);
 }
 
 // ---------------------------------------------------------------------------
@@ -334,7 +527,7 @@ uint32_t grid_cap(int threads) {
   return (uint32_t)(device_cu_count() * per_cu);
 }
 
-template <int J, int R, int MC, int kMaxT, bool kPrefetch>
+template <int J, int R, int MC, int kMaxT, int kDepth, int kStage = 0>
 void launch_cfg(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x,
                 int64_t ldx, int mode, float* y, int64_t ldy, const Plan& pl, hipStream_t s) {
   const Codebook& cb = host_codebook();
@@ -344,7 +537,7 @@ void launch_cfg(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, ui
   const uint32_t cap = grid_cap(pl.threads);
   const uint32_t grid = tiles < cap ? tiles : cap;
 #define TQ_GEMV_LAUNCH(M_)                                                                                     \
-  hipLaunchKernelGGL((gemv_kernel<J, R, MC, M_, kMaxT, kPrefetch>), dim3(grid), dim3(pl.threads), 0, s, pk, sc, N, \
+  hipLaunchKernelGGL((gemv_kernel<J, R, MC, M_, kMaxT, kDepth, kStage>), dim3(grid), dim3(pl.threads), 0, s, pk, sc, N, \
                      nb, mask, x, ldx, cb, y, ldy, pl.TK, tiles)
   switch (mode) {
     case 0: TQ_GEMV_LAUNCH(0); break;
@@ -355,34 +548,35 @@ void launch_cfg(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, ui
 #undef TQ_GEMV_LAUNCH
 }
 
-// GEMV configuration for one activation row.
-struct GemvConfig {
-  int J;          // K-blocks per lane (1..4)
-  int R;          // rows per wavefront per tile (2 or 4)
-  int max_t;      // workgroup size bound (1024 or 512)
-  bool prefetch;  // second register set for the next tile
-};
-
-// Measured on MI355X over the decode shapes (K = 4096..28672): one K-block
-// per lane, two rows per wavefront per tile and the register prefetch are
-// the fastest choice for every shape; K > 32768 takes more blocks per lane
-// (and no prefetch, which would spill).
-GemvConfig choose_gemv_config(uint32_t nb, uint32_t N) {
-  (void)N;
-  GemvConfig c;
-  c.max_t = 1024;
-  c.J = min_j(nb, c.max_t);
-  c.R = 2;
-  c.prefetch = true;
-  return c;
-}
+// Decode GEMV shape, measured on MI355X over the Llama-3-8B and 70B decode
+// layers: two rows per wavefront per tile, one tile of loads in flight ahead
+// of the one being computed, x' staged in LDS, the fewest K-blocks per lane
+// that fit a row into a 1024-thread workgroup.
+constexpr int kGemvRows = 2;
+constexpr int kGemvDepth = 2;
+constexpr bool kGemvStage = true;
+constexpr int kGemvMinJ = 1;
 
 template <int J>
 void launch_gemv_j(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x,
-                   int mode, float* y, const GemvConfig& c, hipStream_t s) {
-  const Plan pl = plan_for(nb, c.max_t, J);
-  // The second register set only fits without spills at one block per lane.
-  launch_cfg<J, 2, 1, 1024, J == 1>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+                   int mode, float* y, hipStream_t s) {
+  const Plan pl = plan_for(nb, 1024, J);
+  // Groups of 4 elements each thread stages (a power of two, at most 8).
+  const uint32_t K = nb * 32, per = 4u * (uint32_t)pl.threads;
+  const uint32_t passes = (K + per - 1) / per;
+  constexpr int R = kGemvRows, D = kGemvDepth;
+  if constexpr (J <= 2) {
+    if (kGemvStage && K <= (uint32_t)kStageFloats && passes <= 8) {
+      if (passes <= 1) launch_cfg<J, R, 1, 1024, D, 1>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else if (passes <= 2) launch_cfg<J, R, 1, 1024, D, 2>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else if (passes <= 4) launch_cfg<J, R, 1, 1024, D, 4>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else launch_cfg<J, R, 1, 1024, D, 8>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      return;
+    }
+  }
+  // Larger K: every lane loads and rotates its own blocks; the loads of the
+  // next tile only fit in registers (without spills) at one block per lane.
+  launch_cfg<J, 2, 1, 1024, J == 1 ? D : 1>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
 }
 
 }  // namespace
@@ -394,12 +588,12 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N,
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
   const uint8_t* xb = static_cast<const uint8_t*>(x);
-  const GemvConfig c = choose_gemv_config(nb, (uint32_t)N);
-  switch (c.J) {
-    case 1: launch_gemv_j<1>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, c, s); break;
-    case 2: launch_gemv_j<2>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, c, s); break;
-    case 3: launch_gemv_j<3>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, c, s); break;
-    default: launch_gemv_j<4>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, c, s); break;
+  const int J = min_j(nb, 1024) > kGemvMinJ ? min_j(nb, 1024) : kGemvMinJ;
+  switch (J) {
+    case 1: launch_gemv_j<1>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
+    case 2: launch_gemv_j<2>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
+    case 3: launch_gemv_j<3>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
+    default: launch_gemv_j<4>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
   }
   return hipGetLastError();
 }
@@ -421,19 +615,19 @@ hipError_t launch_gemm_valu(const uint8_t* packed, const uint16_t* scales, int64
     float* ym = y + m0 * ldy;
     if (left >= 4 && nb <= 256) {
       const Plan pl = plan_for(nb, 256, 1);
-      launch_cfg<1, 2, 4, 256, false>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s);
+      launch_cfg<1, 2, 4, 256, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s);
       m0 += 4;
     } else if (left >= 2 && nb <= 512) {
       const Plan pl = plan_for(nb, 512, 1);
-      launch_cfg<1, 2, 2, 512, false>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s);
+      launch_cfg<1, 2, 2, 512, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s);
       m0 += 2;
     } else {
       const Plan pl = plan_for(nb, 1024, min_j(nb, 1024));
       switch (pl.J) {
-        case 1: launch_cfg<1, 2, 1, 1024, false>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-        case 2: launch_cfg<2, 2, 1, 1024, false>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-        case 3: launch_cfg<3, 2, 1, 1024, false>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-        default: launch_cfg<4, 2, 1, 1024, false>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
+        case 1: launch_cfg<1, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
+        case 2: launch_cfg<2, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
+        case 3: launch_cfg<3, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
+        default: launch_cfg<4, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
       }
       m0 += 1;
     }
