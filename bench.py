@@ -105,24 +105,16 @@ def main():
         # 2K and writes 4K bytes, then the GEMV reads the 4K-byte x'
         step_bytes += L * (gemv_bytes(n, k, 2) if not args.prerotate else gemv_bytes(n, k, 4) + 6 * k)
 
-    def step(events=None):
+    def step():
         for layer in range(L):
             for gname in groups:
                 packed, scales = model[layer][gname]
                 x = xs[layer][gname]
-                if (not args.prerotate):
-                    if events is not None:
-                        events.append((gname, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-                        events[-1][1].record(stream)
+                if not args.prerotate:
                     tqa.gemv(packed, scales, x, out=y_buf[gname])
                 else:
                     xr = tqa.rotate(x, out=xr_buf[gname])
-                    if events is not None:
-                        events.append((gname, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
-                        events[-1][1].record(stream)
                     tqa.gemv(packed, scales, xr, rotated=True, out=y_buf[gname])
-                if events is not None:
-                    events[-1][2].record(stream)
 
     # --------------------------------------------------------------- timed
     # The step's launches are captured once into a HIP graph (torch.cuda.graph
@@ -160,29 +152,52 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ------------------------------------------------- per-launch GEMV timing
-    per = {g: [] for g in groups}
-    for _ in range(3):
-        ev = []
-        step(ev)
-        torch.cuda.synchronize()
-        for gname, a, b in ev:
-            per[gname].append(a.elapsed_time(b))
-    gemv_launch_bytes = 0.0
-    gemv_launch_ms = 0.0
-    per_group = {}
+    # Each group's 32 launches (one per layer) are captured in a graph of
+    # their own and replayed between two events on the launch stream: the
+    # average launch duration of each GEMV shape.
     xb = 2 if not args.prerotate else 4
+    per_group = {}
+    group_ms = {}
     for gname, (n, k) in groups.items():
-        ms = sum(per[gname]) / len(per[gname])
+        def group_step(gname=gname):
+            for layer in range(L):
+                packed, scales = model[layer][gname]
+                x = xs[layer][gname]
+                if not args.prerotate:
+                    tqa.gemv(packed, scales, x, out=y_buf[gname])
+                else:
+                    tqa.gemv(packed, scales, tqa.rotate(x, out=xr_buf[gname]), rotated=True, out=y_buf[gname])
+        if args.no_graph:
+            ms = _time(torch, stream, group_step, 5) / L
+        else:
+            gg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gg):
+                group_step()
+            ms = _time(torch, stream, gg.replay, 5) / L
+            del gg
+        group_ms[gname] = ms
         per_group[gname] = {"N": n, "K": k, "us": round(ms * 1e3, 2),
                             "GB_s": round(gemv_bytes(n, k, xb) / (ms * 1e-3) / 1e9, 1)}
-        gemv_launch_bytes += gemv_bytes(n, k, xb)
-        gemv_launch_ms += ms
-    achieved = gemv_launch_bytes / (gemv_launch_ms * 1e-3) / 1e9
-    layer_kernel_ms = gemv_launch_ms          # the four group launches of one layer
+    # Roofline of the dominant kernel: the instantiation that serves the
+    # K = 4096 groups (q|k|v, o, gate|up: 96 of the 128 launches of a step and
+    # 72% of its bytes); down (K = 14336) stages its activation in four
+    # passes per thread and is a separate instantiation.
+    dom = [g for g, (n, k) in groups.items() if k == 4096]
+    dom_bytes = sum(gemv_bytes(groups[g][0], groups[g][1], xb) for g in dom)
+    dom_ms = sum(group_ms[g] for g in dom)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    layer_kernel_ms = sum(group_ms.values())   # the four group launches of one layer
+    # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
+    # or None when it was taken from other kernel sources than these.
+    from dequant_gemv_tq_amd import profiling as tq_profiling
+    rec = tq_profiling.read_record(os.path.join(ROOT, "profiles", "gemv_traffic_llama8b.md"))
+    traffic = rec["traffic_bytes_per_launch"] if (rec and not args.prerotate) else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "gemv_kernel (fused TQ4_1S GEMV)", "launches_per_step": 4 * L,
-                "bytes_per_launch_avg": round(gemv_launch_bytes / 4), "avg_launch_us": round(gemv_launch_ms / 4 * 1e3, 2)}
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_kernel<1, 2, 1, 3, 1024, 2, 1> (fused TQ4_1S GEMV, bf16 x, K = 4096)",
+                "groups": dom, "launches_per_step": len(dom) * L,
+                "bytes_per_launch_avg": round(dom_bytes / len(dom)),
+                "avg_launch_us": round(dom_ms / len(dom) * 1e3, 2)}
 
     out = {
         "metric": "fused TQ4_1S GEMV achieved HBM GB/s (% of peak) at batch 1; quantize GB/s",

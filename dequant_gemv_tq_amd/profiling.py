@@ -1,0 +1,209 @@
+"""rocprofv3 summaries of the decode GEMV: HBM traffic and kernel durations.
+
+HBM traffic, from the repository root:
+
+    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch -- python3 -m dequant_gemv_tq_amd.profiling run
+    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write -- python3 -m dequant_gemv_tq_amd.profiling run
+    python3 -m dequant_gemv_tq_amd.profiling summarize OUT/fetch/fetch_results.db OUT/write/write_results.db \\
+        > profiles/gemv_traffic_llama8b.md
+
+Kernel durations of a benchmark run:
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- \\
+        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
+    python3 -m dequant_gemv_tq_amd.profiling stats OUT/trace/bench_kernel_stats.csv > profiles/...md
+
+``run`` launches, in this order: a plain elementwise copy (negation) of
+1 GiB (calibration: it reads and writes exactly 1 GiB), then for each Llama-3-8B decode group
+(q|k|v, o, gate|up, down) eight fused GEMVs over eight distinct copies of one
+quantized layer with a bf16 activation.  ``summarize`` reads the two
+counter databases, turns the KiB per dispatch of each counter into bytes with
+the factor the copy kernel gives (known bytes / counted bytes) and writes a
+short Markdown summary ending in one JSON line that the benchmark reads.  The
+JSON carries the SHA-256 of the GEMV sources, so that a number taken before a
+kernel change is not reported for the changed kernel.
+"""
+
+from __future__ import annotations
+
+import hashlib
+import json
+import os
+import sqlite3
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+GROUPS = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
+MEMBERS = {"qkv": ["q", "k", "v"], "o": ["o"], "gate_up": ["gate", "up"], "down": ["down"]}
+COPIES = 8
+COPY_BYTES = 1 << 30
+DOMINANT = ("qkv", "o", "gate_up")          # groups served by the K = 4096 instantiation
+SOURCES = ("csrc/tq_gemv.hip", "csrc/tq_internal.hpp")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(n: int, k: int, x_bytes: int = 2) -> int:
+    """Packed nibbles + fp16 scales + activation + fp32 output of one GEMV."""
+    return n * k // 2 + n * k // 16 * 2 + k * x_bytes + n * 4
+
+
+def run() -> None:
+    sys.path.insert(0, ROOT)
+    import torch
+    import dequant_gemv_tq_amd as tqa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)             # an elementwise kernel (copy_ may become a DMA transfer)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+    for gname, (n, k) in GROUPS.items():
+        W = torch.cat([wl.llama8b_weight(t, 0, dev) for t in MEMBERS[gname]], dim=0)
+        p, s = tqa.quantize(W)
+        del W
+        reps = [(p.clone(), s.clone()) for _ in range(COPIES)]
+        x = wl.activation(1, k, wl.generator(wl.seed_of(2, 0, 50), dev), dev, torch.bfloat16)[0].contiguous()
+        y = torch.empty(n, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for pp, ss in reps:
+            tqa.gemv(pp, ss, x, out=y)
+        torch.cuda.synchronize()
+        del reps, p, s
+        torch.cuda.empty_cache()
+    print("traffic run done", flush=True)
+
+
+def _per_dispatch(db: str, counter: str):
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select dispatch_id, kernel_name, sum(value) from counters_collection where counter_name = ? "
+        "group by dispatch_id, kernel_name order by dispatch_id", (counter,)).fetchall()
+    con.close()
+    return [(d, name, v) for d, name, v in rows]
+
+
+def _split(rows):
+    copies = [v for _, name, v in rows if "neg_kernel" in name]
+    gemv = [(name, v) for _, name, v in rows if "gemv_kernel" in name]
+    if len(gemv) != COPIES * len(GROUPS):
+        raise RuntimeError(f"expected {COPIES * len(GROUPS)} GEMV dispatches, found {len(gemv)}")
+    per = {}
+    for i, gname in enumerate(GROUPS):
+        chunk = gemv[i * COPIES:(i + 1) * COPIES]
+        per[gname] = (chunk[0][0], statistics.median(v for _, v in chunk))
+    if not copies:
+        raise RuntimeError("calibration copy (negation kernel) not found")
+    return statistics.median(copies), per
+
+
+def summarize(fetch_db: str, write_db: str) -> None:
+    f_copy, f_per = _split(_per_dispatch(fetch_db, "FETCH_SIZE"))
+    w_copy, w_per = _split(_per_dispatch(write_db, "WRITE_SIZE"))
+    kib = COPY_BYTES / 1024
+    f_scale = kib / f_copy
+    w_scale = kib / w_copy
+    lines = [
+        "# Decode GEMV HBM traffic (Llama-3-8B groups, bf16 activation, fused rotation)",
+        "",
+        "Commands (repository root on the GPU host; OUT is any scratch folder):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch -- python3 -m dequant_gemv_tq_amd.profiling run",
+        "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write -- python3 -m dequant_gemv_tq_amd.profiling run",
+        "python3 -m dequant_gemv_tq_amd.profiling summarize OUT/fetch/fetch_results.db OUT/write/write_results.db",
+        "```",
+        "",
+        f"Calibration: a 1 GiB elementwise copy reads FETCH_SIZE = {f_copy:.0f} KiB and WRITE_SIZE = {w_copy:.0f} KiB "
+        f"per dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write) turn counted KiB into bytes.",
+        "",
+        "| group | N x K | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB (scaled) | algorithmic MB | ratio |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    dom_t = dom_a = 0.0
+    for gname, (n, k) in GROUPS.items():
+        fk = f_per[gname][1]
+        wk = w_per[gname][1]
+        t = (fk * f_scale + wk * w_scale) * 1024
+        alg = algorithmic_bytes(n, k)
+        if gname in DOMINANT:
+            dom_t += t
+            dom_a += alg
+        lines.append(f"| {gname} | {n} x {k} | {fk:.0f} | {wk:.0f} | {t / 1e6:.2f} | {alg / 1e6:.2f} | {t / alg:.3f} |")
+    rec = {"kernel": "gemv_kernel<1, 2, 1, 3, 1024, 2, 1>", "groups": list(DOMINANT),
+           "traffic_bytes_per_launch": round(dom_t / len(DOMINANT)),
+           "algorithmic_bytes_per_launch": round(dom_a / len(DOMINANT)),
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "source_sha256": source_hash()}
+    lines += ["", "Per launch of the dominant instantiation (mean over q|k|v, o, gate|up):", "",
+              f"traffic-json: {json.dumps(rec)}", ""]
+    print("\n".join(lines))
+
+
+TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- "
+                 "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline")
+
+
+def stats(csv_path: str) -> None:
+    """Markdown table of the library's kernels from a rocprofv3 kernel_stats.csv."""
+    import csv
+    import re
+    rows = list(csv.DictReader(open(csv_path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["# Kernel durations of the benchmark (Llama-3-8B decode stream and secondary rows)", "",
+             "Command (repository root on the GPU host; OUT is any scratch folder):", "", "```",
+             TRACE_COMMAND, "python3 -m dequant_gemv_tq_amd.profiling stats OUT/trace/bench_kernel_stats.csv",
+             "```", "",
+             "Library kernels (`tq::`), from rocprofv3's kernel statistics; durations in microseconds.", "",
+             "| kernel | calls | average | min | max | share of all GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        m = re.search(r"tq::\(anonymous namespace\)::(\w+(?:<[^>]*>)?)", r["Name"])
+        if not m:
+            continue
+        lines.append(f"| `{m.group(1)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.2f}% |")
+    lines += ["", "The decode GEMV of the q|k|v, o and gate|up groups (K = 4096, bf16 activation, rotation "
+              "fused) is `gemv_kernel<1, 2, 1, 3, 1024, 2, 1>`; down (K = 14336) is "
+              "`gemv_kernel<1, 2, 1, 3, 1024, 2, 4>`.  Other kernels: the quantizer, the small-batch GEMM "
+              "(VALU `gemv_kernel<..., MC, 1, ...>` for M < 16, `gemm_mfma_kernel` for M >= 16), "
+              "dequantization and the NVFP4 / MXFP6 rows; the remaining GPU time is PyTorch drawing the "
+              "synthetic weights.", ""]
+    print("\n".join(lines))
+
+
+def read_record(path: str) -> dict | None:
+    """The JSON line of a summary, or None when absent or taken from other sources."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    return rec if rec.get("source_sha256") == source_hash() else None
+    except OSError:
+        return None
+    return None
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "run":
+        run()
+    elif len(sys.argv) == 4 and sys.argv[1] == "summarize":
+        summarize(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 3 and sys.argv[1] == "stats":
+        stats(sys.argv[2])
+    else:
+        print(__doc__)
+        sys.exit(2)
