@@ -1,0 +1,135 @@
+"""Full-size parity on sampled outputs, in the launch configurations the benchmark times.
+
+The decode layers of the Llama-3-8B, 27B (hidden 5120 / intermediate 17408) and
+Llama-3-70B shapes, with the q|k|v and gate|up row groups concatenated as one
+launch sees them:
+
+* TQ4_1S quantize: packed nibbles and fp16 scales of sampled rows bit-exact
+  against the oracle's canonical float32 quantizer;
+* the fused GEMV with a bf16 activation (rotation fused, as benchmarked):
+  sampled y within |dy| <= 1e-3 * sum_k |W_deq[n,k] x[k]| of the float64 oracle
+  on the GPU's own packed weights;
+* tq_gemm at M = 4, 16, 64 on pre-rotated bf16 activations (8B gate|up, down);
+* NVFP4 and MXFP6 quantize + GEMV (M = 1 and 8) on the 27B MLP shapes, codes
+  and block scales of sampled rows bit-exact.  The NVFP4 tensor scale depends
+  on the whole tensor: its amax is taken on the host from the full weight and
+  handed to the oracle as one extra row, so that the oracle applies its own
+  definition to the same maximum.
+
+Sampled rows: the first two, the middle, the last and twelve seeded ones.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_tq_amd as tqa
+from oracle import blockfp as obf
+from oracle import tq4_1s as otq
+import workloads
+from gpu_helpers import say, u16, f32np, assert_within
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+TQ_SHAPES = [
+    ("8B q|k|v", 6144, 4096), ("8B o", 4096, 4096), ("8B gate|up", 28672, 4096), ("8B down", 4096, 14336),
+    ("27B q|k|v", 7168, 5120), ("27B gate|up", 34816, 5120), ("27B down", 5120, 17408),
+    ("70B q|k|v", 10240, 8192), ("70B o", 8192, 8192), ("70B gate|up", 57344, 8192), ("70B down", 8192, 28672),
+]
+
+
+def sample_rows(n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = {0, min(1, n - 1), n // 2, n - 1}
+    rows.update(int(r) for r in rng.integers(0, n, 12))
+    return np.array(sorted(rows))
+
+
+def _weight(n, k, seed, variant="gauss"):
+    g = workloads.generator(seed, DEV)
+    if variant == "t4":
+        return workloads.student_t4_weight(n, k, g, DEV, torch.bfloat16)
+    return workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+
+
+@pytest.mark.parametrize("label,n,k", TQ_SHAPES, ids=[s[0] for s in TQ_SHAPES])
+def test_tq4_full_size_quantize_and_fused_gemv(label, n, k):
+    seed = n * 131 + k
+    W = _weight(n, k, seed, "t4" if n % 3 == 0 else "gauss")
+    x = workloads.activation(1, k, workloads.generator(seed + 1, DEV), DEV, torch.bfloat16)[0].contiguous()
+    say(f"[full] {label} {n}x{k} quantize + gemv(bf16 x, fused rotation)")
+    packed, scales = tqa.quantize(W)
+    y = tqa.gemv(packed, scales, x)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, seed)
+    idx = torch.as_tensor(rows, device=DEV)
+    Wh = W.index_select(0, idx).float().cpu().numpy()
+    op, osc = otq.quantize_o32(Wh)
+    gp = packed.index_select(0, idx).cpu().numpy()
+    gs = u16(scales.index_select(0, idx))
+    np.testing.assert_array_equal(gs, osc, err_msg=f"scales {label}")
+    np.testing.assert_array_equal(gp, op, err_msg=f"packed {label}")
+    yr, a = otq.gemv_rows_o64(gp, gs, x.float().cpu().numpy())
+    worst = assert_within(f32np(y)[rows], yr, a, what=f"gemv {label}")
+    assert worst < 1e-4
+    y2 = tqa.gemv(packed, scales, x)
+    assert torch.equal(y, y2), f"{label}: a second launch differs"
+
+
+@pytest.mark.parametrize("m", [4, 16, 64])
+@pytest.mark.parametrize("label,n,k", [TQ_SHAPES[2], TQ_SHAPES[3]], ids=["8B gate|up", "8B down"])
+def test_tq4_full_size_gemm(label, n, k, m):
+    seed = n + k + m
+    W = _weight(n, k, seed)
+    X = workloads.activation(m, k, workloads.generator(seed + 1, DEV), DEV, torch.bfloat16)
+    say(f"[full] {label} {n}x{k} gemm M={m}")
+    packed, scales = tqa.quantize(W)
+    Y = tqa.gemm(packed, scales, tqa.rotate(X, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    rows = sample_rows(n, seed)
+    idx = torch.as_tensor(rows, device=DEV)
+    yr, a = otq.gemm_o64(packed.index_select(0, idx).cpu().numpy(), u16(scales.index_select(0, idx)),
+                         X.float().cpu().numpy())
+    assert_within(f32np(Y)[:, rows], yr, a, what=f"gemm {label} M={m}")
+
+
+def _host_amax(W: torch.Tensor) -> np.float32:
+    best = np.float32(0)
+    for r0 in range(0, W.shape[0], 4096):
+        best = max(best, np.abs(W[r0:r0 + 4096].float().cpu().numpy()).max())
+    return np.float32(best)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+@pytest.mark.parametrize("label,n,k", [("27B gate|up", 34816, 5120), ("27B down", 5120, 17408)],
+                         ids=["27B gate|up", "27B down"])
+def test_blockfp_full_size(fmt, label, n, k):
+    seed = n * 7 + k + (0 if fmt == "nvfp4" else 1)
+    g = workloads.generator(seed, DEV)
+    W = workloads.add_outliers(workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.float32), 0.001, 20.0, g)
+    W = W.to(torch.bfloat16)
+    say(f"[full] {fmt} {label} {n}x{k} quantize + gemm M=1, 8")
+    codes, bs, ts = tqa.blockfp_quantize(fmt, W)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, seed)
+    idx = torch.as_tensor(rows, device=DEV)
+    Wh = W.index_select(0, idx).float().cpu().numpy()
+    if fmt == "nvfp4":
+        extra = np.zeros((1, k), np.float32)
+        extra[0, 0] = _host_amax(W)
+        oc, osb, ost = obf.nvfp4_quantize_o32(np.concatenate([Wh, extra]))
+        oc, osb = oc[:-1], osb[:-1]
+        assert np.float32(ts.cpu().numpy()[0]).view(np.uint32) == np.float32(ost).view(np.uint32)
+        Wd = obf.nvfp4_dequantize_o64(oc, osb, ost)
+    else:
+        oc, osb = obf.mxfp6_quantize_o32(Wh)
+        Wd = obf.mxfp6_dequantize_o64(oc, osb)
+    np.testing.assert_array_equal(bs.index_select(0, idx).cpu().numpy(), osb, err_msg=f"{fmt} block scales")
+    np.testing.assert_array_equal(codes.index_select(0, idx).cpu().numpy(), oc, err_msg=f"{fmt} codes")
+    for m in (1, 8):
+        X = workloads.activation(m, k, workloads.generator(seed + m, DEV), DEV, torch.bfloat16)
+        Y = tqa.blockfp_gemm(fmt, codes, bs, ts, X)
+        torch.cuda.synchronize()
+        yr, a = obf.gemm_deq_o64(Wd, X.float().cpu().numpy())
+        assert_within(f32np(Y)[:, rows], yr, a, what=f"{fmt} {label} M={m}")
