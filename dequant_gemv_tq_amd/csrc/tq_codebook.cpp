@@ -1,15 +1,12 @@
-// Host-side constants: the 16-level Lloyd-Max codebook for N(0,1) and the
-// splitmix64 sign mask.
+// Host-side constants: the 16-level Lloyd-Max codebook for N(0,1) with its
+// 15 decision thresholds, and the splitmix64 sign mask.
 //
 // TQ4 page ("企业官网建设流程全解析", hotelren.com/news/5458160), "格式原理"
 // item 2 and the paragraph after the list: rotated coordinates are quantized
 // one by one to the nearest optimal N(0,1) centroid; the codebook comes from
-// Lloyd's algorithm.  The normal law is symmetric, so the fixed point is
-// symmetric and only the 8 positive centroids are iterated: the innermost
-// positive cell starts at the boundary 0, every other boundary is the
-// midpoint of its neighbours, and each centroid moves to the conditional
-// mean of its cell, (phi(a) - phi(b)) / (Phi(b) - Phi(a)).
-#include <cmath>
+// Lloyd's algorithm.  The centroids are the float32 constants of
+// tq_internal.hpp; a threshold is the midpoint of two neighbouring float32
+// centroids, formed in float64 and rounded once to float32.
 #include <mutex>
 
 #include "tq_internal.hpp"
@@ -17,39 +14,9 @@
 namespace tq {
 namespace {
 
-double normal_pdf(double x) {
-  if (std::isinf(x)) return 0.0;
-  return std::exp(-0.5 * x * x) * 0.39894228040143267794;   // 1/sqrt(2 pi)
-}
-
-// Upper-tail probability Q(x) = P(X > x) = erfc(x / sqrt 2) / 2, accurate for x >= 0.
-double upper_tail(double x) { return 0.5 * std::erfc(x * 0.70710678118654752440); }
-
 Codebook build_codebook() {
-  constexpr int kPos = 8;
-  double c[kPos];
-  for (int k = 0; k < kPos; ++k) c[k] = 0.25 + 0.3 * k;      // any increasing positive start
-  for (int it = 0; it < 1000000; ++it) {
-    double lo[kPos], hi[kPos];
-    for (int k = 0; k < kPos; ++k) {
-      lo[k] = (k == 0) ? 0.0 : 0.5 * (c[k - 1] + c[k]);
-      hi[k] = (k == kPos - 1) ? INFINITY : 0.5 * (c[k] + c[k + 1]);
-    }
-    double change = 0.0;
-    for (int k = 0; k < kPos; ++k) {
-      double mass = upper_tail(lo[k]) - upper_tail(hi[k]);
-      double nc = (normal_pdf(lo[k]) - normal_pdf(hi[k])) / mass;
-      change = std::fmax(change, std::fabs(nc - c[k]));
-      c[k] = nc;
-    }
-    if (change < 1e-15) break;
-  }
   Codebook cb;
-  for (int k = 0; k < kPos; ++k) {
-    float f = (float)c[k];
-    cb.c[8 + k] = f;
-    cb.c[7 - k] = -f;
-  }
+  for (int k = 0; k < 16; ++k) cb.c[k] = centroid(k);
   for (int k = 0; k < 15; ++k) cb.m[k] = (float)(((double)cb.c[k] + (double)cb.c[k + 1]) * 0.5);
   return cb;
 }

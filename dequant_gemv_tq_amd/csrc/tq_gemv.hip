@@ -142,31 +142,26 @@ __device__ __forceinline__ void decode_block(const uint4& p, uint32_t sc, const 
   for (int m = 0; m < MC; ++m) acc[m] = __builtin_fmaf(d0, a[m][0], __builtin_fmaf(d1, a[m][1], acc[m]));
 }
 
-// Pair table fill straight from the codebook argument (scalar registers): no
-// staging through LDS and no barrier before it.  Wavefront w (of 16 virtual
-// ones) writes entries e = 16 w + 4 u + lane / 16 (u < 4), copies
-// 2 (lane % 16) and 2 (lane % 16) + 1, so the high centroid c[e / 16] =
-// c[w] is a wavefront-uniform choice and the low one c[e % 16] = c[4 u +
-// lane / 16] a per-lane choice of four.  Consecutive lanes
-// store consecutive 16-byte chunks of the table (no bank conflicts).
-__device__ __forceinline__ void fill_pair_lut(const Codebook& cb, uint8_t* lut, int tid, int nthreads) {
-  // readfirstlane makes each centroid an opaque register value, so the
-  // selects below stay selects (a select between two argument loads is
-  // otherwise folded into one load from a selected address, which copies
-  // the argument to scratch memory).
-  float c[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) c[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cb.c[k])));
+// Pair table fill from the codebook constants (immediates: nothing waits on
+// memory).  Wavefront w (of 16 virtual ones) writes entries e = 16 w + 4 u +
+// lane / 16 (u < 4), copies 2 (lane % 16) and 2 (lane % 16) + 1, so the high
+// centroid c[e / 16] = c[w] is a wavefront-uniform choice and the low one
+// c[e % 16] = c[4 u + lane / 16] a per-lane choice of four.  Consecutive
+// lanes store consecutive 16-byte chunks of the table (no bank conflicts).
+__device__ __forceinline__ void fill_pair_lut(uint8_t* lut, int tid, int nthreads) {
   const int lane = tid & 63, g = lane >> 4;
   for (int w = tid >> 6; w < 16; w += nthreads >> 6) {
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    float hi = c[0];
+    float hi = centroid(0);
 #pragma unroll
-    for (int k = 1; k < 16; ++k) hi = wu == k ? c[k] : hi;
+    for (int k = 1; k < 16; ++k) hi = wu == k ? centroid(k) : hi;
     uint8_t* base = lut + ((16 * wu + g) << 8) + 16 * (lane & 15);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float lo = g == 0 ? c[4 * u] : g == 1 ? c[4 * u + 1] : g == 2 ? c[4 * u + 2] : c[4 * u + 3];
+      const float lo = g == 0   ? centroid(4 * u)
+                       : g == 1 ? centroid(4 * u + 1)
+                       : g == 2 ? centroid(4 * u + 2)
+                                : centroid(4 * u + 3);
       *reinterpret_cast<float4*>(base + (u << 10)) = make_float4(lo, hi, lo, hi);
     }
   }
@@ -259,6 +254,20 @@ constexpr int kStageFloats = 20480;
 // Tiles whose cross-wavefront partial sums wait in LDS before being combined.
 constexpr int kRing = 32;
 
+// Work split of one launch, fixed on the host so that the prologue has no
+// integer division: TK lanes per row slot (a multiple of 64), S slots per
+// workgroup (S * TK threads), slot of wavefront w = (w * slot_mul) >> 8
+// (exact for the at most 16 wavefronts of a workgroup), and workgroup g of G
+// takes tiles g, g + G, ... : q + (g < r) of them.
+struct GemvGrid {
+  int TK;
+  int S;
+  uint32_t slot_mul;
+  uint32_t G;
+  uint32_t q;
+  uint32_t r;
+};
+
 // kMode: 0 = x' fp32, 1 = x' bf16, 2 = raw fp32 x, 3 = raw bf16 x (rotated in the prologue).
 // kStage: stage x' in LDS once per workgroup with kStage groups of 4
 // elements per thread (MC == 1, K <= kStageFloats); 0: every lane loads and
@@ -270,8 +279,7 @@ template <int J, int R, int MC, int kMode, int kMaxT, int kDepth, int kStage>
 __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ packed,
                                                      const uint32_t* __restrict__ scales, uint32_t N, uint32_t nb,
                                                      uint32_t mask, const uint8_t* __restrict__ x, int64_t ldx,
-                                                     Codebook cb, float* __restrict__ y, int64_t ldy, int TK,
-                                                     uint32_t tiles) {
+                                                     float* __restrict__ y, int64_t ldy, GemvGrid gg) {
   constexpr int V = R * MC;
   static_assert(V == 1 || V == 2 || V == 4 || V == 8, "R * MC must be 1, 2, 4 or 8");
   constexpr bool kXbf16 = kMode == 1 || kMode == 3;
@@ -292,11 +300,12 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   // TK is a multiple of 64, so the row slot and the wavefront's place along
   // K are wavefront-uniform: readfirstlane lets the row addressing run on
   // the scalar unit.
-  const int slot = __builtin_amdgcn_readfirstlane(tid / TK);   // row slot of this thread
+  const int TK = gg.TK, S = gg.S, nthreads = S * TK;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = (int)(((uint32_t)wave * gg.slot_mul) >> 8);   // row slot of this thread
   const int lk = tid - slot * TK;             // lane index along K
   const int wk = lk >> 6;                     // wavefront index along K within the slot
   const int WK = TK >> 6;
-  const int S = blockDim.x / TK;
   const uint32_t laneoff = (uint32_t)(lane & (kCopies - 1)) * 8u;
 
   // Loads are branch-free: indices are clamped into the tensor, so a lane
@@ -324,15 +333,15 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
 
   // The first kDepth tiles' weights and the activation are requested before
   // anything else so that their latency overlaps the table fill.
-  const uint32_t G = gridDim.x;
+  const uint32_t G = gg.G;
   uint32_t t = blockIdx.x;
-  const uint32_t last = t + (tiles - 1 - t) / G * G;   // this workgroup's last tile
-  const uint32_t n = (last - t) / G + 1;               // and its tile count
+  const uint32_t n = gg.q + (t < gg.r ? 1u : 0u);      // this workgroup's tile count
+  const uint32_t last = t + (n - 1) * G;               // and its last tile
 
   float xr[J][MC][32];
   ActivationStage<kMode, kStage ? kStage : 1> xst;
   if constexpr (kStage) {
-    xst.load(x, nb * 32, tid, blockDim.x);
+    xst.load(x, nb * 32, tid, nthreads);
   } else {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -345,10 +354,10 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   if constexpr (kDepth >= 2) load_tile(min(t + G, last), pb, sb);
   if constexpr (kDepth >= 3) load_tile(min(t + 2 * G, last), pc, sc);
 
-  fill_pair_lut(cb, lut, tid, blockDim.x);
+  fill_pair_lut(lut, tid, nthreads);
 
   if constexpr (kStage) {
-    xst.store(nb * 32, mask, xs, tid, blockDim.x);
+    xst.store(nb * 32, mask, xs, tid, nthreads);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   uint32_t ti = 0;
   auto flush = [&](uint32_t first, uint32_t cnt) {
     __syncthreads();
-    for (uint32_t e = tid; e < cnt * (uint32_t)(S * V); e += blockDim.x) {
+    for (uint32_t e = tid; e < cnt * (uint32_t)(S * V); e += (uint32_t)nthreads) {
       const uint32_t jl = e / (uint32_t)(S * V), rem = e - jl * (uint32_t)(S * V);
       const int s2 = (int)rem / V, v2 = (int)rem % V;
       const uint32_t li = first + jl;
@@ -530,15 +539,25 @@ uint32_t grid_cap(int threads) {
 template <int J, int R, int MC, int kMaxT, int kDepth, int kStage = 0>
 void launch_cfg(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x,
                 int64_t ldx, int mode, float* y, int64_t ldy, const Plan& pl, hipStream_t s) {
-  const Codebook& cb = host_codebook();
   const int S = pl.threads / pl.TK;
   const uint32_t rows_per_tile = (uint32_t)(S * R);
   const uint32_t tiles = (N + rows_per_tile - 1) / rows_per_tile;
+  // As many workgroups as fit the chip, trimmed so that every workgroup gets
+  // the same number of tiles or one fewer (a round of 1.5 tiles per CU would
+  // leave half the chip idle for the second half of the launch).
   const uint32_t cap = grid_cap(pl.threads);
-  const uint32_t grid = tiles < cap ? tiles : cap;
+  const uint32_t per_wg = (tiles + cap - 1) / cap;
+  const uint32_t grid = (tiles + per_wg - 1) / per_wg;
+  GemvGrid gg;
+  gg.TK = pl.TK;
+  gg.S = S;
+  gg.slot_mul = (256u * 64u + (uint32_t)pl.TK - 1u) / (uint32_t)pl.TK;   // ceil(256 / WK)
+  gg.G = grid;
+  gg.q = tiles / grid;
+  gg.r = tiles % grid;
 #define TQ_GEMV_LAUNCH(M_)                                                                                     \
   hipLaunchKernelGGL((gemv_kernel<J, R, MC, M_, kMaxT, kDepth, kStage>), dim3(grid), dim3(pl.threads), 0, s, pk, sc, N, \
-                     nb, mask, x, ldx, cb, y, ldy, pl.TK, tiles)
+                     nb, mask, x, ldx, y, ldy, gg)
   switch (mode) {
     case 0: TQ_GEMV_LAUNCH(0); break;
     case 1: TQ_GEMV_LAUNCH(1); break;

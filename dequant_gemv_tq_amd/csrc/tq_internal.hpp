@@ -17,6 +17,19 @@ constexpr int kBlock = 32;           // TQ4_1S block length
 constexpr int kHalf = 16;            // elements per scale (d0: 0-15, d1: 16-31)
 constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;   // float32(1/sqrt(32)) = 0x3E3504F3
 
+// The 16-level Lloyd-Max quantizer for N(0,1) (TQ4 page, "格式原理" item 2 and
+// the paragraph after the list): the 8 positive centroids rounded to float32,
+// ascending; the law is symmetric, so centroid k < 8 is -kCentroidPos[7 - k].
+// They are the fixed point of Lloyd's iteration (cell boundaries at the
+// midpoints, each centroid the conditional mean (phi(a) - phi(b)) / (Phi(b) -
+// Phi(a)) of its cell) iterated in float64 to a change below 1e-15 and
+// rounded once; every value sits well away from a float32 rounding boundary.
+// Device code uses them as immediates, so no kernel reads a codebook from
+// memory.
+constexpr float kCentroidPos[8] = {0x1.06f3fap-3f, 0x1.8d5c88p-2f, 0x1.5042bcp-1f, 0x1.e27a72p-1f,
+                                   0x1.41985ep+0f, 0x1.9e384ap+0f, 0x1.08d58ep+1f, 0x1.5dc57ep+1f};
+__host__ __device__ constexpr float centroid(int k) { return k < 8 ? -kCentroidPos[7 - k] : kCentroidPos[k - 8]; }
+
 // Codebook handed to kernels by value (kernel-argument segment, read through
 // the scalar cache): 16 ascending centroids and the 15 midpoint thresholds.
 struct Codebook {
