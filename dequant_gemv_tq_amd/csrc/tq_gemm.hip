@@ -6,20 +6,29 @@
 //
 // For M >= 16 the contraction is dense enough for the matrix cores:
 // v_mfma_f32_16x16x32_bf16 computes a 16(m) x 16(n) tile over 32 k.
-//   * B operand (weights): lane l holds row n = l % 16 of the n-tile and the
-//     k-slot group g = l / 16.  One 16-byte load gives a lane the 32 nibbles
-//     of block b0 + g of its row; dword s of that load feeds MFMA step s, so
-//     every weight is loaded once and dequantized once (lookup, scale, round
-//     to bf16) straight into the operand registers -- no LDS staging.
-//   * A operand (activations): the same (g, s) k-assignment, i.e. lane l
-//     loads 8 consecutive bf16 of X'[m = l % 16] at element 32 (b0 + g) + 8 s.
-//     An MFMA only pairs A and B slots of the same lane group, so any k
-//     permutation shared by A and B gives the same sum.
-//   * Output: lane l, register r holds D[4 (l / 16) + r][l % 16].
-//   * A workgroup is 4 wavefronts on one 16-row n-tile; wavefront w takes
-//     every 4th group of 4 blocks along K (split-K inside the workgroup) and
-//     the four partial tiles are summed through LDS, so even N = 4096 gives
-//     256 workgroups.
+//   * Operand layout.  Lane l has column n = l % 16 and k-slot group
+//     g = l / 16.  MFMA step s (0-3) of a group of four blocks b0..b0+3
+//     covers block b0 + s, and group g takes its elements 8 g .. 8 g + 7, so
+//     an activation operand load of 16 rows reads 16 whole 64-byte block rows
+//     (coalesced).  The weights arrive the other way round -- one 16-byte
+//     load gives lane (n, g) all four dwords of block b0 + g of row n -- and
+//     a 4 x 4 transpose of dwords across the lane groups (two
+//     v_permlane32_swap and two v_permlane16_swap) hands dword g of block
+//     b0 + s to group g for step s.  Output: lane l, register r holds
+//     D[4 g + r][l % 16].
+//   * Dequantization once per weight: a byte of two nibbles is looked up in
+//     the replicated pair table (one v_perm + one ds_read_b64 per two
+//     weights), multiplied by its fp16 scale in float32 and rounded to bf16
+//     by v_cvt_pk_bf16_f32 -- about two VALU ops per weight for any M.
+//   * Operand reuse.  A wavefront covers RT tiles of 16 weight rows and MT
+//     tiles of 16 activation rows: each activation operand is loaded once
+//     per step and used for RT row tiles, each weight operand for MT
+//     activation tiles.
+//   * Split K inside the workgroup: wavefront w of 4 takes groups w, w + 4,
+//     ... along K; the next group's weights and activations are requested
+//     while the current one is computed (each register set is reloaded right
+//     after its last use), and the four partial tiles are summed through LDS
+//     (the pair table's space) at the end.
 // Arithmetic intensity stays below the bf16 ridge for M <= 64 (about 3.2 M
 // flop per byte of packed weight), so HBM remains the bound.
 //
@@ -36,117 +45,258 @@ namespace {
 
 typedef short bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2v v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(bf16x8, u);
+}
 
 // Split 8 float32 values into bf16 hi (truncation) and lo (RNE of the exact residual).
 __device__ __forceinline__ void split8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const uint32_t h = __float_as_uint(v[t]) & 0xffff0000u;
-    hi[t] = (short)(h >> 16);
-    lo[t] = (short)f32_to_bf16_rne(v[t] - __uint_as_float(h));
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t a = __float_as_uint(v[2 * t]) & 0xffff0000u, b = __float_as_uint(v[2 * t + 1]) & 0xffff0000u;
+    h[t] = (a >> 16) | b;
+    l[t] = pack_bf16x2(v[2 * t] - __uint_as_float(a), v[2 * t + 1] - __uint_as_float(b));
+  }
+  hi = as_bf16x8(h[0], h[1], h[2], h[3]);
+  lo = as_bf16x8(l[0], l[1], l[2], l[3]);
+}
+
+// The 8 weights of dword w (elements 8 s .. 8 s + 7 of a block) times scale d, as float32.
+__device__ __forceinline__ void dequant8(uint32_t w, float d, const uint8_t* lut, uint32_t laneoff, float (&v)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 c = *reinterpret_cast<const float2*>(lut + pair_addr(w, laneoff, k));
+    v[2 * k] = c.x * d;
+    v[2 * k + 1] = c.y * d;
   }
 }
 
-template <int MT, bool kF32X>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint4* __restrict__ packed,
-                                                        const uint32_t* __restrict__ scales, uint32_t N,
-                                                        uint32_t nb, const void* __restrict__ Xv, int64_t ldx,
-                                                        uint32_t M, float* __restrict__ Y, int64_t ldy,
-                                                        Codebook cb) {
-  __shared__ float lut[16];
-  __shared__ f32x4 part[kWaves - 1][MT][64];
+// 4 x 4 transpose of dwords across the four 16-lane groups: on entry lane
+// (n, g) holds dwords 0-3 of block b0 + g; on exit out[s] is dword g of block
+// b0 + s.  permlane32_swap(a, b) leaves (a rows 0-1, b rows 0-1) in its
+// first result and (a rows 2-3, b rows 2-3) in its second; permlane16_swap
+// does the same for row pairs (0, 1) and (2, 3).
+__device__ __forceinline__ void transpose_groups(const uint4& p, uint32_t (&out)[4]) {
+  auto s32 = __builtin_amdgcn_permlane32_swap(p.x, p.z, false, false);   // j = 0: words 0 and 2
+  auto t32 = __builtin_amdgcn_permlane32_swap(p.y, p.w, false, false);   // j = 1: words 1 and 3
+  auto a = __builtin_amdgcn_permlane16_swap(s32[0], t32[0], false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(s32[1], t32[1], false, false);
+  out[0] = a[0];
+  out[1] = a[1];
+  out[2] = b[0];
+  out[3] = b[1];
+}
+
+template <bool kF32X>
+struct AOperand;
+
+template <>
+struct AOperand<false> {                  // bf16 activations: one operand per (step, m tile)
+  uint4 a;
+  __device__ __forceinline__ void load(const uint8_t* X, int64_t ldx, uint32_t m, uint32_t M, uint32_t k, bool ok) {
+    a = make_uint4(0u, 0u, 0u, 0u);
+    if (ok && m < M) a = *reinterpret_cast<const uint4*>(X + ((size_t)m * ldx + k) * 2);
+  }
+};
+
+template <>
+struct AOperand<true> {                   // float32 activations, kept as bf16 hi/lo
+  bf16x8 hi, lo;
+  float raw[8];
+  __device__ __forceinline__ void load(const uint8_t* X, int64_t ldx, uint32_t m, uint32_t M, uint32_t k, bool ok) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) raw[t] = 0.f;
+    if (ok && m < M) {
+      const float4* src = reinterpret_cast<const float4*>(X + ((size_t)m * ldx + k) * 4);
+      const float4 u0 = src[0], u1 = src[1];
+      raw[0] = u0.x; raw[1] = u0.y; raw[2] = u0.z; raw[3] = u0.w;
+      raw[4] = u1.x; raw[5] = u1.y; raw[6] = u1.z; raw[7] = u1.w;
+    }
+  }
+};
+
+// MT activation tiles (M <= 16 MT), RT weight-row tiles per workgroup.
+template <int MT, int RT, bool kF32X>
+__global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __restrict__ packed,
+                                                                const uint32_t* __restrict__ scales, uint32_t N,
+                                                                uint32_t nb, const uint8_t* __restrict__ X,
+                                                                int64_t ldx, uint32_t M, float* __restrict__ Y,
+                                                                int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLutBytes];
+  static_assert((kWaves - 1) * RT * MT * 64 * 16 <= kLutBytes, "partial tiles must fit the table's space");
+  uint8_t* const lut = smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15;
-  const int g = lane >> 4;
-  stage_centroids(cb, lut);
+  const uint32_t g = (uint32_t)(lane >> 4);
+  const uint32_t laneoff = (uint32_t)(lane & (kCopies - 1)) * 8u;
+
+  const uint32_t n0 = blockIdx.x * (16u * RT);
+  const uint32_t ngroups = (nb + 3u) / 4u;
+
+  // Row addresses (clamped: rows past N read a valid row and are not written).
+  const uint4* prow[RT];
+  const uint32_t* srow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const uint32_t row = min(n0 + 16u * rt + (uint32_t)nl, N - 1u);
+    prow[rt] = packed + (size_t)row * nb;
+    srow[rt] = scales + (size_t)row * nb;
+  }
+
+  // Weights of group q for this lane: block 4 q + g of its row, and the
+  // scale pairs of all four blocks (clamped: a block past nb belongs to a
+  // step that is skipped).
+  uint4 p[RT];
+  uint32_t sc[RT][4];
+  auto load_w = [&](uint32_t q) {
+    const uint32_t b = min(4u * q + g, nb - 1u);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      p[rt] = prow[rt][b];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) sc[rt][s2] = srow[rt][min(4u * q + (uint32_t)s2, nb - 1u)];
+    }
+  };
+  AOperand<kF32X> A[4][MT];
+  auto load_a = [&](uint32_t q, int s) {
+    const uint32_t b = 4u * q + (uint32_t)s;
+    const bool ok = b < nb;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) A[s][mt].load(X, ldx, mt * 16u + (uint32_t)nl, M, 32u * b + 8u * g, ok);
+  };
+
+  uint32_t q = (uint32_t)wave;
+  const bool any = q < ngroups;
+  if (any) {
+    load_w(q);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) load_a(q, s);
+  }
+  fill_pair_lut(lut, tid, kThreads);
   __syncthreads();
 
-  const uint32_t n0 = blockIdx.x * 16u;
-  const uint32_t row = n0 + nl;
-  const bool row_ok = row < N;
-
-  f32x4 acc[MT];
+  f32x4 acc[RT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (uint32_t b0 = 4u * wave; b0 < nb; b0 += 4u * kWaves) {
-    const uint32_t b = b0 + g;
-    const bool ok = b < nb;
-    uint4 p = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t sc = 0u;
-    if (ok && row_ok) {
-      p = packed[(size_t)row * nb + b];
-      sc = scales[(size_t)row * nb + b];
+  for (; q < ngroups; q += kWaves) {
+    const uint32_t qn = q + kWaves < ngroups ? q + kWaves : q;   // next group (a re-read of q at the end)
+    // Dword g of block b0 + s for step s, and the scale of its half.
+    uint32_t wt[RT][4];
+    float dd[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      transpose_groups(p[rt], wt[rt]);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) dd[rt][s2] = f16_bits_to_f32(g < 2u ? (sc[rt][s2] & 0xffffu) : (sc[rt][s2] >> 16));
     }
-    const float d0 = f16_bits_to_f32(sc & 0xffffu);
-    const float d1 = f16_bits_to_f32(sc >> 16);
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+    const uint32_t nsteps = min(4u, nb - 4u * q);          // steps whose block exists (wavefront-uniform)
+    load_w(qn);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float d = s < 2 ? d0 : d1;
-      float wv[8];
+      if ((uint32_t)s < nsteps) {   // a step past the last block contributes nothing
+        bf16x8 Bh[RT], Bl[RT];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) wv[t] = d * lut[(w[s] >> (4 * t)) & 15u];
-      if constexpr (!kF32X) {
-        const uint16_t* X = static_cast<const uint16_t*>(Xv);
-        bf16x8 B;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) B[t] = (short)f32_to_bf16_rne(wv[t]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const uint32_t m = mt * 16u + nl;
-          bf16x8 A = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-          if (ok && m < M) A = *reinterpret_cast<const bf16x8*>(X + (size_t)m * ldx + (size_t)b * 32 + 8 * s);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[mt], 0, 0, 0);
-        }
-      } else {
-        const float* X = static_cast<const float*>(Xv);
-        bf16x8 Bh, Bl;
-        split8(wv, Bh, Bl);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const uint32_t m = mt * 16u + nl;
-          float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (ok && m < M) {
-            const float4* src = reinterpret_cast<const float4*>(X + (size_t)m * ldx + (size_t)b * 32 + 8 * s);
-            const float4 u0 = src[0], u1 = src[1];
-            xv[0] = u0.x; xv[1] = u0.y; xv[2] = u0.z; xv[3] = u0.w;
-            xv[4] = u1.x; xv[5] = u1.y; xv[6] = u1.z; xv[7] = u1.w;
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint32_t w = wt[rt][s];
+          const float d = dd[rt][s];
+          float v[8];
+          dequant8(w, d, lut, laneoff, v);
+          if constexpr (!kF32X) {
+            Bh[rt] = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                               pack_bf16x2(v[6], v[7]));
+          } else {
+            split8(v, Bh[rt], Bl[rt]);
           }
-          bf16x8 Ah, Al;
-          split8(xv, Ah, Al);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, Bh, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, Bl, acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, Bh, acc[mt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if constexpr (!kF32X) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, A[s][mt].a);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Bh[rt], acc[rt][mt], 0, 0, 0);
+          } else {
+            bf16x8 ah, al;
+            split8(A[s][mt].raw, ah, al);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, Bh[rt], acc[rt][mt], 0, 0, 0);
+              acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, Bl[rt], acc[rt][mt], 0, 0, 0);
+              acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, Bh[rt], acc[rt][mt], 0, 0, 0);
+            }
+          }
         }
       }
+      load_a(qn, s);      // step s's operands are consumed: request the next group's
     }
   }
 
+  // Sum the four wavefronts' partial tiles through the table's LDS space.
+  __syncthreads();
+  f32x4* part = reinterpret_cast<f32x4*>(smem);
   if (wave > 0) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) part[wave - 1][mt][lane] = acc[mt];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) part[(((wave - 1) * RT + rt) * MT + mt) * 64 + lane] = acc[rt][mt];
   }
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 v = acc[mt];
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint32_t row = n0 + 16u * rt + (uint32_t)nl;
 #pragma unroll
-      for (int w2 = 0; w2 < kWaves - 1; ++w2) v += part[w2][mt][lane];
-      if (row_ok) {
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 v = acc[rt][mt];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t m = mt * 16u + 4u * g + r;
-          if (m < M) Y[(size_t)m * ldy + row] = v[r];
+        for (int w2 = 0; w2 < kWaves - 1; ++w2) v += part[((w2 * RT + rt) * MT + mt) * 64 + lane];
+        if (row < N) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t m = mt * 16u + 4u * g + r;
+            if (m < M) Y[(size_t)m * ldy + row] = v[r];
+          }
         }
       }
     }
   }
+}
+
+template <int MT, int RT, bool kF32X>
+void launch_mfma(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
+                 uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
+  const dim3 grid((N + 16u * RT - 1) / (16u * RT)), block(kThreads);
+  hipLaunchKernelGGL((gemm_mfma_kernel<MT, RT, kF32X>), grid, block, 0, s, pk, sc, N, nb, X, ldx, M, Y, ldy);
+}
+
+// Weight-row tiles per workgroup: as many as keep about two workgroups per
+// compute unit busy (each workgroup reads the whole activation block from
+// L2, so fewer, taller workgroups cut that traffic).
+template <int MT, bool kF32X>
+void launch_mt(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
+               uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
+  const uint32_t target = 2u * (uint32_t)device_cu_count();
+  const uint32_t tiles16 = (N + 15u) / 16u;
+  if (tiles16 >= 4u * target) launch_mfma<MT, 4, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
+  else if (tiles16 >= 2u * target) launch_mfma<MT, 2, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
+  else launch_mfma<MT, 1, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
 }
 
 }  // namespace
@@ -154,37 +304,31 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint4* __restrict_
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
                        const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
   if (M < 16) return launch_gemm_valu(packed, scales, N, K, M, xr, xbf16, ldx, y, ldy, s);
-  const Codebook& cb = host_codebook();
   const uint32_t nb = (uint32_t)(K / kBlock);
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
   const uint8_t* X = static_cast<const uint8_t*>(xr);
   const int64_t xs = xbf16 ? 2 : 4;
-  const dim3 grid((unsigned)((N + 15) / 16)), block(256);
-  for (int64_t m0 = 0; m0 < M; m0 += 64) {
-    const int64_t mc = (M - m0 < 64) ? M - m0 : 64;
-    const void* Xm = X + m0 * ldx * xs;
+  // Float32 activations take three MFMAs per product and twice the operand
+  // registers: at most 32 activation rows per pass.
+  const int64_t chunk = xbf16 ? 64 : 32;
+  for (int64_t m0 = 0; m0 < M; m0 += chunk) {
+    const int64_t mc = (M - m0 < chunk) ? M - m0 : chunk;
+    const uint8_t* Xm = X + m0 * ldx * xs;
     float* Ym = y + m0 * ldy;
     const int mt = (int)((mc + 15) / 16);
-#define TQ_LAUNCH_MFMA(MT_, F32_)                                                                                  \
-  hipLaunchKernelGGL((gemm_mfma_kernel<MT_, F32_>), grid, block, 0, s, pk, sc, (uint32_t)N, nb, Xm, ldx,          \
-                     (uint32_t)mc, Ym, ldy, cb)
+    const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
       switch (mt) {
-        case 1: TQ_LAUNCH_MFMA(1, false); break;
-        case 2: TQ_LAUNCH_MFMA(2, false); break;
-        case 3: TQ_LAUNCH_MFMA(3, false); break;
-        default: TQ_LAUNCH_MFMA(4, false); break;
+        case 1: launch_mt<1, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
+        case 2: launch_mt<2, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
+        case 3: launch_mt<3, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
+        default: launch_mt<4, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
       }
     } else {
-      switch (mt) {
-        case 1: TQ_LAUNCH_MFMA(1, true); break;
-        case 2: TQ_LAUNCH_MFMA(2, true); break;
-        case 3: TQ_LAUNCH_MFMA(3, true); break;
-        default: TQ_LAUNCH_MFMA(4, true); break;
-      }
+      if (mt == 1) launch_mt<1, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
+      else launch_mt<2, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
     }
-#undef TQ_LAUNCH_MFMA
   }
   return hipGetLastError();
 }

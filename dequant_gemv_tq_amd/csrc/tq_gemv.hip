@@ -36,8 +36,6 @@
 namespace tq {
 namespace {
 
-constexpr int kCopies = 32;                       // LUT copies: one per lane of a 32-lane group
-constexpr int kLutBytes = 256 * kCopies * 8;      // 64 KiB
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
@@ -140,31 +138,6 @@ __device__ __forceinline__ void decode_block(const uint4& p, uint32_t sc, const 
   const float d1 = f16_bits_to_f32(sc >> 16);
 #pragma unroll
   for (int m = 0; m < MC; ++m) acc[m] = __builtin_fmaf(d0, a[m][0], __builtin_fmaf(d1, a[m][1], acc[m]));
-}
-
-// Pair table fill from the codebook constants (immediates: nothing waits on
-// memory).  Wavefront w (of 16 virtual ones) writes entries e = 16 w + 4 u +
-// lane / 16 (u < 4), copies 2 (lane % 16) and 2 (lane % 16) + 1, so the high
-// centroid c[e / 16] = c[w] is a wavefront-uniform choice and the low one
-// c[e % 16] = c[4 u + lane / 16] a per-lane choice of four.  Consecutive
-// lanes store consecutive 16-byte chunks of the table (no bank conflicts).
-__device__ __forceinline__ void fill_pair_lut(uint8_t* lut, int tid, int nthreads) {
-  const int lane = tid & 63, g = lane >> 4;
-  for (int w = tid >> 6; w < 16; w += nthreads >> 6) {
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    float hi = centroid(0);
-#pragma unroll
-    for (int k = 1; k < 16; ++k) hi = wu == k ? centroid(k) : hi;
-    uint8_t* base = lut + ((16 * wu + g) << 8) + 16 * (lane & 15);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float lo = g == 0   ? centroid(4 * u)
-                       : g == 1 ? centroid(4 * u + 1)
-                       : g == 2 ? centroid(4 * u + 2)
-                                : centroid(4 * u + 3);
-      *reinterpret_cast<float4*>(base + (u << 10)) = make_float4(lo, hi, lo, hi);
-    }
-  }
 }
 
 // One cross-lane stage of the 32-point FWHT when 8 consecutive lanes hold a

@@ -135,6 +135,45 @@ __device__ __forceinline__ void stage_centroids(const Codebook& cb, float* lut16
   }
 }
 
+// Pair lookup table for decoding packed nibbles: entry e (a byte of two
+// indices) holds the float32 pair (c[e & 15], c[e >> 4]), replicated 32
+// times; copy l of entry e sits at LDS byte (e << 8) | 8 l, so the 32 lanes an
+// LDS pass serves with ds_read_b64 (lane l uses copy l % 32) always hit
+// distinct banks, and the address is one v_perm_b32 that places the byte of
+// the packed word next to the lane offset.  64 KiB.
+constexpr int kCopies = 32;
+constexpr int kLutBytes = 256 * kCopies * 8;
+
+// Pair table fill from the codebook constants (immediates: nothing waits on
+// memory).  Wavefront w (of 16 virtual ones) writes entries e = 16 w + 4 u +
+// lane / 16 (u < 4), copies 2 (lane % 16) and 2 (lane % 16) + 1, so the high
+// centroid c[e / 16] = c[w] is a wavefront-uniform choice and the low one
+// c[e % 16] = c[4 u + lane / 16] a per-lane choice of four.  Consecutive
+// lanes store consecutive 16-byte chunks of the table (no bank conflicts).
+__device__ __forceinline__ void fill_pair_lut(uint8_t* lut, int tid, int nthreads) {
+  const int lane = tid & 63, g = lane >> 4;
+  for (int w = tid >> 6; w < 16; w += nthreads >> 6) {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    float hi = centroid(0);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) hi = wu == k ? centroid(k) : hi;
+    uint8_t* base = lut + ((16 * wu + g) << 8) + 16 * (lane & 15);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float lo = g == 0   ? centroid(4 * u)
+                       : g == 1 ? centroid(4 * u + 1)
+                       : g == 2 ? centroid(4 * u + 2)
+                                : centroid(4 * u + 3);
+      *reinterpret_cast<float4*>(base + (u << 10)) = make_float4(lo, hi, lo, hi);
+    }
+  }
+}
+
+// LDS address of the pair entry for byte k (0-3) of packed word w.
+__device__ __forceinline__ uint32_t pair_addr(uint32_t w, uint32_t laneoff, int k) {
+  return __builtin_amdgcn_perm(w, laneoff, 0x0C0C0000u | ((4u + (uint32_t)k) << 8));
+}
+
 // Load one 32-element block (fp32 or bf16) into registers; p is 16-byte aligned.
 template <bool kBf16>
 __device__ __forceinline__ void load_block(const void* p, float (&v)[32]) {

@@ -181,6 +181,21 @@ def test_gemm_fp32_split_mfma_any_k(m):
         assert worst < 1e-4
 
 
+@pytest.mark.parametrize("m", [16, 40, 64])
+def test_gemm_tall_row_tiles(m):
+    """Shapes tall enough for the 2- and 4-row-tile workgroups, with K leaving a partial group of four blocks
+    (bf16 operands: K in the thousands, where their rounding stays inside the bound)."""
+    for n, k in ((32784, 1056), (17000, 1120)):
+        g = workloads.generator(n + k + m, DEV)
+        W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+        X = workloads.activation(m, k, g, DEV, torch.bfloat16)
+        packed, scales = tqa.quantize(W)
+        say(f"[gemm] tall M={m} {n}x{k}")
+        Y = tqa.gemm(packed, scales, tqa.rotate(X, dtype=torch.bfloat16))
+        yr, a = otq.gemm_o64(packed.cpu().numpy(), u16(scales), X.float().cpu().numpy())
+        assert_within(f32np(Y), yr, a, what=f"gemm tall M={m} {n}x{k}")
+
+
 def test_gemm_bf16_large_k():
     """bf16 activations (one MFMA pass) at the decode shapes' K."""
     for k in (4096, 14336):
