@@ -38,6 +38,8 @@
 // bf16 hi + lo (hi by truncation, lo = bf16(v - hi), exact residual) and three
 // MFMAs (hi*hi + hi*lo + lo*hi) keep about 16 significant bits per product,
 // which holds the bound at any K.
+#include <type_traits>
+
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -80,6 +82,15 @@ __device__ __forceinline__ void dequant8(uint32_t w, float d, const uint8_t* lut
     const float2 c = *reinterpret_cast<const float2*>(lut + pair_addr(w, laneoff, k));
     v[2 * k] = c.x * d;
     v[2 * k + 1] = c.y * d;
+  }
+}
+
+// f(std::integral_constant<int, j>) for j = 0 .. N-1.
+template <int N, typename F, int J = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>{});
+    static_for<N, F, J + 1>(static_cast<F&&>(f));
   }
 }
 
@@ -127,8 +138,9 @@ struct AOperand<true> {                   // float32 activations, kept as bf16 h
   }
 };
 
-// MT activation tiles (M <= 16 MT), RT weight-row tiles per workgroup.
-template <int MT, int RT, bool kF32X>
+// MT activation tiles (M <= 16 MT), RT weight-row tiles per workgroup, WD
+// groups of weights in flight per wavefront.
+template <int MT, int RT, int WD, bool kF32X>
 __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __restrict__ packed,
                                                                 const uint32_t* __restrict__ scales, uint32_t N,
                                                                 uint32_t nb, const uint8_t* __restrict__ X,
@@ -157,34 +169,52 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
     srow[rt] = scales + (size_t)row * nb;
   }
 
-  // Weights of group q for this lane: block 4 q + g of its row, and the
-  // scale pairs of all four blocks (clamped: a block past nb belongs to a
-  // step that is skipped).
-  uint4 p[RT];
-  uint32_t sc[RT][4];
-  auto load_w = [&](uint32_t q) {
+  // The groups of this wavefront are q_i = wave + 4 i, i < nq.  Indices
+  // past the last group are clamped to it: those loads re-read a group
+  // already loaded and are discarded.
+  const uint32_t nq = (uint32_t)wave < ngroups ? (ngroups - 1u - (uint32_t)wave) / 4u + 1u : 0u;
+  auto grp = [&](uint32_t i) { return (uint32_t)wave + 4u * min(i, nq - 1u); };
+
+  // Weights of group q for this lane: block 4 q + g of its row and that
+  // block's scale pair (clamped: a block past nb belongs to a step that is
+  // skipped).
+  struct WSet {
+    uint4 p[RT];
+    uint32_t sc[RT];
+  };
+  WSet ws[WD];
+  auto load_w = [&](WSet& w, uint32_t q) {
     const uint32_t b = min(4u * q + g, nb - 1u);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      p[rt] = prow[rt][b];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) sc[rt][s2] = srow[rt][min(4u * q + (uint32_t)s2, nb - 1u)];
+      w.p[rt] = prow[rt][b];
+      w.sc[rt] = srow[rt][b];
     }
   };
-  AOperand<kF32X> A[4][MT];
-  auto load_a = [&](uint32_t q, int s) {
+  // Activation operands: AD register sets.  Loads complete in issue order
+  // (one vmcnt counter), so a wait for an operand also waits for every
+  // weight load issued before it; with AD == WD each set is refilled right
+  // behind the weight set of the same group and every wait covers exactly
+  // the group about to be computed.  (AD == 1 refills during the group
+  // before, which leaves the weight prefetch only one group of lead.)
+  constexpr int AD = MT <= 2 ? WD : 1;
+  AOperand<kF32X> A[AD][4][MT];
+  auto load_a = [&](int set, uint32_t q, int s) {
     const uint32_t b = 4u * q + (uint32_t)s;
     const bool ok = b < nb;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) A[s][mt].load(X, ldx, mt * 16u + (uint32_t)nl, M, 32u * b + 8u * g, ok);
+    for (int mt = 0; mt < MT; ++mt) A[set][s][mt].load(X, ldx, mt * 16u + (uint32_t)nl, M, 32u * b + 8u * g, ok);
   };
 
-  uint32_t q = (uint32_t)wave;
-  const bool any = q < ngroups;
-  if (any) {
-    load_w(q);
+  if (nq > 0u) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) load_a(q, s);
+    for (int j = 0; j < WD; ++j) {
+      load_w(ws[j], grp((uint32_t)j));
+      if (j < AD) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) load_a(j, grp((uint32_t)j), s);
+      }
+    }
   }
   fill_pair_lut(lut, tid, kThreads);
   __syncthreads();
@@ -195,29 +225,33 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (; q < ngroups; q += kWaves) {
-    const uint32_t qn = q + kWaves < ngroups ? q + kWaves : q;   // next group (a re-read of q at the end)
+  // Group i with weight set w (set number j): compute, then (reload) refill
+  // w with group i + WD; the activation operands of step s are refilled with
+  // group i + AD as soon as step s has used them.
+  auto body = [&](uint32_t i, WSet& w, auto jc, auto reload) {
+    constexpr int ja = decltype(jc)::value % AD;
+    const uint32_t q = grp(i), qn = grp(i + (uint32_t)AD);
     // Dword g of block b0 + s for step s, and the scale of its half.
     uint32_t wt[RT][4];
     float dd[RT][4];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      transpose_groups(p[rt], wt[rt]);
+      transpose_groups(w.p[rt], wt[rt]);
+      uint32_t sct[4];
+      transpose_groups(make_uint4(w.sc[rt], w.sc[rt], w.sc[rt], w.sc[rt]), sct);
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) dd[rt][s2] = f16_bits_to_f32(g < 2u ? (sc[rt][s2] & 0xffffu) : (sc[rt][s2] >> 16));
+      for (int s2 = 0; s2 < 4; ++s2) dd[rt][s2] = f16_bits_to_f32(g < 2u ? (sct[s2] & 0xffffu) : (sct[s2] >> 16));
     }
+    if constexpr (decltype(reload)::value) load_w(w, grp(i + (uint32_t)WD));
     const uint32_t nsteps = min(4u, nb - 4u * q);          // steps whose block exists (wavefront-uniform)
-    load_w(qn);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if ((uint32_t)s < nsteps) {   // a step past the last block contributes nothing
         bf16x8 Bh[RT], Bl[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const uint32_t w = wt[rt][s];
-          const float d = dd[rt][s];
           float v[8];
-          dequant8(w, d, lut, laneoff, v);
+          dequant8(wt[rt][s], dd[rt][s], lut, laneoff, v);
           if constexpr (!kF32X) {
             Bh[rt] = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                                pack_bf16x2(v[6], v[7]));
@@ -228,13 +262,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if constexpr (!kF32X) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, A[s][mt].a);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, A[ja][s][mt].a);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Bh[rt], acc[rt][mt], 0, 0, 0);
           } else {
             bf16x8 ah, al;
-            split8(A[s][mt].raw, ah, al);
+            split8(A[ja][s][mt].raw, ah, al);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
               acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, Bh[rt], acc[rt][mt], 0, 0, 0);
@@ -244,9 +278,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
           }
         }
       }
-      load_a(qn, s);      // step s's operands are consumed: request the next group's
+      load_a(ja, qn, s);   // step s's operands are consumed: request their next group's
     }
+  };
+
+  // A fixed trip count with the remainder after it (no conditional reloads
+  // inside the loop), so the compiler's wait counts stay exact.
+  uint32_t i = 0;
+  for (; i + WD <= nq; i += WD) {
+    static_for<WD>([&](auto jc) { body(i + (uint32_t)jc.value, ws[jc.value], jc, std::true_type{}); });
   }
+  static_for<WD - 1>([&](auto jc) {
+    if (i + (uint32_t)jc.value < nq) body(i + (uint32_t)jc.value, ws[jc.value], jc, std::false_type{});
+  });
 
   // Sum the four wavefronts' partial tiles through the table's LDS space.
   __syncthreads();
@@ -279,11 +323,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
   }
 }
 
+// Weight groups in flight per wavefront: three where the registers allow.
+template <int MT, int RT, bool kF32X>
+constexpr int gemm_depth() { return (kF32X ? 2 : 1) * MT * RT <= 4 ? 3 : 2; }
+// Workgroups aimed for per compute unit when choosing the row tiles.
+constexpr uint32_t kGemmWgPerCu = 2;
+
 template <int MT, int RT, bool kF32X>
 void launch_mfma(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
                  uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
   const dim3 grid((N + 16u * RT - 1) / (16u * RT)), block(kThreads);
-  hipLaunchKernelGGL((gemm_mfma_kernel<MT, RT, kF32X>), grid, block, 0, s, pk, sc, N, nb, X, ldx, M, Y, ldy);
+  hipLaunchKernelGGL((gemm_mfma_kernel<MT, RT, gemm_depth<MT, RT, kF32X>(), kF32X>), grid, block, 0, s, pk, sc, N, nb, X, ldx, M,
+                     Y, ldy);
 }
 
 // Weight-row tiles per workgroup: as many as keep about two workgroups per
@@ -292,9 +343,9 @@ void launch_mfma(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, c
 template <int MT, bool kF32X>
 void launch_mt(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
                uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
-  const uint32_t target = 2u * (uint32_t)device_cu_count();
+  const uint32_t target = kGemmWgPerCu * (uint32_t)device_cu_count();
   const uint32_t tiles16 = (N + 15u) / 16u;
-  if (tiles16 >= 4u * target) launch_mfma<MT, 4, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
+  if (MT == 1 && !kF32X && tiles16 >= 4u * target) launch_mfma<1, 4, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
   else if (tiles16 >= 2u * target) launch_mfma<MT, 2, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
   else launch_mfma<MT, 1, kF32X>(pk, sc, N, nb, X, ldx, M, Y, ldy, s);
 }
