@@ -44,11 +44,6 @@ __device__ __forceinline__ uint32_t encode_mag(float a) {
 
 __device__ __forceinline__ uint32_t sign_of(float v) { return __float_as_uint(v) >> 31; }
 
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e == 0u ? (float)m * 0x1p-9f : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
-}
-
 // --------------------------------------------------------------------------
 // NVFP4 quantizer: fill -> amax (atomicMax on the bit pattern of |w|,
 // which orders like the value for non-negative floats) -> encode -> finalize.
@@ -56,26 +51,43 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 
 __global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
+// |w| bit patterns of one 16-byte chunk (the sign bit cleared).
+template <bool kBf16>
+__device__ __forceinline__ uint32_t chunk_max(const uint4& u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t m = 0u;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (kBf16) m = max(m, max((w[t] << 16) & 0x7fff0000u, w[t] & 0x7fff0000u));
+    else m = max(m, w[t] & 0x7fffffffu);
+  }
+  return m;
+}
+
+// Grid-stride max with four 16-byte loads in flight per thread, reduced
+// across the workgroup in LDS, then one atomicMax per workgroup.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint8_t* __restrict__ W, size_t n16,
                                                         uint32_t* __restrict__ out) {
+  __shared__ uint32_t red[kThreads / 64];
+  const uint4* src = reinterpret_cast<const uint4*>(W);
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x;
   uint32_t m = 0u;
-  for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < n16; i += (size_t)gridDim.x * kThreads) {
-    uint4 u = reinterpret_cast<const uint4*>(W)[i];
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if constexpr (kBf16) {
-        uint32_t lo = (w[t] << 16) & 0x7fff0000u, hi = w[t] & 0x7fff0000u;
-        m = max(m, max(lo, hi));
-      } else {
-        m = max(m, w[t] & 0x7fffffffu);
-      }
-    }
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    m = max(m, max(max(chunk_max<kBf16>(a), chunk_max<kBf16>(b)), max(chunk_max<kBf16>(c), chunk_max<kBf16>(d))));
   }
+  for (; i < n16; i += stride) m = max(m, chunk_max<kBf16>(src[i]));
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+    atomicMax(out, m);
+  }
 }
 
 // One thread per 16-element block.
@@ -170,128 +182,7 @@ __global__ __launch_bounds__(kThreads) void mxfp6_encode_kernel(const uint8_t* _
   bscales[g] = (uint8_t)byte;
 }
 
-// --------------------------------------------------------------------------
-// Fused decode GEMV/GEMM for M <= 16 (VALU): lanes own 32-element K chunks
-// (two NVFP4 blocks or one MXFP6 block) and keep MC activation rows of that
-// chunk in registers; each weight is decoded once and used MC times.
-// --------------------------------------------------------------------------
-
-constexpr int kMaxT = 1024;
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-// Decoded 32 weights of chunk b of a row.
-template <int kFmt>
-__device__ __forceinline__ void decode_chunk(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ bs,
-                                             uint32_t nchunk, uint32_t row, uint32_t b, float st,
-                                             const float* lut, float (&w)[32]) {
-  if constexpr (kFmt == TQ_FMT_NVFP4) {
-    const uint4 p = reinterpret_cast<const uint4*>(codes)[(size_t)row * nchunk + b];
-    const uint32_t s2 = reinterpret_cast<const uint16_t*>(bs)[(size_t)row * nchunk + b];
-    const float e0 = e4m3_decode(s2 & 0xffu) * st;
-    const float e1 = e4m3_decode(s2 >> 8) * st;
-    const uint32_t q[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = lut[(q[i >> 3] >> (4 * (i & 7))) & 15u] * (i < 16 ? e0 : e1);
-  } else {
-    const uint2* src = reinterpret_cast<const uint2*>(codes) + ((size_t)row * nchunk + b) * 3;
-    uint64_t bits[3];
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      uint2 u = src[t];
-      bits[t] = (uint64_t)u.x | ((uint64_t)u.y << 32);
-    }
-    const uint32_t byte = bs[(size_t)row * nchunk + b];
-    const float scale = byte == 0u ? 0x1p-127f : __uint_as_float(byte << 23);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int bit = 6 * i;
-      uint64_t c = bits[bit >> 6] >> (bit & 63);
-      if ((bit & 63) > 58) c |= bits[(bit >> 6) + 1] << (64 - (bit & 63));
-      w[i] = lut[(uint32_t)c & 63u] * scale;
-    }
-  }
-}
-
-template <int kFmt, int MC, bool kXbf16>
-__global__ __launch_bounds__(kMaxT) void blockfp_gemv_kernel(const uint8_t* __restrict__ codes,
-                                                             const uint8_t* __restrict__ bscales,
-                                                             const float* __restrict__ tscale, uint32_t N,
-                                                             uint32_t nchunk, const uint8_t* __restrict__ x,
-                                                             int64_t ldx, float* __restrict__ y, int64_t ldy) {
-  __shared__ float lut[64];
-  __shared__ float red[MC][kMaxT / 64];
-  const int T = blockDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = T >> 6;
-  if (tid < 64) {
-    float v;
-    if constexpr (kFmt == TQ_FMT_NVFP4) {        // E2M1: bias 1, one mantissa bit
-      const uint32_t c = tid & 7u, e = c >> 1, m = c & 1u;
-      v = e == 0u ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
-      v = (tid & 8) ? -v : v;
-    } else {                                      // E3M2: bias 3, two mantissa bits
-      const uint32_t c = tid & 31u, e = c >> 2, m = c & 3u;
-      v = e == 0u ? 0.0625f * (float)m : __builtin_ldexpf(1.0f + 0.25f * (float)m, (int)e - 3);
-      v = (tid & 32) ? -v : v;
-    }
-    lut[tid] = v;
-  }
-  const float st = kFmt == TQ_FMT_NVFP4 ? *tscale : 1.0f;
-  float xr[MC][32];
-  const bool valid = (uint32_t)tid < nchunk;
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    if (valid) load_block<kXbf16>(x + m * ldx + (size_t)tid * (kXbf16 ? 64 : 128), xr[m]);
-    else
-#pragma unroll
-      for (int i = 0; i < 32; ++i) xr[m][i] = 0.f;
-  }
-  __syncthreads();
-  for (uint32_t row = blockIdx.x; row < N; row += gridDim.x) {
-    float acc[MC];
-#pragma unroll
-    for (int m = 0; m < MC; ++m) acc[m] = 0.f;
-    if (valid) {
-      float w[32];
-      decode_chunk<kFmt>(codes, bscales, nchunk, row, tid, st, lut, w);
-#pragma unroll
-      for (int m = 0; m < MC; ++m)
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[m] = __builtin_fmaf(w[i], xr[m][i], acc[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < MC; ++m) acc[m] = wave_sum(acc[m]);
-    if (lane == 0) {
-#pragma unroll
-      for (int m = 0; m < MC; ++m) red[m][wave] = acc[m];
-    }
-    __syncthreads();
-    if (tid < MC) {
-      float v = 0.f;
-      for (int w2 = 0; w2 < nwaves; ++w2) v += red[tid][w2];
-      y[tid * ldy + row] = v;
-    }
-    __syncthreads();
-  }
-}
-
 inline uint32_t grid_for(uint32_t total) { return (total + kThreads - 1) / kThreads; }
-
-template <int kFmt, int MC>
-void launch_bfp_gemv(const uint8_t* codes, const uint8_t* bs, const float* ts, uint32_t N, uint32_t nchunk,
-                     const uint8_t* x, bool xbf16, int64_t ldx_bytes, float* y, int64_t ldy, hipStream_t s) {
-  const int T = (int)((nchunk + 63) / 64 * 64);
-  const uint32_t grid = N < 65536u ? N : 65536u;
-  if (xbf16)
-    hipLaunchKernelGGL((blockfp_gemv_kernel<kFmt, MC, true>), dim3(grid), dim3(T), 0, s, codes, bs, ts, N, nchunk, x,
-                       ldx_bytes, y, ldy);
-  else
-    hipLaunchKernelGGL((blockfp_gemv_kernel<kFmt, MC, false>), dim3(grid), dim3(T), 0, s, codes, bs, ts, N, nchunk,
-                       x, ldx_bytes, y, ldy);
-}
 
 }  // namespace
 
@@ -304,7 +195,8 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
     hipLaunchKernelGGL(fill_u32, dim3(1), dim3(1), 0, s, ts, 0u);
     const size_t n16 = (size_t)(N * K * esz / 16);
     const size_t want = (n16 + kThreads - 1) / kThreads;
-    const uint32_t grid = (uint32_t)(want < 8192 ? want : 8192);
+    const size_t cap = (size_t)(4 * device_cu_count());
+    const uint32_t grid = (uint32_t)(want < cap ? want : cap);
     if (bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(kThreads), 0, s, w, n16, ts);
     else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(kThreads), 0, s, w, n16, ts);
     const int64_t blocks = N * K / 16;
@@ -342,24 +234,7 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
                                int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
                                hipStream_t s) {
-  const uint32_t nchunk = (uint32_t)(K / 32);
-  const int64_t xs = xbf16 ? 2 : 4;
-  const uint8_t* xb = static_cast<const uint8_t*>(x);
-  for (int64_t m0 = 0; m0 < M;) {
-    const int64_t left = M - m0;
-    const int mc = left >= 2 ? 2 : 1;           // 2 rows x 32 fp32 per lane fit without spills
-    const uint8_t* xm = xb + m0 * ldx * xs;
-    float* ym = y + m0 * ldy;
-    if (fmt == TQ_FMT_NVFP4) {
-      if (mc == 2) launch_bfp_gemv<TQ_FMT_NVFP4, 2>(codes, bscales, tscale, (uint32_t)N, nchunk, xm, xbf16, ldx * xs, ym, ldy, s);
-      else launch_bfp_gemv<TQ_FMT_NVFP4, 1>(codes, bscales, tscale, (uint32_t)N, nchunk, xm, xbf16, ldx * xs, ym, ldy, s);
-    } else {
-      if (mc == 2) launch_bfp_gemv<TQ_FMT_MXFP6, 2>(codes, bscales, tscale, (uint32_t)N, nchunk, xm, xbf16, ldx * xs, ym, ldy, s);
-      else launch_bfp_gemv<TQ_FMT_MXFP6, 1>(codes, bscales, tscale, (uint32_t)N, nchunk, xm, xbf16, ldx * xs, ym, ldy, s);
-    }
-    m0 += mc;
-  }
-  return hipGetLastError();
+  return launch_blockfp_gemv(fmt, codes, bscales, tscale, N, K, M, x, xbf16, ldx, y, ldy, s);
 }
 
 }  // namespace tq

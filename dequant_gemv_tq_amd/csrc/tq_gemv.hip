@@ -109,36 +109,138 @@ __device__ __forceinline__ void wave_reduce(float (&v)[V], int lane) {
   v[0] += dpp<kQuadXor1>(v[0]);
 }
 
-template <int MC>
-__device__ __forceinline__ void decode_block(const uint4& p, uint32_t sc, const float (&x)[MC][32],
-                                             const uint8_t* lut, uint32_t laneoff, float (&acc)[MC]) {
-  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
-  // All 16 pair lookups of the block are issued before the first FMA so the
-  // LDS latency is paid once per block, not once per byte.
-  float2 c[16];
+// ---------------------------------------------------------------------------
+// Weight formats.  Each holds its device pointers and provides the per-lane
+// data of one 32-element block (Raw), its load, and the decode-and-multiply
+// of one block against MC activation rows held in registers.
+// ---------------------------------------------------------------------------
+
+// TQ4_1S: 16 bytes of nibble indices and an fp16 scale pair per block;
+// decoded through the replicated pair table (1 v_perm + 1 ds_read_b64 + 2
+// FMAs per two weights).
+struct FmtTQ4 {
+  static constexpr bool kLut = true;
+  struct Raw {
+    uint4 p;
+    uint32_t s;
+  };
+  const uint4* codes;
+  const uint32_t* scales;
+  __device__ __forceinline__ void prepare() {}
+  __device__ __forceinline__ Raw load(size_t row, uint32_t nb, uint32_t b) const {
+    return Raw{codes[row * nb + b], scales[row * nb + b]};
+  }
+  template <int MC>
+  __device__ __forceinline__ void decode(const Raw& r, const float (&x)[MC][32], const uint8_t* lut,
+                                         uint32_t laneoff, float (&acc)[MC]) const {
+    const uint32_t w[4] = {r.p.x, r.p.y, r.p.z, r.p.w};
+    // All 16 pair lookups of the block are issued before the first FMA so
+    // the LDS latency is paid once per block, not once per byte.
+    float2 c[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t addr = __builtin_amdgcn_perm(w[q], laneoff, 0x0C0C0000u | ((4u + k) << 8));
-      c[4 * q + k] = *reinterpret_cast<const float2*>(lut + addr);
+      for (int k = 0; k < 4; ++k) c[4 * q + k] = *reinterpret_cast<const float2*>(lut + pair_addr(w[q], laneoff, k));
+    float a[MC][2];
+#pragma unroll
+    for (int m = 0; m < MC; ++m) a[m][0] = a[m][1] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        a[m][i >> 3] = __builtin_fmaf(c[i].x, x[m][2 * i], a[m][i >> 3]);
+        a[m][i >> 3] = __builtin_fmaf(c[i].y, x[m][2 * i + 1], a[m][i >> 3]);
+      }
     }
-  float a[MC][2];
+    const float d0 = f16_bits_to_f32(r.s & 0xffffu);
+    const float d1 = f16_bits_to_f32(r.s >> 16);
 #pragma unroll
-  for (int m = 0; m < MC; ++m) a[m][0] = a[m][1] = 0.f;
+    for (int m = 0; m < MC; ++m) acc[m] = __builtin_fmaf(d0, a[m][0], __builtin_fmaf(d1, a[m][1], acc[m]));
+  }
+};
+
+// NVFP4: 16 bytes of E2M1 codes (element 2j in the low nibble of byte j),
+// two E4M3 block scales per 32 elements and one float32 tensor scale.  The
+// codes are decoded by v_cvt_scalef32_pk_f32_fp4 (two per instruction, scale
+// 1, exact); each 16-element half-sum is multiplied once by its effective
+// scale fl(e4m3 * s_t), the value the oracle's dequantization uses.
+struct FmtNVFP4 {
+  static constexpr bool kLut = false;
+  struct Raw {
+    uint4 p;
+    uint32_t s;
+  };
+  const uint4* codes;
+  const uint16_t* scales;
+  const float* tscale;
+  float st;
+  __device__ __forceinline__ void prepare() { st = *tscale; }
+  __device__ __forceinline__ Raw load(size_t row, uint32_t nb, uint32_t b) const {
+    return Raw{codes[row * nb + b], scales[row * nb + b]};
+  }
+  template <int MC>
+  __device__ __forceinline__ void decode(const Raw& r, const float (&x)[MC][32], const uint8_t*, uint32_t,
+                                         float (&acc)[MC]) const {
+    const uint32_t w[4] = {r.p.x, r.p.y, r.p.z, r.p.w};
+    float a[MC][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+    for (int m = 0; m < MC; ++m) a[m][0] = a[m][1] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // Byte k of word q holds elements 8 q + 2 k (low nibble) and 8 q + 2 k + 1.
+      const decltype(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(0u, 1.0f, 0)) v[4] = {
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 1),
+          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 3)};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = 4 * q + k;
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+          a[m][i >> 3] = __builtin_fmaf(v[k][0], x[m][2 * i], a[m][i >> 3]);
+          a[m][i >> 3] = __builtin_fmaf(v[k][1], x[m][2 * i + 1], a[m][i >> 3]);
+        }
+      }
+    }
+    const float e0 = e4m3_decode(r.s & 0xffu) * st;
+    const float e1 = e4m3_decode((r.s >> 8) & 0xffu) * st;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) acc[m] = __builtin_fmaf(e0, a[m][0], __builtin_fmaf(e1, a[m][1], acc[m]));
+  }
+};
+
+// MXFP6: 24 bytes of E3M2 codes per block (element i at bits 6i..6i+5 of the
+// little-endian 192-bit block) and one E8M0 scale 2^(byte - 127).  One
+// v_cvt_scalef32_pk32_f32_bf6 decodes the whole block (scale 1, exact); the
+// block sum is scaled by ldexp, exact for every byte.
+struct FmtMXFP6 {
+  static constexpr bool kLut = false;
+  struct Raw {
+    uint2 c[3];
+    uint32_t s;
+  };
+  const uint2* codes;
+  const uint8_t* scales;
+  __device__ __forceinline__ void prepare() {}
+  __device__ __forceinline__ Raw load(size_t row, uint32_t nb, uint32_t b) const {
+    const uint2* src = codes + (row * nb + b) * 3;
+    return Raw{{src[0], src[1], src[2]}, scales[row * nb + b]};
+  }
+  template <int MC>
+  __device__ __forceinline__ void decode(const Raw& r, const float (&x)[MC][32], const uint8_t*, uint32_t,
+                                         float (&acc)[MC]) const {
+    typedef unsigned u32x6 __attribute__((ext_vector_type(6)));
+    const u32x6 bits = {r.c[0].x, r.c[0].y, r.c[1].x, r.c[1].y, r.c[2].x, r.c[2].y};
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk32_f32_bf6(bits, 1.0f);
+    float a[MC];
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-      a[m][i >> 3] = __builtin_fmaf(c[i].x, x[m][2 * i], a[m][i >> 3]);
-      a[m][i >> 3] = __builtin_fmaf(c[i].y, x[m][2 * i + 1], a[m][i >> 3]);
+      a[m] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) a[m] = __builtin_fmaf(v[i], x[m][i], a[m]);
+      acc[m] += __builtin_ldexpf(a[m], (int)r.s - 127);
     }
   }
-  const float d0 = f16_bits_to_f32(sc & 0xffffu);
-  const float d1 = f16_bits_to_f32(sc >> 16);
-#pragma unroll
-  for (int m = 0; m < MC; ++m) acc[m] = __builtin_fmaf(d0, a[m][0], __builtin_fmaf(d1, a[m][1], acc[m]));
-}
+};
 
 // One cross-lane stage of the 32-point FWHT when 8 consecutive lanes hold a
 // block, 4 consecutive elements each: elements i and i + 4d sit in lanes
@@ -248,10 +350,9 @@ struct GemvGrid {
 // kDepth: tiles whose loads a wavefront keeps in flight (register sets): 1
 // = load, wait, compute; 2 and 3 issue the loads of the tiles one and two
 // steps ahead before the current tile is computed.
-template <int J, int R, int MC, int kMode, int kMaxT, int kDepth, int kStage>
-__global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ packed,
-                                                     const uint32_t* __restrict__ scales, uint32_t N, uint32_t nb,
-                                                     uint32_t mask, const uint8_t* __restrict__ x, int64_t ldx,
+template <typename Fmt, int J, int R, int MC, int kMode, int kMaxT, int kDepth, int kStage>
+__global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32_t nb, uint32_t mask,
+                                                     const uint8_t* __restrict__ x, int64_t ldx,
                                                      float* __restrict__ y, int64_t ldy, GemvGrid gg) {
   constexpr int V = R * MC;
   static_assert(V == 1 || V == 2 || V == 4 || V == 8, "R * MC must be 1, 2, 4 or 8");
@@ -263,10 +364,11 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   // the cross-wavefront partial sums.
   constexpr int kXsBytes = kStage ? kStageFloats * 4 : 0;
   constexpr int kRedBytes = kRing * (kMaxT / 64) * V * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLutBytes + kXsBytes + kRedBytes];
+  constexpr int kTable = Fmt::kLut ? kLutBytes : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kTable + kXsBytes + kRedBytes];
   uint8_t* const lut = smem;
-  float* const xs = reinterpret_cast<float*>(smem + kLutBytes);
-  float (*const red)[kMaxT / 64][V] = reinterpret_cast<float (*)[kMaxT / 64][V]>(smem + kLutBytes + kXsBytes);
+  float* const xs = reinterpret_cast<float*>(smem + kTable);
+  float (*const red)[kMaxT / 64][V] = reinterpret_cast<float (*)[kMaxT / 64][V]>(smem + kTable + kXsBytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,20 +388,18 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   // discarded (x' is zero past the last block; rows past N are not written).
   static_assert(kDepth >= 1 && kDepth <= 3, "kDepth must be 1, 2 or 3");
   constexpr int RB = kDepth >= 2 ? R : 1, RC = kDepth >= 3 ? R : 1;
-  uint4 pa[R][J], pb[RB][J], pc[RC][J];
-  uint32_t sa[R][J], sb[RB][J], sc[RC][J];
-  auto load_tile = [&](uint32_t t, auto& p, auto& s) {
+  using Raw = typename Fmt::Raw;
+  Raw pa[R][J], pb[RB][J], pc[RC][J];
+  fmt.prepare();
+  auto load_tile = [&](uint32_t t, auto& p) {
     const uint32_t row0 = (t * S + slot) * R;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t row = min(row0 + r, N - 1);
-      const uint4* prow = packed + (size_t)row * nb;
-      const uint32_t* srow = scales + (size_t)row * nb;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const uint32_t b = min((uint32_t)(lk + j * TK), nb - 1);
-        p[r][j] = prow[b];
-        s[r][j] = srow[b];
+        p[r][j] = fmt.load(row, nb, b);
       }
     }
   };
@@ -323,11 +423,11 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
       for (int m = 0; m < MC; ++m) load_block<kXbf16>(x + m * ldx + (size_t)b * (kXbf16 ? 64 : 128), xr[j][m]);
     }
   }
-  load_tile(t, pa, sa);
-  if constexpr (kDepth >= 2) load_tile(min(t + G, last), pb, sb);
-  if constexpr (kDepth >= 3) load_tile(min(t + 2 * G, last), pc, sc);
+  load_tile(t, pa);
+  if constexpr (kDepth >= 2) load_tile(min(t + G, last), pb);
+  if constexpr (kDepth >= 3) load_tile(min(t + 2 * G, last), pc);
 
-  fill_pair_lut(lut, tid, nthreads);
+  if constexpr (Fmt::kLut) fill_pair_lut(lut, tid, nthreads);
 
   if constexpr (kStage) {
     xst.store(nb * 32, mask, xs, tid, nthreads);
@@ -392,7 +492,7 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
     __syncthreads();                        // the ring slots are rewritten next
   };
 
-  auto do_tile = [&](uint32_t tt, const auto& p, const auto& s) {
+  auto do_tile = [&](uint32_t tt, const auto& p) {
     float v[V];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -400,7 +500,7 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
 #pragma unroll
       for (int m = 0; m < MC; ++m) acc[m] = 0.f;
 #pragma unroll
-      for (int j = 0; j < J; ++j) decode_block<MC>(p[r][j], s[r][j], xr[j], lut, laneoff, acc);
+      for (int j = 0; j < J; ++j) fmt.template decode<MC>(p[r][j], xr[j], lut, laneoff, acc);
 #pragma unroll
       for (int m = 0; m < MC; ++m) v[r * MC + m] = acc[m];
     }
@@ -432,42 +532,42 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(const uint4* __restrict__ p
   // last tile (cache hits) and are discarded.
   if constexpr (kDepth == 1) {
     for (uint32_t i = 1; i < n; ++i) {
-      do_tile(t, pa, sa);
+      do_tile(t, pa);
       t += G;
-      load_tile(t, pa, sa);
+      load_tile(t, pa);
     }
-    do_tile(t, pa, sa);
+    do_tile(t, pa);
   } else if constexpr (kDepth == 2) {
     uint32_t i = 0;
     for (; i + 2 <= n; i += 2) {
-      do_tile(t, pa, sa);
-      load_tile(min(t + 2 * G, last), pa, sa);
+      do_tile(t, pa);
+      load_tile(min(t + 2 * G, last), pa);
       __builtin_amdgcn_sched_barrier(0);     // keep the reload ahead of the next tile's math
       t += G;
-      do_tile(t, pb, sb);
-      load_tile(min(t + 2 * G, last), pb, sb);
+      do_tile(t, pb);
+      load_tile(min(t + 2 * G, last), pb);
       __builtin_amdgcn_sched_barrier(0);
       t += G;
     }
-    if (i < n) do_tile(t, pa, sa);
+    if (i < n) do_tile(t, pa);
   } else {
     uint32_t i = 0;
     for (; i + 3 <= n; i += 3) {
-      do_tile(t, pa, sa);
-      load_tile(min(t + 3 * G, last), pa, sa);
+      do_tile(t, pa);
+      load_tile(min(t + 3 * G, last), pa);
       __builtin_amdgcn_sched_barrier(0);
       t += G;
-      do_tile(t, pb, sb);
-      load_tile(min(t + 3 * G, last), pb, sb);
+      do_tile(t, pb);
+      load_tile(min(t + 3 * G, last), pb);
       __builtin_amdgcn_sched_barrier(0);
       t += G;
-      do_tile(t, pc, sc);
-      load_tile(min(t + 3 * G, last), pc, sc);
+      do_tile(t, pc);
+      load_tile(min(t + 3 * G, last), pc);
       __builtin_amdgcn_sched_barrier(0);
       t += G;
     }
-    if (i < n) do_tile(t, pa, sa);
-    if (i + 1 < n) do_tile(t + G, pb, sb);
+    if (i < n) do_tile(t, pa);
+    if (i + 1 < n) do_tile(t + G, pb);
   }
   if (WK > 1 && ti % kRing != 0) flush(ti - ti % kRing, ti % kRing);
 }
@@ -509,9 +609,9 @@ uint32_t grid_cap(int threads) {
   return (uint32_t)(device_cu_count() * per_cu);
 }
 
-template <int J, int R, int MC, int kMaxT, int kDepth, int kStage = 0>
-void launch_cfg(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x,
-                int64_t ldx, int mode, float* y, int64_t ldy, const Plan& pl, hipStream_t s) {
+template <typename Fmt, int J, int R, int MC, int kMaxT, int kDepth, int kStage = 0>
+void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int64_t ldx, int mode,
+                float* y, int64_t ldy, const Plan& pl, hipStream_t s) {
   const int S = pl.threads / pl.TK;
   const uint32_t rows_per_tile = (uint32_t)(S * R);
   const uint32_t tiles = (N + rows_per_tile - 1) / rows_per_tile;
@@ -529,13 +629,13 @@ void launch_cfg(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, ui
   gg.q = tiles / grid;
   gg.r = tiles % grid;
 #define TQ_GEMV_LAUNCH(M_)                                                                                     \
-  hipLaunchKernelGGL((gemv_kernel<J, R, MC, M_, kMaxT, kDepth, kStage>), dim3(grid), dim3(pl.threads), 0, s, pk, sc, N, \
-                     nb, mask, x, ldx, y, ldy, gg)
+  hipLaunchKernelGGL((gemv_kernel<Fmt, J, R, MC, M_, kMaxT, kDepth, kStage>), dim3(grid), dim3(pl.threads), 0, s, \
+                     fmt, N, nb, mask, x, ldx, y, ldy, gg)
   switch (mode) {
     case 0: TQ_GEMV_LAUNCH(0); break;
     case 1: TQ_GEMV_LAUNCH(1); break;
-    case 2: TQ_GEMV_LAUNCH(2); break;
-    default: TQ_GEMV_LAUNCH(3); break;
+    case 2: if constexpr (Fmt::kLut) TQ_GEMV_LAUNCH(2); break;   // rotation: TQ4_1S only
+    default: if constexpr (Fmt::kLut) TQ_GEMV_LAUNCH(3); break;
   }
 #undef TQ_GEMV_LAUNCH
 }
@@ -549,9 +649,9 @@ constexpr int kGemvDepth = 2;
 constexpr bool kGemvStage = true;
 constexpr int kGemvMinJ = 1;
 
-template <int J>
-void launch_gemv_j(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x,
-                   int mode, float* y, hipStream_t s) {
+template <typename Fmt, int J>
+void launch_gemv_j(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int mode, float* y,
+                   hipStream_t s) {
   const Plan pl = plan_for(nb, 1024, J);
   // Groups of 4 elements each thread stages (a power of two, at most 8).
   const uint32_t K = nb * 32, per = 4u * (uint32_t)pl.threads;
@@ -559,70 +659,99 @@ void launch_gemv_j(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb,
   constexpr int R = kGemvRows, D = kGemvDepth;
   if constexpr (J <= 2) {
     if (kGemvStage && K <= (uint32_t)kStageFloats && passes <= 8) {
-      if (passes <= 1) launch_cfg<J, R, 1, 1024, D, 1>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
-      else if (passes <= 2) launch_cfg<J, R, 1, 1024, D, 2>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
-      else if (passes <= 4) launch_cfg<J, R, 1, 1024, D, 4>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
-      else launch_cfg<J, R, 1, 1024, D, 8>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      if (passes <= 1) launch_cfg<Fmt, J, R, 1, 1024, D, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else if (passes <= 2) launch_cfg<Fmt, J, R, 1, 1024, D, 2>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else if (passes <= 4) launch_cfg<Fmt, J, R, 1, 1024, D, 4>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else launch_cfg<Fmt, J, R, 1, 1024, D, 8>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
       return;
     }
   }
-  // Larger K: every lane loads and rotates its own blocks; the loads of the
+  // Larger K: every lane loads (and rotates) its own blocks; the loads of the
   // next tile only fit in registers (without spills) at one block per lane.
-  launch_cfg<J, 2, 1, 1024, J == 1 ? D : 1>(pk, sc, N, nb, mask, x, 0, mode, y, 0, pl, s);
+  launch_cfg<Fmt, J, 2, 1, 1024, J == 1 ? D : 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+}
+
+template <typename Fmt>
+void launch_gemv_fmt(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int mode, float* y,
+                     hipStream_t s) {
+  const int J = min_j(nb, 1024) > kGemvMinJ ? min_j(nb, 1024) : kGemvMinJ;
+  switch (J) {
+    case 1: launch_gemv_j<Fmt, 1>(fmt, N, nb, mask, x, mode, y, s); break;
+    case 2: launch_gemv_j<Fmt, 2>(fmt, N, nb, mask, x, mode, y, s); break;
+    case 3: launch_gemv_j<Fmt, 3>(fmt, N, nb, mask, x, mode, y, s); break;
+    default: launch_gemv_j<Fmt, 4>(fmt, N, nb, mask, x, mode, y, s); break;
+  }
+}
+
+// VALU small-batch path for M < 16: chunks of MC = 4, 2 or 1 activation rows
+// held in registers (float32, 32 VGPRs per row per owned block), one launch
+// per chunk; workgroups of at most 256 threads leave 256 VGPRs per lane.
+template <typename Fmt>
+void launch_gemm_valu_fmt(const Fmt& fmt, uint32_t N, uint32_t nb, int64_t M, const uint8_t* xb, int mode,
+                          int64_t ldx_bytes, float* y, int64_t ldy, hipStream_t s) {
+  for (int64_t m0 = 0; m0 < M;) {
+    const int64_t left = M - m0;
+    const uint8_t* xm = xb + m0 * ldx_bytes;
+    float* ym = y + m0 * ldy;
+    if (left >= 4 && nb <= 256) {
+      const Plan pl = plan_for(nb, 256, 1);
+      launch_cfg<Fmt, 1, 2, 4, 256, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      m0 += 4;
+    } else if (left >= 2 && nb <= 512) {
+      const Plan pl = plan_for(nb, 512, 1);
+      launch_cfg<Fmt, 1, 2, 2, 512, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      m0 += 2;
+    } else {
+      const Plan pl = plan_for(nb, 1024, min_j(nb, 1024));
+      switch (pl.J) {
+        case 1: launch_cfg<Fmt, 1, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        case 2: launch_cfg<Fmt, 2, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        case 3: launch_cfg<Fmt, 3, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        default: launch_cfg<Fmt, 4, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+      }
+      m0 += 1;
+    }
+  }
+}
+
+FmtTQ4 tq4_format(const uint8_t* packed, const uint16_t* scales) {
+  return FmtTQ4{reinterpret_cast<const uint4*>(packed), reinterpret_cast<const uint32_t*>(scales)};
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t mask,
                        const void* x, bool xbf16, bool rotated, float* y, hipStream_t s) {
-  const uint32_t nb = (uint32_t)(K / kBlock);
   const int mode = rotated ? (xbf16 ? 1 : 0) : (xbf16 ? 3 : 2);
-  const uint4* pk = reinterpret_cast<const uint4*>(packed);
-  const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
-  const uint8_t* xb = static_cast<const uint8_t*>(x);
-  const int J = min_j(nb, 1024) > kGemvMinJ ? min_j(nb, 1024) : kGemvMinJ;
-  switch (J) {
-    case 1: launch_gemv_j<1>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
-    case 2: launch_gemv_j<2>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
-    case 3: launch_gemv_j<3>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
-    default: launch_gemv_j<4>(pk, sc, (uint32_t)N, nb, mask, xb, mode, y, s); break;
-  }
+  launch_gemv_fmt(tq4_format(packed, scales), (uint32_t)N, (uint32_t)(K / kBlock), mask,
+                  static_cast<const uint8_t*>(x), mode, y, s);
   return hipGetLastError();
 }
 
-// VALU path of tq_gemm for M < 16: chunks of MC = 4, 2 or 1 activation rows
-// held in registers (float32, 32 VGPRs per row per owned block), one launch
-// per chunk; workgroups of at most 256 threads leave 256 VGPRs per lane.
 hipError_t launch_gemm_valu(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
                             const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
-  const uint32_t nb = (uint32_t)(K / kBlock);
-  const uint4* pk = reinterpret_cast<const uint4*>(packed);
-  const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
+  launch_gemm_valu_fmt(tq4_format(packed, scales), (uint32_t)N, (uint32_t)(K / kBlock), M,
+                       static_cast<const uint8_t*>(xr), xbf16 ? 1 : 0, ldx * (xbf16 ? 2 : 4), y, ldy, s);
+  return hipGetLastError();
+}
+
+// Block-float decode GEMV/GEMM (M < 16 per launch chunk, VALU) on the same
+// kernels: the activation is used as given (no rotation).
+hipError_t launch_blockfp_gemv(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
+                               int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
+                               hipStream_t s) {
+  const uint32_t nb = (uint32_t)(K / 32);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
   const int mode = xbf16 ? 1 : 0;
-  const int64_t xs = xbf16 ? 2 : 4;
-  const uint8_t* xb = static_cast<const uint8_t*>(xr);
-  for (int64_t m0 = 0; m0 < M;) {
-    const int64_t left = M - m0;
-    const uint8_t* xm = xb + m0 * ldx * xs;
-    float* ym = y + m0 * ldy;
-    if (left >= 4 && nb <= 256) {
-      const Plan pl = plan_for(nb, 256, 1);
-      launch_cfg<1, 2, 4, 256, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s);
-      m0 += 4;
-    } else if (left >= 2 && nb <= 512) {
-      const Plan pl = plan_for(nb, 512, 1);
-      launch_cfg<1, 2, 2, 512, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s);
-      m0 += 2;
-    } else {
-      const Plan pl = plan_for(nb, 1024, min_j(nb, 1024));
-      switch (pl.J) {
-        case 1: launch_cfg<1, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-        case 2: launch_cfg<2, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-        case 3: launch_cfg<3, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-        default: launch_cfg<4, 2, 1, 1024, 1>(pk, sc, (uint32_t)N, nb, 0u, xm, ldx * xs, mode, ym, ldy, pl, s); break;
-      }
-      m0 += 1;
-    }
+  const int64_t ldx_bytes = ldx * (xbf16 ? 2 : 4);
+  if (fmt == TQ_FMT_NVFP4) {
+    const FmtNVFP4 f{reinterpret_cast<const uint4*>(codes), reinterpret_cast<const uint16_t*>(bscales), tscale, 0.f};
+    if (M == 1) launch_gemv_fmt(f, (uint32_t)N, nb, 0u, xb, mode, y, s);
+    else launch_gemm_valu_fmt(f, (uint32_t)N, nb, M, xb, mode, ldx_bytes, y, ldy, s);
+  } else {
+    const FmtMXFP6 f{reinterpret_cast<const uint2*>(codes), bscales};
+    if (M == 1) launch_gemv_fmt(f, (uint32_t)N, nb, 0u, xb, mode, y, s);
+    else launch_gemm_valu_fmt(f, (uint32_t)N, nb, M, xb, mode, ldx_bytes, y, ldy, s);
   }
   return hipGetLastError();
 }

@@ -174,6 +174,12 @@ __device__ __forceinline__ uint32_t pair_addr(uint32_t w, uint32_t laneoff, int 
   return __builtin_amdgcn_perm(w, laneoff, 0x0C0C0000u | ((4u + (uint32_t)k) << 8));
 }
 
+// E4M3fn code (no sign) -> float32, exact: bias 7, subnormal step 2^-9.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e == 0u ? (float)m * 0x1p-9f : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+}
+
 // Load one 32-element block (fp32 or bf16) into registers; p is 16-byte aligned.
 template <bool kBf16>
 __device__ __forceinline__ void load_block(const void* p, float (&v)[32]) {
@@ -215,6 +221,9 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
                        const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K,
                                    uint8_t* codes, uint8_t* bscales, float* tscale, hipStream_t s);
+hipError_t launch_blockfp_gemv(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
+                               int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
+                               hipStream_t s);
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
                                float* y, int64_t ldy, hipStream_t s);
