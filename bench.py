@@ -178,23 +178,23 @@ def main():
         group_ms[gname] = ms
         per_group[gname] = {"N": n, "K": k, "us": round(ms * 1e3, 2),
                             "GB_s": round(gemv_bytes(n, k, xb) / (ms * 1e-3) / 1e9, 1)}
-    # Roofline of the dominant kernel: the instantiation that serves the
-    # K = 4096 groups (q|k|v, o, gate|up: 96 of the 128 launches of a step and
-    # 72% of its bytes); down (K = 14336) stages its activation in four
-    # passes per thread and is a separate instantiation.
-    dom = [g for g, (n, k) in groups.items() if k == 4096]
+    # Roofline of the dominant kernel: the instantiation that serves q|k|v and
+    # gate|up (K = 4096, one row per wavefront; 64 of the 128 launches of a
+    # step and 57% of its bytes).  o (one two-row tile per workgroup) and down
+    # (K = 14336, activation staged in four passes) are other instantiations.
+    from dequant_gemv_tq_amd import profiling as tq_profiling
+    dom = list(tq_profiling.DOMINANT)
     dom_bytes = sum(gemv_bytes(groups[g][0], groups[g][1], xb) for g in dom)
     dom_ms = sum(group_ms[g] for g in dom)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     layer_kernel_ms = sum(group_ms.values())   # the four group launches of one layer
     # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
     # or None when it was taken from other kernel sources than these.
-    from dequant_gemv_tq_amd import profiling as tq_profiling
     rec = tq_profiling.read_record(os.path.join(ROOT, "profiles", "gemv_traffic_llama8b.md"))
     traffic = rec["traffic_bytes_per_launch"] if (rec and not args.prerotate) else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_kernel<1, 2, 1, 3, 1024, 2, 1> (fused TQ4_1S GEMV, bf16 x, K = 4096)",
+                "kernel": f"{tq_profiling.DOMINANT_KERNEL} (fused TQ4_1S GEMV, bf16 x, K = 4096)",
                 "groups": dom, "launches_per_step": len(dom) * L,
                 "bytes_per_launch_avg": round(dom_bytes / len(dom)),
                 "avg_launch_us": round(dom_ms / len(dom) * 1e3, 2)}

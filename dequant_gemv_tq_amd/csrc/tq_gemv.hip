@@ -641,22 +641,24 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
 }
 
 // Decode GEMV shape, measured on MI355X over the Llama-3-8B and 70B decode
-// layers: two rows per wavefront per tile, one tile of loads in flight ahead
-// of the one being computed, x' staged in LDS, the fewest K-blocks per lane
-// that fit a row into a 1024-thread workgroup.
-constexpr int kGemvRows = 2;
+// layers: one tile of loads in flight ahead of the one being computed, x'
+// staged in LDS, the fewest K-blocks per lane that fit a row into a
+// 1024-thread workgroup, and one row per wavefront per tile -- except when a
+// single round of two-row tiles already covers the matrix (one tile per
+// workgroup, nothing to pipeline), where two rows per wavefront halve the
+// per-row reduction work.  (Llama-3-8B decode groups, graph-timed: q|k|v
+// 7.4 -> 6.6 us, gate|up 16.8 -> 15.6 us with one row; o 5.7 us with two.)
 constexpr int kGemvDepth = 2;
 constexpr bool kGemvStage = true;
 constexpr int kGemvMinJ = 1;
 
-template <typename Fmt, int J>
-void launch_gemv_j(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int mode, float* y,
-                   hipStream_t s) {
-  const Plan pl = plan_for(nb, 1024, J);
+template <typename Fmt, int J, int R>
+void launch_gemv_jr(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int mode, float* y,
+                    const Plan& pl, hipStream_t s) {
   // Groups of 4 elements each thread stages (a power of two, at most 8).
   const uint32_t K = nb * 32, per = 4u * (uint32_t)pl.threads;
   const uint32_t passes = (K + per - 1) / per;
-  constexpr int R = kGemvRows, D = kGemvDepth;
+  constexpr int D = kGemvDepth;
   if constexpr (J <= 2) {
     if (kGemvStage && K <= (uint32_t)kStageFloats && passes <= 8) {
       if (passes <= 1) launch_cfg<Fmt, J, R, 1, 1024, D, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
@@ -668,7 +670,17 @@ void launch_gemv_j(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const
   }
   // Larger K: every lane loads (and rotates) its own blocks; the loads of the
   // next tile only fit in registers (without spills) at one block per lane.
-  launch_cfg<Fmt, J, 2, 1, 1024, J == 1 ? D : 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+  launch_cfg<Fmt, J, R, 1, 1024, J == 1 ? D : 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+}
+
+template <typename Fmt, int J>
+void launch_gemv_j(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int mode, float* y,
+                   hipStream_t s) {
+  const Plan pl = plan_for(nb, 1024, J);
+  const uint32_t slots = (uint32_t)(pl.threads / pl.TK);
+  const uint32_t tiles2 = (N + 2u * slots - 1u) / (2u * slots);
+  if (tiles2 <= grid_cap(pl.threads)) launch_gemv_jr<Fmt, J, 2>(fmt, N, nb, mask, x, mode, y, pl, s);
+  else launch_gemv_jr<Fmt, J, 1>(fmt, N, nb, mask, x, mode, y, pl, s);
 }
 
 template <typename Fmt>

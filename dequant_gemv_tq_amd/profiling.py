@@ -39,7 +39,8 @@ GROUPS = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "dow
 MEMBERS = {"qkv": ["q", "k", "v"], "o": ["o"], "gate_up": ["gate", "up"], "down": ["down"]}
 COPIES = 8
 COPY_BYTES = 1 << 30
-DOMINANT = ("qkv", "o", "gate_up")          # groups served by the K = 4096 instantiation
+DOMINANT = ("qkv", "gate_up")               # groups served by the dominant instantiation
+DOMINANT_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1>"   # K = 4096, one row per wavefront
 SOURCES = ("csrc/tq_gemv.hip", "csrc/tq_internal.hpp")
 
 
@@ -142,12 +143,12 @@ def summarize(fetch_db: str, write_db: str) -> None:
             dom_t += t
             dom_a += alg
         lines.append(f"| {gname} | {n} x {k} | {fk:.0f} | {wk:.0f} | {t / 1e6:.2f} | {alg / 1e6:.2f} | {t / alg:.3f} |")
-    rec = {"kernel": "gemv_kernel<1, 2, 1, 3, 1024, 2, 1>", "groups": list(DOMINANT),
+    rec = {"kernel": DOMINANT_KERNEL, "groups": list(DOMINANT),
            "traffic_bytes_per_launch": round(dom_t / len(DOMINANT)),
            "algorithmic_bytes_per_launch": round(dom_a / len(DOMINANT)),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "source_sha256": source_hash()}
-    lines += ["", "Per launch of the dominant instantiation (mean over q|k|v, o, gate|up):", "",
+    lines += ["", "Per launch of the dominant instantiation (mean over q|k|v and gate|up):", "",
               f"traffic-json: {json.dumps(rec)}", ""]
     print("\n".join(lines))
 
@@ -172,15 +173,18 @@ def stats(csv_path: str) -> None:
         m = re.search(r"tq::\(anonymous namespace\)::(\w+(?:<[^>]*>)?)", r["Name"])
         if not m:
             continue
-        lines.append(f"| `{m.group(1)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        name = m.group(1).replace("tq::(anonymous namespace)::", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.2f}% |")
-    lines += ["", "The decode GEMV of the q|k|v, o and gate|up groups (K = 4096, bf16 activation, rotation "
-              "fused) is `gemv_kernel<1, 2, 1, 3, 1024, 2, 1>`; down (K = 14336) is "
-              "`gemv_kernel<1, 2, 1, 3, 1024, 2, 4>`.  Other kernels: the quantizer, the small-batch GEMM "
-              "(VALU `gemv_kernel<..., MC, 1, ...>` for M < 16, `gemm_mfma_kernel` for M >= 16), "
-              "dequantization and the NVFP4 / MXFP6 rows; the remaining GPU time is PyTorch drawing the "
-              "synthetic weights.", ""]
+    lines += ["", "Decode GEMV instantiations `gemv_kernel<format, J, R, MC, mode, threads, depth, stage>`: "
+              "q|k|v and gate|up (K = 4096, bf16 activation, rotation fused, one row per wavefront) run "
+              f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 2, 1>`; down "
+              "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 4>`.  "
+              "Other kernels: the quantizer, the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M < 16, "
+              "`gemm_mfma_kernel` for M >= 16), dequantization and the NVFP4 / MXFP6 rows (`gemv_kernel<FmtNVFP4"
+              ", ...>`, `gemv_kernel<FmtMXFP6, ...>`); the remaining GPU time is PyTorch drawing the synthetic "
+              "weights.", ""]
     print("\n".join(lines))
 
 
