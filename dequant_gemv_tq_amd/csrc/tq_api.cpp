@@ -125,7 +125,8 @@ tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* bloc
   if (K % 32) return TQ_ESHAPE;
   if (M > 16 || K > 32768 || N > 0x7fffffff) return TQ_ESHAPE;
   if (!float_or_bf16(xt)) return TQ_EDTYPE;
-  if (!aligned(codes, 8) || !aligned(x, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4)) return TQ_EALIGN;
+  if (!aligned(codes, f == TQ_FMT_NVFP4 ? 16 : 8) || !aligned(x, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4))
+    return TQ_EALIGN;
   if (f == TQ_FMT_NVFP4 && (!aligned(block_scales, 2) || !aligned(tensor_scale, 4))) return TQ_EALIGN;
   return from_hip(tq::launch_blockfp_gemm((int)f, codes, block_scales, tensor_scale, N, K, M, x, xt == TQ_BF16, ldx,
                                           y, ldy, stream));

@@ -81,8 +81,10 @@ const char* tq_status_str(int status);
 /* [host] The 16 centroids (ascending) of the 16-level Lloyd-Max quantizer of
  * N(0,1) and the 15 decision thresholds m_k = float32((c_k + c_{k+1}) / 2),
  * as the kernels use them (TQ4 page, "格式原理" item 2 and the paragraph after
- * it: Lloyd's algorithm on the rotated-coordinate law).  The library computes
- * them once, in double precision, to a fixed point and rounds to float32.
+ * it: Lloyd's algorithm on the rotated-coordinate law).  The centroids are
+ * the fixed point of Lloyd's iteration computed in double precision and
+ * rounded once to float32; the library ships these float32 constants (the
+ * kernels use them as immediates) and forms the thresholds from them.
  * Either pointer may be NULL.  Returns TQ_OK. */
 tq_status tq_codebook(float centroids[16], float thresholds[15]);
 
@@ -177,9 +179,15 @@ tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N
                               hipStream_t stream);
 
 /* Y[m, n] = sum_k W_deq[n, k] X[m, k] for a block-float weight (fused
- * decode, float32 accumulation).  X [M, K] row stride ldx, TQ_F32 or
- * TQ_BF16, 16-byte aligned; Y [M, N] float32, row stride ldy.  K % 32 == 0,
- * K <= 32768, M <= 16; NVFP4 block_scales 2-byte aligned.
+ * decode, float32 accumulation; the activation is used as given, there is
+ * no rotation).  Codes are decoded by gfx950's scaled-convert instructions
+ * (E2M1 two at a time, E3M2 a whole 32-element block at a time, scale 1,
+ * exact); each 16- (NVFP4) or 32-element (MXFP6) partial sum is multiplied
+ * once by its scale: float32(e4m3 * tensor_scale) for NVFP4, 2^(e8m0 - 127)
+ * (ldexp, exact) for MXFP6.  X [M, K] row stride ldx, TQ_F32 or TQ_BF16,
+ * 16-byte aligned; Y [M, N] float32, row stride ldy.  K % 32 == 0,
+ * K <= 32768, M <= 16; NVFP4 codes 16-byte aligned (MXFP6 codes 8-byte),
+ * NVFP4 block_scales 2-byte aligned.
  * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales,
                           const float* tensor_scale, int64_t N, int64_t K, int64_t M,

@@ -106,6 +106,8 @@ def test_other_calls_reject_before_launch():
     assert L.tq_blockfp_quantize(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
     assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 17, g, F32, 64, g, 8, None) == ESHAPE
     assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None) == EDTYPE
+    assert L.tq_blockfp_gemm(1, _p(GOOD + 8), g, g, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN   # NVFP4 codes: 16 B
+    assert L.tq_blockfp_gemm(2, _p(GOOD + 4), g, None, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN  # MXFP6 codes: 8 B
 
 
 def test_binding_refuses_cpu_tensors():
