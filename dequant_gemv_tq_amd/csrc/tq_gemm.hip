@@ -113,28 +113,36 @@ __device__ __forceinline__ void transpose_groups(const uint4& p, uint32_t (&out)
 template <bool kF32X>
 struct AOperand;
 
+// Activation operand loads are issued unconditionally from a clamped,
+// in-bounds address (row min(m, M - 1), element k of a block that exists)
+// and the operand is zeroed afterwards when (m, block) lies outside X: a
+// load under a lane condition becomes an exec-masked branch, after which the
+// compiler can no longer count outstanding loads and waits for all of them.
 template <>
 struct AOperand<false> {                  // bf16 activations: one operand per (step, m tile)
   uint4 a;
+  bool live;
   __device__ __forceinline__ void load(const uint8_t* X, int64_t ldx, uint32_t m, uint32_t M, uint32_t k, bool ok) {
-    a = make_uint4(0u, 0u, 0u, 0u);
-    if (ok && m < M) a = *reinterpret_cast<const uint4*>(X + ((size_t)m * ldx + k) * 2);
+    a = *reinterpret_cast<const uint4*>(X + ((size_t)min(m, M - 1u) * ldx + k) * 2);
+    live = ok && m < M;
   }
+  __device__ __forceinline__ uint4 value() const { return live ? a : make_uint4(0u, 0u, 0u, 0u); }
 };
 
 template <>
-struct AOperand<true> {                   // float32 activations, kept as bf16 hi/lo
-  bf16x8 hi, lo;
+struct AOperand<true> {                   // float32 activations, split to bf16 hi/lo at use
   float raw[8];
+  bool live;
   __device__ __forceinline__ void load(const uint8_t* X, int64_t ldx, uint32_t m, uint32_t M, uint32_t k, bool ok) {
+    const float4* src = reinterpret_cast<const float4*>(X + ((size_t)min(m, M - 1u) * ldx + k) * 4);
+    const float4 u0 = src[0], u1 = src[1];
+    raw[0] = u0.x; raw[1] = u0.y; raw[2] = u0.z; raw[3] = u0.w;
+    raw[4] = u1.x; raw[5] = u1.y; raw[6] = u1.z; raw[7] = u1.w;
+    live = ok && m < M;
+  }
+  __device__ __forceinline__ void value(float (&v)[8]) const {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) raw[t] = 0.f;
-    if (ok && m < M) {
-      const float4* src = reinterpret_cast<const float4*>(X + ((size_t)m * ldx + k) * 4);
-      const float4 u0 = src[0], u1 = src[1];
-      raw[0] = u0.x; raw[1] = u0.y; raw[2] = u0.z; raw[3] = u0.w;
-      raw[4] = u1.x; raw[5] = u1.y; raw[6] = u1.z; raw[7] = u1.w;
-    }
+    for (int t = 0; t < 8; ++t) v[t] = live ? raw[t] : 0.f;
   }
 };
 
@@ -202,8 +210,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
   auto load_a = [&](int set, uint32_t q, int s) {
     const uint32_t b = 4u * q + (uint32_t)s;
     const bool ok = b < nb;
+    const uint32_t bc = min(b, nb - 1u);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) A[set][s][mt].load(X, ldx, mt * 16u + (uint32_t)nl, M, 32u * b + 8u * g, ok);
+    for (int mt = 0; mt < MT; ++mt) A[set][s][mt].load(X, ldx, mt * 16u + (uint32_t)nl, M, 32u * bc + 8u * g, ok);
   };
 
   if (nq > 0u) {
@@ -262,13 +271,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if constexpr (!kF32X) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, A[ja][s][mt].a);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, A[ja][s][mt].value());
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
               acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Bh[rt], acc[rt][mt], 0, 0, 0);
           } else {
             bf16x8 ah, al;
-            split8(A[ja][s][mt].raw, ah, al);
+            float av[8];
+            A[ja][s][mt].value(av);
+            split8(av, ah, al);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
               acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, Bh[rt], acc[rt][mt], 0, 0, 0);
