@@ -31,6 +31,10 @@
 //     at every cross-lane step, ~2.5 VALU ops per row instead of ~11.
 //   * Several wavefronts along K (TK = 64 * WK lanes per row slot) combine
 //     through a small double-buffered LDS array, one barrier per tile.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "tq_internal.hpp"
 
 namespace tq {
@@ -609,6 +613,27 @@ uint32_t grid_cap(int threads) {
   return (uint32_t)(device_cu_count() * per_cu);
 }
 
+// Persistent grid of one instantiation: the workgroups all compute units hold
+// at once, as the runtime's occupancy calculator gives them for its register
+// and LDS use (a grid larger than that runs a second round of workgroups,
+// each paying the prologue again).  Cached per kernel, size and device.
+uint32_t resident_grid(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int>, uint32_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(kernel, threads, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int blocks = 0;
+  uint32_t g = grid_cap(threads);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, 0) == hipSuccess && blocks > 0)
+    g = (uint32_t)(blocks * device_cu_count());
+  cache.emplace(key, g);
+  return g;
+}
+
 template <typename Fmt, int J, int R, int MC, int kMaxT, int kDepth, int kStage = 0>
 void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int64_t ldx, int mode,
                 float* y, int64_t ldy, const Plan& pl, hipStream_t s) {
@@ -618,7 +643,15 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
   // As many workgroups as fit the chip, trimmed so that every workgroup gets
   // the same number of tiles or one fewer (a round of 1.5 tiles per CU would
   // leave half the chip idle for the second half of the launch).
-  const uint32_t cap = grid_cap(pl.threads);
+  const void* kern = nullptr;
+  switch (mode) {
+    case 0: kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 0, kMaxT, kDepth, kStage>; break;
+    case 1: kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 1, kMaxT, kDepth, kStage>; break;
+    case 2: if constexpr (Fmt::kLut) kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 2, kMaxT, kDepth, kStage>; break;
+    default: if constexpr (Fmt::kLut) kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 3, kMaxT, kDepth, kStage>; break;
+  }
+  if (!kern) return;                         // rotation modes exist for TQ4_1S only (the entry points check)
+  const uint32_t cap = resident_grid(kern, pl.threads);
   const uint32_t per_wg = (tiles + cap - 1) / cap;
   const uint32_t grid = (tiles + per_wg - 1) / per_wg;
   GemvGrid gg;
@@ -697,7 +730,10 @@ void launch_gemv_fmt(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, con
 
 // VALU small-batch path for M < 16: chunks of MC = 4, 2 or 1 activation rows
 // held in registers (float32, 32 VGPRs per row per owned block), one launch
-// per chunk; workgroups of at most 256 threads leave 256 VGPRs per lane.
+// per chunk, each keeping the next tile's weights in flight.  Four rows fit
+// 256-thread workgroups up to K = 8192, two rows 512- or 1024-thread
+// workgroups up to K = 32768 (one row per wavefront per tile at 1024
+// threads, where the register budget is 128).
 template <typename Fmt>
 void launch_gemm_valu_fmt(const Fmt& fmt, uint32_t N, uint32_t nb, int64_t M, const uint8_t* xb, int mode,
                           int64_t ldx_bytes, float* y, int64_t ldy, hipStream_t s) {
@@ -707,16 +743,20 @@ void launch_gemm_valu_fmt(const Fmt& fmt, uint32_t N, uint32_t nb, int64_t M, co
     float* ym = y + m0 * ldy;
     if (left >= 4 && nb <= 256) {
       const Plan pl = plan_for(nb, 256, 1);
-      launch_cfg<Fmt, 1, 2, 4, 256, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      launch_cfg<Fmt, 1, 2, 4, 256, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
       m0 += 4;
     } else if (left >= 2 && nb <= 512) {
       const Plan pl = plan_for(nb, 512, 1);
-      launch_cfg<Fmt, 1, 2, 2, 512, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      launch_cfg<Fmt, 1, 2, 2, 512, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      m0 += 2;
+    } else if (left >= 2 && nb <= 1024) {
+      const Plan pl = plan_for(nb, 1024, 1);
+      launch_cfg<Fmt, 1, 1, 2, 1024, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
       m0 += 2;
     } else {
       const Plan pl = plan_for(nb, 1024, min_j(nb, 1024));
       switch (pl.J) {
-        case 1: launch_cfg<Fmt, 1, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        case 1: launch_cfg<Fmt, 1, 2, 1, 1024, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
         case 2: launch_cfg<Fmt, 2, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
         case 3: launch_cfg<Fmt, 3, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
         default: launch_cfg<Fmt, 4, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
