@@ -334,6 +334,142 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
   }
 }
 
+// ---------------------------------------------------------------------------
+// M <= 16 with bf16 activations and K <= 4096: one persistent 1024-thread
+// workgroup per CU, shaped like the fused GEMV.  The sixteen wavefronts split
+// K (wavefront w takes groups w and w + 16 of four blocks) and keep
+// their activation operands in registers for the whole launch; the
+// workgroup walks 16-row weight tiles (tiles g, g + G, ...) with the next
+// two tiles' weights in flight while the current one is decoded and multiplied;
+// the sixteen partial 16 x 16 tiles are summed through a double-buffered LDS
+// area, one barrier per tile.  The pair table is filled once per launch.
+// ---------------------------------------------------------------------------
+constexpr int kWide = 16;
+
+template <int NQ>
+__global__ __launch_bounds__(64 * kWide) void gemm16_kernel(const uint4* __restrict__ packed,
+                                                           const uint32_t* __restrict__ scales, uint32_t N,
+                                                           uint32_t nb, const uint8_t* __restrict__ X, int64_t ldx,
+                                                           uint32_t M, float* __restrict__ Y, int64_t ldy, uint32_t G,
+                                                           uint32_t tq, uint32_t tr) {
+  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+  __shared__ f32x4 part[2][kWide][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15;
+  const uint32_t g = (uint32_t)(lane >> 4);
+  const uint32_t laneoff = (uint32_t)(lane & (kCopies - 1)) * 8u;
+  const uint32_t ngroups = (nb + 3u) / 4u;
+
+  // Activation operands of this wavefront's groups, loaded once.
+  AOperand<false> A[NQ][4];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const uint32_t q = (uint32_t)wave + (uint32_t)(kWide * j);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t b = 4u * q + (uint32_t)s;
+      A[j][s].load(X, ldx, (uint32_t)nl, M, 32u * min(b, nb - 1u) + 8u * g, b < nb);
+    }
+  }
+
+  // Weight register sets: block 4 q + g of the lane's row for each group, and its scale pair.
+  struct WSet {
+    uint4 p[NQ];
+    uint32_t sc[NQ];
+  };
+  auto load_w = [&](WSet& w, uint32_t tile) {
+    const uint32_t row = min(tile * 16u + (uint32_t)nl, N - 1u);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const uint32_t b = min(4u * ((uint32_t)wave + (uint32_t)(kWide * j)) + g, nb - 1u);
+      w.p[j] = packed[(size_t)row * nb + b];
+      w.sc[j] = scales[(size_t)row * nb + b];
+    }
+  };
+
+  uint32_t t = blockIdx.x;
+  const uint32_t n = tq + (t < tr ? 1u : 0u);
+  const uint32_t last = t + (n - 1u) * G;
+  WSet pa, pb, pc;
+  load_w(pa, t);
+  load_w(pb, min(t + G, last));
+  load_w(pc, min(t + 2 * G, last));
+  fill_pair_lut(lut, tid, 64 * kWide);
+  __syncthreads();
+
+  uint32_t parity = 0;
+  // Tile tt from register set w; w is refilled with tile `next` as soon as
+  // its registers are consumed, before the cross-wavefront reduction.
+  auto do_tile = [&](uint32_t tt, WSet& w, uint32_t next) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const uint32_t q = (uint32_t)wave + (uint32_t)(kWide * j);
+      if (q < ngroups) {                       // wavefront-uniform
+        uint32_t wt[4], sct[4];
+        transpose_groups(w.p[j], wt);
+        transpose_groups(make_uint4(w.sc[j], w.sc[j], w.sc[j], w.sc[j]), sct);
+        const uint32_t nsteps = min(4u, nb - 4u * q);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if ((uint32_t)s < nsteps) {
+            const float d = f16_bits_to_f32(g < 2u ? (sct[s] & 0xffffu) : (sct[s] >> 16));
+            float v[8];
+            dequant8(wt[s], d, lut, laneoff, v);
+            const bf16x8 B = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                       pack_bf16x2(v[6], v[7]));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[j][s].value()), B, acc, 0, 0, 0);
+          }
+        }
+      }
+    }
+    load_w(w, next);
+    part[parity][wave][lane] = acc;
+    __syncthreads();
+    if (tid < 256) {                           // output (m, row) of partial lane l = tid / 4, register r = tid % 4
+      const int l = tid >> 2, r = tid & 3;
+      float sum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kWide; ++w2) sum += part[parity][w2][l][r];
+      const uint32_t m = 4u * (uint32_t)(l >> 4) + (uint32_t)r;
+      const uint32_t row = tt * 16u + (uint32_t)(l & 15);
+      if (m < M && row < N) Y[(size_t)m * ldy + row] = sum;
+    }
+    parity ^= 1u;
+  };
+
+  // Fixed trip count with clamped, unconditional prefetches (exact waits),
+  // as in the fused GEMV.
+  uint32_t i = 0;
+  for (; i + 3 <= n; i += 3) {
+    do_tile(t, pa, min(t + 3 * G, last));
+    t += G;
+    do_tile(t, pb, min(t + 3 * G, last));
+    t += G;
+    do_tile(t, pc, min(t + 3 * G, last));
+    t += G;
+  }
+  if (i < n) do_tile(t, pa, last);
+  if (i + 1 < n) do_tile(t + G, pb, last);
+}
+
+void launch_gemm16(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
+                   uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
+  const uint32_t tiles = (N + 15u) / 16u;
+  const uint32_t cap = (uint32_t)device_cu_count();
+  const uint32_t per_wg = (tiles + cap - 1u) / cap;
+  const uint32_t grid = (tiles + per_wg - 1u) / per_wg;
+  const uint32_t nq = ((nb + 3u) / 4u + kWide - 1u) / kWide;
+#define TQ_GEMM16(NQ_)                                                                                       \
+  hipLaunchKernelGGL((gemm16_kernel<NQ_>), dim3(grid), dim3(64 * kWide), 0, s, pk, sc, N, nb, X, ldx, M, Y, ldy, \
+                     grid, tiles / grid, tiles % grid)
+  if (nq <= 1) TQ_GEMM16(1);
+  else TQ_GEMM16(2);
+#undef TQ_GEMM16
+}
+
 // Weight groups in flight per wavefront: three where the registers allow.
 template <int MT, int RT, bool kF32X>
 constexpr int gemm_depth() { return (kF32X ? 2 : 1) * MT * RT <= 4 ? 3 : 2; }
@@ -381,6 +517,10 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
     const int mt = (int)((mc + 15) / 16);
     const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
+      if (mt == 1 && nb <= 4u * kWide * 2u) {   // K <= 4096: the persistent one-tile-of-M kernel
+        launch_gemm16(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
+        continue;
+      }
       switch (mt) {
         case 1: launch_mt<1, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
         case 2: launch_mt<2, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;

@@ -196,6 +196,22 @@ def test_gemm_tall_row_tiles(m):
         assert_within(f32np(Y), yr, a, what=f"gemm tall M={m} {n}x{k}")
 
 
+@pytest.mark.parametrize("n,k", [(300, 1120), (1000, 3200), (517, 4096), (4100, 4096), (33, 2048), (90, 5120)])
+def test_gemm_m16_persistent(n, k):
+    """M = 16 with bf16 activations and K <= 4096 runs the persistent kernel whose 16 wavefronts split K:
+    one or two groups of four blocks per wavefront, some wavefronts idle, ragged row tiles (K = 5120 takes
+    the other kernel)."""
+    m = 16
+    g = workloads.generator(n * 7 + k, DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    X = workloads.activation(m, k, g, DEV, torch.bfloat16)
+    packed, scales = tqa.quantize(W)
+    say(f"[gemm] persistent M=16 {n}x{k}")
+    Y = tqa.gemm(packed, scales, tqa.rotate(X, dtype=torch.bfloat16))
+    yr, a = otq.gemm_o64(packed.cpu().numpy(), u16(scales), X.float().cpu().numpy())
+    assert_within(f32np(Y), yr, a, what=f"gemm M=16 {n}x{k}")
+
+
 def test_gemm_bf16_large_k():
     """bf16 activations (one MFMA pass) at the decode shapes' K."""
     for k in (4096, 14336):
