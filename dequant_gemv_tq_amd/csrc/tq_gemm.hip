@@ -38,6 +38,7 @@
 // bf16 hi + lo (hi by truncation, lo = bf16(v - hi), exact residual) and three
 // MFMAs (hi*hi + hi*lo + lo*hi) keep about 16 significant bits per product,
 // which holds the bound at any K.
+#include <algorithm>
 #include <type_traits>
 
 #include "tq_internal.hpp"
@@ -335,25 +336,38 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 }
 
 // ---------------------------------------------------------------------------
-// M <= 16 with bf16 activations and K <= 4096: one persistent 1024-thread
-// workgroup per CU, shaped like the fused GEMV.  The sixteen wavefronts split
-// K (wavefront w takes groups w and w + 16 of four blocks) and keep
-// their activation operands in registers for the whole launch; the
-// workgroup walks 16-row weight tiles (tiles g, g + G, ...) with the next
-// two tiles' weights in flight while the current one is decoded and multiplied;
-// the sixteen partial 16 x 16 tiles are summed through a double-buffered LDS
-// area, one barrier per tile.  The pair table is filled once per launch.
+// Persistent small-batch kernel, bf16 activations, M <= 64: one 1024-thread
+// workgroup per CU, shaped like the fused GEMV.  K is covered in passes of
+// 16 * NQ groups of four blocks (NQ * 2048 elements): in a pass, wavefront w
+// takes groups w, w + 16, ... of the pass and keeps their activation
+// operands (MT tiles of 16 rows) in registers while the workgroup walks its
+// 16-row weight tiles (tiles g, g + G, ...) with the next tile's weights in
+// flight.  The sixteen partial 16 x 16 MT tiles of a weight tile wait in an
+// LDS ring (64 KiB) that all 1024 threads reduce, in wavefront order, every
+// few tiles.  With more than one pass the sums of the earlier passes wait in
+// an LDS accumulator (32 KiB, one float per output of the workgroup; the
+// host splits taller launches) and Y is written once, by the last pass: a
+// global read of Y in the loop would also wait for the weight prefetch,
+// since vector loads complete in issue order.  The activation operands are requested before
+// the pair table is filled and the weights after it: a workgroup that issued
+// everything at once (a few hundred KiB per CU) stalled its wavefronts on
+// load issue for several microseconds before computing anything.
 // ---------------------------------------------------------------------------
 constexpr int kWide = 16;
+constexpr int kRingBytes = 65536;
+constexpr int kAccFloats = 8192;      // outputs of one workgroup that the pass accumulator holds
 
-template <int NQ>
-__global__ __launch_bounds__(64 * kWide) void gemm16_kernel(const uint4* __restrict__ packed,
-                                                           const uint32_t* __restrict__ scales, uint32_t N,
-                                                           uint32_t nb, const uint8_t* __restrict__ X, int64_t ldx,
-                                                           uint32_t M, float* __restrict__ Y, int64_t ldy, uint32_t G,
-                                                           uint32_t tq, uint32_t tr) {
+template <int MT, int NQ>
+__global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __restrict__ packed,
+                                                                const uint32_t* __restrict__ scales, uint32_t N,
+                                                                uint32_t nb, const uint8_t* __restrict__ X,
+                                                                int64_t ldx, uint32_t M, float* __restrict__ Y,
+                                                                int64_t ldy, uint32_t G, uint32_t tq, uint32_t tr) {
+  constexpr int kRing = kRingBytes / (kWide * 64 * 16 * MT);        // weight tiles per ring
+  static_assert(kRing * 256 * MT == 64 * kWide, "one output per thread per flush");
   __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  __shared__ f32x4 part[2][kWide][64];
+  __shared__ f32x4 ring[kRing][kWide][MT][64];
+  __shared__ float accum[kAccFloats];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -361,113 +375,162 @@ __global__ __launch_bounds__(64 * kWide) void gemm16_kernel(const uint4* __restr
   const uint32_t g = (uint32_t)(lane >> 4);
   const uint32_t laneoff = (uint32_t)(lane & (kCopies - 1)) * 8u;
   const uint32_t ngroups = (nb + 3u) / 4u;
+  constexpr uint32_t kPassGroups = (uint32_t)(kWide * NQ);
+  const uint32_t passes = (ngroups + kPassGroups - 1u) / kPassGroups;
 
-  // Activation operands of this wavefront's groups, loaded once.
-  AOperand<false> A[NQ][4];
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    const uint32_t q = (uint32_t)wave + (uint32_t)(kWide * j);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t b = 4u * q + (uint32_t)s;
-      A[j][s].load(X, ldx, (uint32_t)nl, M, 32u * min(b, nb - 1u) + 8u * g, b < nb);
-    }
-  }
+  const uint32_t t0 = blockIdx.x;
+  const uint32_t n = tq + (t0 < tr ? 1u : 0u);          // this workgroup's tiles
+  const uint32_t last = t0 + (n - 1u) * G;
 
-  // Weight register sets: block 4 q + g of the lane's row for each group, and its scale pair.
+  // Activation operands, loaded unconditionally from clamped addresses: a
+  // row m >= M (it repeats row M - 1) only feeds output rows that are not
+  // written, and a step past the last block is skipped.
+  uint4 A[NQ][4][MT];
   struct WSet {
     uint4 p[NQ];
     uint32_t sc[NQ];
   };
-  auto load_w = [&](WSet& w, uint32_t tile) {
+  // Group j of this wavefront in pass `pass`, block 4 q + g of the lane's
+  // row (clamped: a group past the last one is skipped at compute time).
+  auto group_of = [&](uint32_t pass, int j) { return pass * kPassGroups + (uint32_t)wave + (uint32_t)(kWide * j); };
+  // The scheduling barriers keep each register set's loads together, and a
+  // workgroup barrier separates the two sets before the tile loop (the
+  // compiler interleaved them otherwise), so every path into the loop
+  // carries the same load order and the wait for a set never covers the set
+  // loaded after it.
+  auto load_w = [&](WSet& w, uint32_t tile, uint32_t pass) {
     const uint32_t row = min(tile * 16u + (uint32_t)nl, N - 1u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const uint32_t b = min(4u * ((uint32_t)wave + (uint32_t)(kWide * j)) + g, nb - 1u);
+      const uint32_t b = min(4u * group_of(pass, j) + g, nb - 1u);
       w.p[j] = packed[(size_t)row * nb + b];
       w.sc[j] = scales[(size_t)row * nb + b];
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-
-  uint32_t t = blockIdx.x;
-  const uint32_t n = tq + (t < tr ? 1u : 0u);
-  const uint32_t last = t + (n - 1u) * G;
-  WSet pa, pb, pc;
-  load_w(pa, t);
-  load_w(pb, min(t + G, last));
-  load_w(pc, min(t + 2 * G, last));
-  fill_pair_lut(lut, tid, 64 * kWide);
-  __syncthreads();
-
-  uint32_t parity = 0;
-  // Tile tt from register set w; w is refilled with tile `next` as soon as
-  // its registers are consumed, before the cross-wavefront reduction.
-  auto do_tile = [&](uint32_t tt, WSet& w, uint32_t next) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_a = [&](uint32_t pass) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const uint32_t q = (uint32_t)wave + (uint32_t)(kWide * j);
-      if (q < ngroups) {                       // wavefront-uniform
-        uint32_t wt[4], sct[4];
-        transpose_groups(w.p[j], wt);
-        transpose_groups(make_uint4(w.sc[j], w.sc[j], w.sc[j], w.sc[j]), sct);
-        const uint32_t nsteps = min(4u, nb - 4u * q);
+      const uint32_t q = group_of(pass, j);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if ((uint32_t)s < nsteps) {
-            const float d = f16_bits_to_f32(g < 2u ? (sct[s] & 0xffffu) : (sct[s] >> 16));
-            float v[8];
-            dequant8(wt[s], d, lut, laneoff, v);
-            const bf16x8 B = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                                       pack_bf16x2(v[6], v[7]));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[j][s].value()), B, acc, 0, 0, 0);
-          }
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t b = 4u * q + (uint32_t)s;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint32_t m = min(mt * 16u + (uint32_t)nl, M - 1u);
+          A[j][s][mt] = *reinterpret_cast<const uint4*>(X + ((size_t)m * ldx + 32u * min(b, nb - 1u) + 8u * g) * 2);
         }
       }
     }
-    load_w(w, next);
-    part[parity][wave][lane] = acc;
-    __syncthreads();
-    if (tid < 256) {                           // output (m, row) of partial lane l = tid / 4, register r = tid % 4
-      const int l = tid >> 2, r = tid & 3;
-      float sum = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kWide; ++w2) sum += part[parity][w2][l][r];
-      const uint32_t m = 4u * (uint32_t)(l >> 4) + (uint32_t)r;
-      const uint32_t row = tt * 16u + (uint32_t)(l & 15);
-      if (m < M && row < N) Y[(size_t)m * ldy + row] = sum;
-    }
-    parity ^= 1u;
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Fixed trip count with clamped, unconditional prefetches (exact waits),
-  // as in the fused GEMV.
-  uint32_t i = 0;
-  for (; i + 3 <= n; i += 3) {
-    do_tile(t, pa, min(t + 3 * G, last));
-    t += G;
-    do_tile(t, pb, min(t + 3 * G, last));
-    t += G;
-    do_tile(t, pc, min(t + 3 * G, last));
-    t += G;
+  // Reduce `cnt` ring entries (tiles first .. first + cnt - 1 of this
+  // workgroup's list): thread t owns output (slot t / (256 MT), m tile,
+  // lane l, register r) and adds the sixteen wavefront parts in order.
+  auto flush = [&](uint32_t first, uint32_t cnt, uint32_t pass) {
+    __syncthreads();
+    const uint32_t slot = (uint32_t)tid / (256u * MT);
+    const uint32_t o = (uint32_t)tid % (256u * MT);
+    const int mt = (int)(o / 256u), l = (int)((o % 256u) >> 2), r = (int)(o & 3u);
+    if (slot < cnt) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kWide; ++w2) sum += ring[slot][w2][mt][l][r];
+      float* const acc = accum + (first + slot) * (256u * MT) + o;   // passes > 1 only
+      if (pass > 0) sum = *acc + sum;
+      if (pass + 1 < passes) {
+        *acc = sum;
+      } else {
+        const uint32_t tt = t0 + (first + slot) * G;
+        const uint32_t row = tt * 16u + (uint32_t)(l & 15);
+        const uint32_t m = (uint32_t)mt * 16u + 4u * (uint32_t)(l >> 4) + (uint32_t)r;
+        if (m < M && row < N) Y[(size_t)m * ldy + row] = sum;
+      }
+    }
+    __syncthreads();                        // the ring is rewritten next
+  };
+
+  WSet pa, pb;
+  for (uint32_t pass = 0; pass < passes; ++pass) {
+    // The pass's activation operands and first weights, in the same order
+    // on every pass (the table is filled while the first pass's are in flight).
+    load_a(pass);
+    load_w(pa, t0, pass);
+    if (pass == 0) fill_pair_lut(lut, tid, 64 * kWide);
+    __syncthreads();
+    load_w(pb, min(t0 + G, last), pass);
+
+    uint32_t ti = 0;                        // tiles of this pass done
+    // Tile tt from register set w; w is refilled with tile `next` as soon
+    // as its registers are consumed (not for the last tile of the pass).
+    auto do_tile = [&](WSet& w, uint32_t next, auto reload) {
+      f32x4 acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const uint32_t q = group_of(pass, j);
+        if (q < ngroups) {                   // wavefront-uniform
+          uint32_t wt[4], sct[4];
+          transpose_groups(w.p[j], wt);
+          transpose_groups(make_uint4(w.sc[j], w.sc[j], w.sc[j], w.sc[j]), sct);
+          const uint32_t nsteps = min(4u, nb - 4u * q);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            if ((uint32_t)s < nsteps) {
+              const float d = f16_bits_to_f32(g < 2u ? (sct[s] & 0xffffu) : (sct[s] >> 16));
+              float v[8];
+              dequant8(wt[s], d, lut, laneoff, v);
+              const bf16x8 B = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[j][s][mt]), B,
+                                                                  acc[mt], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if constexpr (decltype(reload)::value) load_w(w, next, pass);
+      const uint32_t slot = ti % (uint32_t)kRing;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ring[slot][wave][mt][lane] = acc[mt];
+      ++ti;
+      if (ti % (uint32_t)kRing == 0u) flush(ti - (uint32_t)kRing, (uint32_t)kRing, pass);
+    };
+    // Fixed trip count with clamped, unconditional prefetches (exact waits).
+    uint32_t t = t0;
+    uint32_t i = 0;
+    for (; i + 2 <= n; i += 2) {
+      do_tile(pa, min(t + 2 * G, last), std::true_type{});
+      t += G;
+      do_tile(pb, min(t + 2 * G, last), std::true_type{});
+      t += G;
+    }
+    if (i < n) do_tile(pa, last, std::false_type{});
+    if (ti % (uint32_t)kRing != 0u) flush(ti - ti % (uint32_t)kRing, ti % (uint32_t)kRing, pass);
   }
-  if (i < n) do_tile(t, pa, last);
-  if (i + 1 < n) do_tile(t + G, pb, last);
 }
 
-void launch_gemm16(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
-                   uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
-  const uint32_t tiles = (N + 15u) / 16u;
+template <int MT, int NQ>
+void launch_small(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
+                  uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
   const uint32_t cap = (uint32_t)device_cu_count();
-  const uint32_t per_wg = (tiles + cap - 1u) / cap;
-  const uint32_t grid = (tiles + per_wg - 1u) / per_wg;
-  const uint32_t nq = ((nb + 3u) / 4u + kWide - 1u) / kWide;
-#define TQ_GEMM16(NQ_)                                                                                       \
-  hipLaunchKernelGGL((gemm16_kernel<NQ_>), dim3(grid), dim3(64 * kWide), 0, s, pk, sc, N, nb, X, ldx, M, Y, ldy, \
-                     grid, tiles / grid, tiles % grid)
-  if (nq <= 1) TQ_GEMM16(1);
-  else TQ_GEMM16(2);
-#undef TQ_GEMM16
+  const uint32_t passes = ((nb + 3u) / 4u + kWide * NQ - 1u) / (kWide * NQ);
+  // With several passes a workgroup's outputs (16 * 16 * MT per tile) must
+  // fit the pass accumulator: taller matrices are launched in row chunks.
+  const uint64_t max_tiles = passes > 1 ? (uint64_t)(kAccFloats / (256 * MT)) * cap : ~0ull;
+  for (uint64_t r0 = 0; r0 < N; r0 += 16u * max_tiles) {
+    const uint32_t Nc = (uint32_t)std::min<uint64_t>(N - r0, 16u * max_tiles);
+    const uint32_t tiles = (Nc + 15u) / 16u;
+    const uint32_t per_wg = (tiles + cap - 1u) / cap;
+    const uint32_t grid = (tiles + per_wg - 1u) / per_wg;
+    hipLaunchKernelGGL((gemm_small_kernel<MT, NQ>), dim3(grid), dim3(64 * kWide), 0, s, pk + r0 * nb, sc + r0 * nb,
+                       Nc, nb, X, ldx, M, Y + r0, ldy, grid, tiles / grid, tiles % grid);
+  }
 }
 
 // Weight groups in flight per wavefront: three where the registers allow.
@@ -507,9 +570,11 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
   const uint8_t* X = static_cast<const uint8_t*>(xr);
   const int64_t xs = xbf16 ? 2 : 4;
-  // Float32 activations take three MFMAs per product and twice the operand
-  // registers: at most 32 activation rows per pass.
-  const int64_t chunk = xbf16 ? 64 : 32;
+  // At most 32 activation rows per launch: the persistent bf16 kernel keeps
+  // its operands in registers (two 16-row tiles fit beside the weight
+  // prefetch), and float32 activations take three MFMAs per product and
+  // twice the operand registers.
+  const int64_t chunk = 32;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {
     const int64_t mc = (M - m0 < chunk) ? M - m0 : chunk;
     const uint8_t* Xm = X + m0 * ldx * xs;
@@ -517,16 +582,8 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
     const int mt = (int)((mc + 15) / 16);
     const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
-      if (mt == 1 && nb <= 4u * kWide * 2u) {   // K <= 4096: the persistent one-tile-of-M kernel
-        launch_gemm16(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
-        continue;
-      }
-      switch (mt) {
-        case 1: launch_mt<1, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
-        case 2: launch_mt<2, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
-        case 3: launch_mt<3, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
-        default: launch_mt<4, false>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s); break;
-      }
+      if (mt == 1) launch_small<1, 2>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);   // the persistent kernel
+      else launch_small<2, 1>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
     } else {
       if (mt == 1) launch_mt<1, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
       else launch_mt<2, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
