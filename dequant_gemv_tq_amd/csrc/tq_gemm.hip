@@ -365,9 +365,13 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
                                                                 int64_t ldy, uint32_t G, uint32_t tq, uint32_t tr) {
   constexpr int kRing = kRingBytes / (kWide * 64 * 16 * MT);        // weight tiles per ring
   static_assert(kRing * 256 * MT == 64 * kWide, "one output per thread per flush");
-  __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
-  __shared__ f32x4 ring[kRing][kWide][MT][64];
-  __shared__ float accum[kAccFloats];
+  // LDS: pair table | partial-tile ring | pass accumulator.  While a pass's
+  // activations are staged, the ring's space holds half of them at a time.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLutBytes + kRingBytes + kAccFloats * 4];
+  uint8_t* const lut = smem;
+  f32x4 (*const ring)[kWide][MT][64] = reinterpret_cast<f32x4 (*)[kWide][MT][64]>(smem + kLutBytes);
+  float* const accum = reinterpret_cast<float*>(smem + kLutBytes + kRingBytes);
+  uint8_t* const stage = smem + kLutBytes;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -382,10 +386,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
   const uint32_t n = tq + (t0 < tr ? 1u : 0u);          // this workgroup's tiles
   const uint32_t last = t0 + (n - 1u) * G;
 
-  // Activation operands, loaded unconditionally from clamped addresses: a
-  // row m >= M (it repeats row M - 1) only feeds output rows that are not
-  // written, and a step past the last block is skipped.
-  uint4 A[NQ][4][MT];
+  uint4 A[NQ][4][MT];                      // this wavefront's activation operands of the pass
   struct WSet {
     uint4 p[NQ];
     uint32_t sc[NQ];
@@ -409,22 +410,58 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto load_a = [&](uint32_t pass) {
-    __builtin_amdgcn_sched_barrier(0);
+  // Activation operands of a pass: 16 MT rows x (16 NQ * 128) elements of
+  // X, staged through LDS in two halves along K by direct-to-LDS loads
+  // (global_load_lds_dwordx4: no registers held, and every instruction
+  // moves 1 KiB of one row, coalesced).  Piece c of row r is stored at
+  // chunk c ^ (r % 16), so that the operand reads (16 rows x four 16-byte
+  // chunks per instruction) spread over the banks; a lane of a DMA
+  // instruction writes the LDS chunk at its own position, so it reads the
+  // global piece that belongs there.  Rows past M repeat row M - 1 and
+  // elements past K are clamped: both only feed outputs that are not
+  // written or steps that are skipped.  (Loading the operands straight
+  // from X in the MFMA layout, 16 rows x 64 bytes per instruction, took
+  // about twice as long.)
+  constexpr uint32_t kPassK = 16u * NQ * 128u;               // elements of K per pass
+  constexpr uint32_t kHalfK = kPassK / 2u;
+  constexpr uint32_t kRowBytes = kHalfK * 2u;                // bytes of one staged row
+  constexpr int kDma = (int)(16u * MT * kRowBytes) / (1024 * kWide);   // 1 KiB DMA instructions per wavefront
+  static_assert(16u * MT * kRowBytes <= (uint32_t)kRingBytes && kRowBytes % 1024u == 0u, "staging layout");
+  const uint32_t K = nb * 32u;
+  auto dma_x = [&](uint32_t pass, uint32_t h) {
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+      const uint32_t base = 1024u * (uint32_t)(i * kWide + wave);          // wavefront-uniform LDS offset
+      const uint32_t off = base + 16u * (uint32_t)lane;
+      const uint32_t r = off / kRowBytes, c = ((off % kRowBytes) / 16u) ^ (r & 15u);
+      const uint32_t m = min(r, M - 1u);
+      const uint32_t k = min(pass * kPassK + h * kHalfK + 8u * c, K - 8u);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(X + ((size_t)m * ldx + k) * 2),
+                                       (__attribute__((address_space(3))) void*)(stage + base), 16, 0, 0);
+    }
+  };
+  // Wait for this wavefront's LDS reads, then for the workgroup.
+  auto lds_done_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+  };
+  // The operands of half h: (j, s) of this wavefront whose 32 elements lie in it.
+  auto read_ops = [&](uint32_t h) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const uint32_t q = group_of(pass, j);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t b = 4u * q + (uint32_t)s;
+        const uint32_t kl = 128u * ((uint32_t)wave + (uint32_t)(kWide * j)) + 32u * (uint32_t)s;   // wavefront-uniform
+        if (kl / kHalfK == h) {
+          const uint32_t c = (kl - h * kHalfK + 8u * g) / 8u;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const uint32_t m = min(mt * 16u + (uint32_t)nl, M - 1u);
-          A[j][s][mt] = *reinterpret_cast<const uint4*>(X + ((size_t)m * ldx + 32u * min(b, nb - 1u) + 8u * g) * 2);
+          for (int mt = 0; mt < MT; ++mt) {
+            const uint32_t r = (uint32_t)(16 * mt + nl);
+            A[j][s][mt] = *reinterpret_cast<const uint4*>(stage + r * kRowBytes + 16u * (c ^ (r & 15u)));
+          }
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Reduce `cnt` ring entries (tiles first .. first + cnt - 1 of this
@@ -455,13 +492,26 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
 
   WSet pa, pb;
   for (uint32_t pass = 0; pass < passes; ++pass) {
-    // The pass's activation operands and first weights, in the same order
-    // on every pass (the table is filled while the first pass's are in flight).
-    load_a(pass);
+    // The pass's activations and first weights, in the same order on every
+    // pass (the table is filled while the first pass's are in flight); the
+    // waits for the activations leave the weights in flight.
+    // (The table is filled before the first DMA is issued: the compiler makes
+    // LDS stores wait for any DMA into LDS still in flight.)
     load_w(pa, t0, pass);
     if (pass == 0) fill_pair_lut(lut, tid, 64 * kWide);
-    __syncthreads();
+    dma_x(pass, 0);
+    __syncthreads();                        // first half staged (and the table filled)
+    read_ops(0);
+    lds_done_barrier();                     // every wavefront has its first-half operands
+    dma_x(pass, 1);
     load_w(pb, min(t0 + G, last), pass);
+    // Second half staged: wait for this wavefront's DMA, issued just
+    // before the 2 NQ loads of pb (vector loads complete in order), so
+    // pb stays in flight; then for the workgroup.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NQ));
+    __builtin_amdgcn_s_barrier();
+    read_ops(1);
+    lds_done_barrier();                     // the ring's space is the ring again
 
     uint32_t ti = 0;                        // tiles of this pass done
     // Tile tt from register set w; w is refilled with tile `next` as soon
