@@ -411,7 +411,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
     __builtin_amdgcn_sched_barrier(0);
   };
   // Activation operands of a pass: 16 MT rows x (16 NQ * 128) elements of
-  // X, staged through LDS in two halves along K by direct-to-LDS loads
+  // X, staged through LDS one 64 KiB part along K at a time by direct-to-LDS loads
   // (global_load_lds_dwordx4: no registers held, and every instruction
   // moves 1 KiB of one row, coalesced).  Piece c of row r is stored at
   // chunk c ^ (r % 16), so that the operand reads (16 rows x four 16-byte
@@ -423,10 +423,12 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
   // from X in the MFMA layout, 16 rows x 64 bytes per instruction, took
   // about twice as long.)
   constexpr uint32_t kPassK = 16u * NQ * 128u;               // elements of K per pass
-  constexpr uint32_t kHalfK = kPassK / 2u;
-  constexpr uint32_t kRowBytes = kHalfK * 2u;                // bytes of one staged row
+  constexpr int kParts = (int)(16u * MT * kPassK * 2u) / kRingBytes;   // staged one ring-full at a time
+  constexpr uint32_t kPartK = kPassK / (uint32_t)kParts;
+  constexpr uint32_t kRowBytes = kPartK * 2u;                // bytes of one staged row
   constexpr int kDma = (int)(16u * MT * kRowBytes) / (1024 * kWide);   // 1 KiB DMA instructions per wavefront
-  static_assert(16u * MT * kRowBytes <= (uint32_t)kRingBytes && kRowBytes % 1024u == 0u, "staging layout");
+  static_assert(kParts >= 2 && 16u * MT * kRowBytes == (uint32_t)kRingBytes && kRowBytes % 1024u == 0u,
+                "staging layout");
   const uint32_t K = nb * 32u;
   auto dma_x = [&](uint32_t pass, uint32_t h) {
 #pragma unroll
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
       const uint32_t off = base + 16u * (uint32_t)lane;
       const uint32_t r = off / kRowBytes, c = ((off % kRowBytes) / 16u) ^ (r & 15u);
       const uint32_t m = min(r, M - 1u);
-      const uint32_t k = min(pass * kPassK + h * kHalfK + 8u * c, K - 8u);
+      const uint32_t k = min(pass * kPassK + h * kPartK + 8u * c, K - 8u);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(X + ((size_t)m * ldx + k) * 2),
                                        (__attribute__((address_space(3))) void*)(stage + base), 16, 0, 0);
     }
@@ -445,15 +447,15 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
     __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt left alone
     __builtin_amdgcn_s_barrier();
   };
-  // The operands of half h: (j, s) of this wavefront whose 32 elements lie in it.
+  // The operands of part h: (j, s) of this wavefront whose 32 elements lie in it.
   auto read_ops = [&](uint32_t h) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint32_t kl = 128u * ((uint32_t)wave + (uint32_t)(kWide * j)) + 32u * (uint32_t)s;   // wavefront-uniform
-        if (kl / kHalfK == h) {
-          const uint32_t c = (kl - h * kHalfK + 8u * g) / 8u;
+        if (kl / kPartK == h) {
+          const uint32_t c = (kl - h * kPartK + 8u * g) / 8u;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const uint32_t r = (uint32_t)(16 * mt + nl);
@@ -500,18 +502,25 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
     load_w(pa, t0, pass);
     if (pass == 0) fill_pair_lut(lut, tid, 64 * kWide);
     dma_x(pass, 0);
-    __syncthreads();                        // first half staged (and the table filled)
+    __syncthreads();                        // first part staged (and the table filled)
     read_ops(0);
-    lds_done_barrier();                     // every wavefront has its first-half operands
-    dma_x(pass, 1);
-    load_w(pb, min(t0 + G, last), pass);
-    // Second half staged: wait for this wavefront's DMA, issued just
-    // before the 2 NQ loads of pb (vector loads complete in order), so
-    // pb stays in flight; then for the workgroup.
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NQ));
-    __builtin_amdgcn_s_barrier();
-    read_ops(1);
-    lds_done_barrier();                     // the ring's space is the ring again
+    lds_done_barrier();                     // every wavefront has its first-part operands
+    static_for<kParts - 1>([&](auto pc) {
+      constexpr int part = decltype(pc)::value + 1;
+      dma_x(pass, (uint32_t)part);
+      if constexpr (part == 1) {
+        load_w(pb, min(t0 + G, last), pass);
+        // Wait for this wavefront's DMA, issued just before the 2 NQ
+        // loads of pb (vector loads complete in order), so pb stays in
+        // flight; then for the workgroup.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NQ));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      __builtin_amdgcn_s_barrier();
+      read_ops((uint32_t)part);
+      lds_done_barrier();                   // the ring's space is free again
+    });
 
     uint32_t ti = 0;                        // tiles of this pass done
     // Tile tt from register set w; w is refilled with tile `next` as soon
@@ -624,7 +633,7 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
   // its operands in registers (two 16-row tiles fit beside the weight
   // prefetch), and float32 activations take three MFMAs per product and
   // twice the operand registers.
-  const int64_t chunk = 32;
+  const int64_t chunk = xbf16 ? 64 : 32;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {
     const int64_t mc = (M - m0 < chunk) ? M - m0 : chunk;
     const uint8_t* Xm = X + m0 * ldx * xs;
@@ -633,7 +642,8 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
     const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
       if (mt == 1) launch_small<1, 2>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);   // the persistent kernel
-      else launch_small<2, 1>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
+      else if (mt == 2) launch_small<2, 1>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
+      else launch_small<4, 1>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
     } else {
       if (mt == 1) launch_mt<1, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
       else launch_mt<2, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
