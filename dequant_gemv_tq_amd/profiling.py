@@ -7,6 +7,11 @@ HBM traffic, from the repository root:
     python3 -m dequant_gemv_tq_amd.profiling summarize OUT/fetch/fetch_results.db OUT/write/write_results.db \\
         > profiles/gemv_traffic_llama8b.md
 
+MFMA utilisation of the small-batch GEMM:
+
+    rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d OUT/mfma -o mfma -- python3 -m dequant_gemv_tq_amd.profiling gemm_run
+    python3 -m dequant_gemv_tq_amd.profiling gemm_summarize OUT/mfma/mfma_results.db > profiles/...md
+
 Kernel durations of a benchmark run:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- \\
@@ -85,6 +90,73 @@ def run() -> None:
         del reps, p, s
         torch.cuda.empty_cache()
     print("traffic run done", flush=True)
+
+
+GEMM_BATCHES = (16, 32, 64)
+
+
+def gemm_run() -> None:
+    """Small-batch GEMM over one Llama-3-8B layer's groups at M = 16, 32, 64 (bf16 pre-rotated activations),
+    COPIES launches per group and batch, for the MFMA counters."""
+    sys.path.insert(0, ROOT)
+    import torch
+    import dequant_gemv_tq_amd as tqa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    for gname, (n, k) in GROUPS.items():
+        W = torch.cat([wl.llama8b_weight(t, 0, dev) for t in MEMBERS[gname]], dim=0)
+        p, s = tqa.quantize(W)
+        del W
+        for m in GEMM_BATCHES:
+            X = tqa.rotate(wl.activation(m, k, wl.generator(wl.seed_of(3, m, 0), dev), dev, torch.bfloat16),
+                           dtype=torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            for _ in range(COPIES):
+                tqa.gemm(p, s, X, out=y)
+            torch.cuda.synchronize()
+    print("gemm counter run done", flush=True)
+
+
+def gemm_summarize(db: str) -> None:
+    """MFMA utilisation and bf16 MFMA flops per GEMM dispatch from a --pmc MfmaUtil MfmaFlopsBF16 run."""
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select dispatch_id, kernel_name, counter_name, sum(value) from counters_collection "
+        "where counter_name in ('MfmaUtil', 'MfmaFlopsBF16') group by dispatch_id, kernel_name, counter_name "
+        "order by dispatch_id").fetchall()
+    con.close()
+    per = {}
+    for d, name, cname, v in rows:
+        if "gemm_small_kernel" not in name:
+            continue
+        per.setdefault(d, {"name": name})[cname] = v
+    disp = [per[d] for d in sorted(per)]
+    expect = len(GROUPS) * len(GEMM_BATCHES) * COPIES
+    if len(disp) != expect:
+        raise RuntimeError(f"expected {expect} GEMM dispatches, found {len(disp)}")
+    lines = ["# Small-batch GEMM: MFMA utilisation (Llama-3-8B groups, bf16 pre-rotated activations)", "",
+             "Commands (repository root on the GPU host; OUT is any scratch folder):", "", "```",
+             "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d OUT/mfma -o mfma -- python3 -m dequant_gemv_tq_amd.profiling "
+             "gemm_run",
+             "python3 -m dequant_gemv_tq_amd.profiling gemm_summarize OUT/mfma/mfma_results.db", "```", "",
+             "MfmaUtil is rocprofv3's derived counter (MFMA busy cycles over GPU-active cycles times SIMD count, "
+             "in %); MfmaFlopsBF16 counts the bf16 MFMA work issued, against 2 * 16 * ceil(M / 16) * N * K for "
+             "the padded activation tiles.", "",
+             "| group | N x K | M | kernel | MFMA busy % | bf16 MFMA GFLOP per launch | padded 2*M*N*K GFLOP |",
+             "|---|---|---|---|---|---|---|"]
+    i = 0
+    for gname, (n, k) in GROUPS.items():
+        for m in GEMM_BATCHES:
+            chunk = disp[i:i + COPIES]
+            i += COPIES
+            util = statistics.median(c.get("MfmaUtil", 0.0) for c in chunk)
+            fl = statistics.median(c.get("MfmaFlopsBF16", 0.0) for c in chunk)
+            import re
+            kn = re.search(r"gemm_small_kernel<[^>]*>", chunk[0]["name"])
+            lines.append(f"| {gname} | {n} x {k} | {m} | `{kn.group(0) if kn else chunk[0]['name']}` | {util:.1f} | "
+                         f"{fl / 1e9:.3f} | {2 * 16 * ((m + 15) // 16) * n * k / 1e9:.3f} |")
+    print("\n".join(lines + [""]))
 
 
 def _per_dispatch(db: str, counter: str):
@@ -181,10 +253,11 @@ def stats(csv_path: str) -> None:
               "q|k|v and gate|up (K = 4096, bf16 activation, rotation fused, one row per wavefront) run "
               f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 2, 1>`; down "
               "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 4>`.  "
-              "Other kernels: the quantizer, the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M < 16, "
-              "`gemm_mfma_kernel` for M >= 16), dequantization and the NVFP4 / MXFP6 rows (`gemv_kernel<FmtNVFP4"
-              ", ...>`, `gemv_kernel<FmtMXFP6, ...>`); the remaining GPU time is PyTorch drawing the synthetic "
-              "weights.", ""]
+              "Other kernels: the quantizer, the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M < 16; "
+              "for M >= 16 the persistent MFMA `gemm_small_kernel<MT, NQ>` with bf16 activations, MT = 1, 2, 4 "
+              "tiles of 16 activation rows, and `gemm_mfma_kernel` with float32 activations), dequantization "
+              "and the NVFP4 / MXFP6 rows (`gemv_kernel<FmtNVFP4, ...>`, `gemv_kernel<FmtMXFP6, ...>`); the "
+              "remaining GPU time is PyTorch drawing the synthetic weights.", ""]
     print("\n".join(lines))
 
 
@@ -208,6 +281,10 @@ if __name__ == "__main__":
         summarize(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 3 and sys.argv[1] == "stats":
         stats(sys.argv[2])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "gemm_run":
+        gemm_run()
+    elif len(sys.argv) == 3 and sys.argv[1] == "gemm_summarize":
+        gemm_summarize(sys.argv[2])
     else:
         print(__doc__)
         sys.exit(2)
