@@ -11,6 +11,7 @@ divided by the step time, with every input already resident in HBM.
 
 The same run also measures, outside the timed step: the quantizer over the
 whole model, the small-batch GEMM at M in {1, 4, 16, 32, 64}, dequantization,
+the load-time int8 transcode of the model and its int8 decode step,
 and NVFP4 / MXFP6 quantize + GEMV on 27B-shaped layers (a few layers by
 default, all 64 plus the 70B quantize with --extended).  ``roofline``
 reports the fused GEMV kernel alone (per-launch HIP event pairs on the
@@ -225,6 +226,7 @@ def main():
     # ----------------------------------------------------- secondary rows
     out["gemm"] = bench_gemm(torch, tqa, wl, model, groups, dev, stream)
     out["dequantize"] = bench_dequant(torch, tqa, model, groups, dev, stream)
+    out["q8_transcode"] = bench_q8(torch, tqa, model, xs, groups, dev, stream, ms_per_step, args.no_graph)
     out["blockfp"] = bench_blockfp(torch, tqa, wl, dev, stream, layers=64 if args.extended else 4)
     if args.extended:
         del model, xs
@@ -282,6 +284,53 @@ def bench_dequant(torch, tqa, model, groups, dev, stream):
     ms = _time(torch, stream, lambda: tqa.dequantize(p, s, dtype=torch.bfloat16, out=out), 5)
     byts = (WEIGHT_BYTES_PER_ELEM + 2.0) * n * k
     return {"shape": [n, k], "out": "bf16", "us": round(ms * 1e3, 1), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1)}
+
+
+def bench_q8(torch, tqa, model, xs, groups, dev, stream, tq4_ms, no_graph):
+    """Load-time TQ4_1S -> int8 transcode of the 32-layer model, then the int8 decode step (same launches
+    and activations as the TQ4_1S step: one q8 GEMV per group and layer, captured in a graph)."""
+    L = len(model)
+    q_ms, q_weights = 0.0, 0
+    q8 = []
+    for layer in range(L):
+        entry = {}
+        for gname, (n, k) in groups.items():
+            p, s = model[layer][gname]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            entry[gname] = tqa.transcode_q8(p, s)
+            b.record(stream)
+            b.synchronize()
+            q_ms += a.elapsed_time(b)
+            q_weights += n * k
+        q8.append(entry)
+    ys = {gname: torch.empty(n, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
+
+    def step():
+        for layer in range(L):
+            for gname in groups:
+                c, qs = q8[layer][gname]
+                tqa.q8_gemv(c, qs, xs[layer][gname], out=ys[gname])
+
+    if no_graph:
+        ms = _time(torch, stream, step, 5)
+    else:
+        step()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        ms = _time(torch, stream, gr.replay, 10)
+        del gr
+    byts = sum(L * (1.0625 * n * k + 2 * k + 4 * n) for n, k in groups.values())
+    res = {"transcode_GB_s": round((WEIGHT_BYTES_PER_ELEM + 1.0625) * q_weights / (q_ms * 1e-3) / 1e9, 1),
+           "transcode_ms_total": round(q_ms, 3), "bytes_per_weight": 1.0625,
+           "gemv_step_ms": round(ms, 4), "gemv_GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
+           "gemv_step_time_vs_tq4": round(ms / tq4_ms, 3),
+           "note": "int8 codes + fp16 block scales; activation quantized to int8 per block inside the GEMV"}
+    del q8
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_blockfp(torch, tqa, wl, dev, stream, layers):

@@ -7,7 +7,7 @@ stream to the C ABI.  There is no CPU fallback: if the library is not built
 or a tensor is not on the GPU, the call raises.
 
 The names follow the C ABI: quantize, dequantize, rotate, gemv, gemm,
-blockfp_quantize, blockfp_gemm, codebook, sign_mask_from_seed.
+blockfp_quantize, blockfp_gemm, transcode_q8, q8_gemv, codebook, sign_mask_from_seed.
 """
 
 from __future__ import annotations
@@ -20,7 +20,7 @@ import torch  # imported before libtq so both bind to the same HIP runtime
 __all__ = [
     "TQError", "lib", "codebook", "sign_mask_from_seed", "DEFAULT_SIGN_MASK",
     "quantize", "dequantize", "rotate", "gemv", "gemm",
-    "blockfp_quantize", "blockfp_gemm", "LIB_PATH",
+    "blockfp_quantize", "blockfp_gemm", "transcode_q8", "q8_gemv", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
@@ -32,7 +32,7 @@ _STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EALIGN", 4: "TQ_ED
 EXPORTED = [
     "tq_abi_version", "tq_status_str", "tq_codebook", "tq_sign_mask_from_seed", "tq_default_sign_mask",
     "tq_quantize", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
-    "tq_blockfp_quantize", "tq_blockfp_gemm",
+    "tq_blockfp_quantize", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
 ]
 
 
@@ -69,8 +69,10 @@ def lib() -> ctypes.CDLL:
     L.tq_gemm.argtypes = [p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
     L.tq_blockfp_quantize.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p]
     L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
+    L.tq_transcode_q8.argtypes = [p, p, i64, i64, u32, p, p, p]
+    L.tq_q8_gemv.argtypes = [p, p, i64, i64, p, c_int, p, p]
     for name in ("tq_quantize", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
-                 "tq_blockfp_quantize", "tq_blockfp_gemm"):
+                 "tq_blockfp_quantize", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -243,3 +245,35 @@ def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tens
                                _dtype_code(x2, "x"), x2.stride(0), _ptr(y), y.stride(0), _stream())
     _check("tq_blockfp_gemm", st)
     return y if x.dim() == 2 else y.reshape(-1)
+
+
+# ----------------------------------------------------------------------------
+# load-time int8 transcode
+# ----------------------------------------------------------------------------
+
+def transcode_q8(packed: torch.Tensor, scales: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None):
+    """TQ4_1S (packed, scales) -> (codes int8 [N, K], q8_scales int16 [N, K/32] = fp16 bits per block)."""
+    _dev(packed, "packed")
+    N, K = packed.shape[0], packed.shape[1] * 2
+    if out is None:
+        codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+        qs = torch.empty((N, K // 32), dtype=torch.int16, device=packed.device)
+    else:
+        codes, qs = out
+    st = lib().tq_transcode_q8(_ptr(packed), _ptr(scales), N, K, sign_mask & 0xFFFFFFFF, _ptr(codes), _ptr(qs),
+                               _stream())
+    _check("tq_transcode_q8", st)
+    return codes, qs
+
+
+def q8_gemv(codes: torch.Tensor, q8_scales: torch.Tensor, x: torch.Tensor, out=None):
+    """y [N] float32 from transcoded int8 weights and the activation x [K] (fp32/bf16, not rotated)."""
+    _dev(codes, "codes")
+    _dev(x, "x")
+    N, K = codes.shape
+    if x.numel() != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous vector of length K")
+    y = torch.empty(N, dtype=torch.float32, device=codes.device) if out is None else out
+    st = lib().tq_q8_gemv(_ptr(codes), _ptr(q8_scales), N, K, _ptr(x), _dtype_code(x, "x"), _ptr(y), _stream())
+    _check("tq_q8_gemv", st)
+    return y

@@ -132,4 +132,22 @@ tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* bloc
                                           y, ldy, stream));
 }
 
+tq_status tq_transcode_q8(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t sign_mask,
+                          int8_t* codes, uint16_t* q8_scales, hipStream_t stream) {
+  if (!codes || !q8_scales) return TQ_EINVAL;
+  if (tq_status st = check_weights(packed, scales, N, K)) return st;
+  if (!aligned(codes, 16) || !aligned(q8_scales, 2)) return TQ_EALIGN;
+  return from_hip(tq::launch_transcode_q8(packed, scales, N, K, sign_mask, codes, q8_scales, stream));
+}
+
+tq_status tq_q8_gemv(const int8_t* codes, const uint16_t* q8_scales, int64_t N, int64_t K, const void* x,
+                     tq_dtype xt, float* y, hipStream_t stream) {
+  if (!codes || !q8_scales || !x || !y || N <= 0 || K <= 0) return TQ_EINVAL;
+  if (K % tq::kBlock) return TQ_ESHAPE;
+  if (K > 32768 || N > 0x7fffffff) return TQ_ESHAPE;
+  if (!float_or_bf16(xt)) return TQ_EDTYPE;
+  if (!aligned(codes, 16) || !aligned(q8_scales, 2) || !aligned(x, 16) || !aligned(y, 4)) return TQ_EALIGN;
+  return from_hip(tq::launch_q8_gemv(codes, q8_scales, N, K, x, xt == TQ_BF16, y, stream));
+}
+
 }  // extern "C"

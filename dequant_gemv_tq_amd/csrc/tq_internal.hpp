@@ -224,6 +224,10 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
 hipError_t launch_blockfp_gemv(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
                                int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
                                hipStream_t s);
+hipError_t launch_transcode_q8(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t mask,
+                               int8_t* codes, uint16_t* qscales, hipStream_t s);
+hipError_t launch_q8_gemv(const int8_t* codes, const uint16_t* qscales, int64_t N, int64_t K, const void* x,
+                          bool xbf16, float* y, hipStream_t s);
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
                                float* y, int64_t ldy, hipStream_t s);

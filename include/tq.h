@@ -194,6 +194,32 @@ tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* bloc
                           const void* x, tq_dtype xt, int64_t ldx, float* y, int64_t ldy,
                           hipStream_t stream);
 
+/* Load-time transcode of TQ4_1S weights to int8 blocks (TQ4 page, the note
+ * under the decode-speed summary and the backend item of "适用前提与边界":
+ * converting TQ4_1S to q8_0 when the model is loaded keeps the TQ4_1S file
+ * size and decodes at the q8_0 path's speed).  Per 32-element block, in
+ * float32: q_i = d_h * c[idx_i]; u = FWHT32(q); w_i = D_i * u_i / sqrt(32);
+ * d = fp16(amax|w| / 127) (round to nearest even, saturating);
+ * codes_i = clamp(rint(w_i / d), -127, 127) (ties to even; d = 0 -> 0).
+ *   codes      [N, K] int8 row-major, 16-byte aligned (output).
+ *   q8_scales  [N, K/32] fp16 bits, one per block, 2-byte aligned (output).
+ * 1.0625 bytes per weight; the codes are bit-exact against the canonical
+ * order above.  K % 32 == 0.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN. */
+tq_status tq_transcode_q8(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
+                          uint32_t sign_mask, int8_t* codes, uint16_t* q8_scales,
+                          hipStream_t stream);
+
+/* Batch-1 GEMV on transcoded int8 weights: the activation x [K] (TQ_F32 or
+ * TQ_BF16, not rotated, 16-byte aligned) is quantized per 32-element block
+ * the same way (dx = amax|x| / 127 in float32, codes rint(x / dx)), and
+ * y_n = sum_b d[n, b] dx[b] sum_i codes[n, b, i] xq[b, i] with exact integer
+ * block sums (v_dot4_i32_i8) and float32 accumulation.
+ *   y  [N] float32, 4-byte aligned (output).
+ * K % 32 == 0, K <= 32768.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN,
+ * TQ_EDTYPE. */
+tq_status tq_q8_gemv(const int8_t* codes, const uint16_t* q8_scales, int64_t N, int64_t K,
+                     const void* x, tq_dtype xt, float* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

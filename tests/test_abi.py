@@ -108,6 +108,16 @@ def test_other_calls_reject_before_launch():
     assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None) == EDTYPE
     assert L.tq_blockfp_gemm(1, _p(GOOD + 8), g, g, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN   # NVFP4 codes: 16 B
     assert L.tq_blockfp_gemm(2, _p(GOOD + 4), g, None, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN  # MXFP6 codes: 8 B
+    # int8 transcode and GEMV
+    assert L.tq_transcode_q8(g, g, 8, 64, 0, None, g, None) == EINVAL
+    assert L.tq_transcode_q8(g, g, 8, 48, 0, g, g, None) == ESHAPE
+    assert L.tq_transcode_q8(g, g, 8, 64, 0, _p(GOOD + 8), g, None) == EALIGN      # codes: 16 B
+    assert L.tq_transcode_q8(g, g, 8, 64, 0, g, _p(GOOD + 1), None) == EALIGN      # scales: 2 B
+    assert L.tq_q8_gemv(g, g, 0, 64, g, F32, g, None) == EINVAL
+    assert L.tq_q8_gemv(g, g, 8, 40, g, F32, g, None) == ESHAPE
+    assert L.tq_q8_gemv(g, g, 8, 32768 + 32, g, F32, g, None) == ESHAPE
+    assert L.tq_q8_gemv(g, g, 8, 64, g, F16, g, None) == EDTYPE
+    assert L.tq_q8_gemv(g, g, 8, 64, _p(GOOD + 8), BF16, g, None) == EALIGN      # x: 16 B
 
 
 def test_binding_refuses_cpu_tensors():
