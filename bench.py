@@ -75,27 +75,32 @@ def main():
     L = wl.LLAMA8B_LAYERS
     model = []                                        # per layer: name -> (packed, scales)
     xs = []                                           # per layer: name -> bf16 activation
-    q_bytes = 0.0
-    q_ms = 0.0
+    # The bf16 model (14 GB) is drawn first; the quantizer then runs over all
+    # 128 tensors back to back between two events on the launch stream.
+    src = []
     for layer in range(L):
         variant = wl.layer_variant(layer)
-        entry = {}
-        for gname, (n, k) in groups.items():
-            W = torch.cat([wl.llama8b_weight(t, layer, dev, variant) for t in members[gname]], dim=0)
-            assert W.shape == (n, k)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            packed, scales = tqa.quantize(W)
-            e1.record(stream)
-            e1.synchronize()
-            q_ms += e0.elapsed_time(e1)
-            q_bytes += (2.0 + WEIGHT_BYTES_PER_ELEM) * n * k
-            entry[gname] = (packed, scales)
-            del W
-        model.append(entry)
+        src.append({gname: torch.cat([wl.llama8b_weight(t, layer, dev, variant) for t in members[gname]], dim=0)
+                    for gname in groups})
         g = wl.generator(wl.seed_of(2, layer, 50), dev)
         xs.append({gname: wl.activation(1, k, g, dev, torch.bfloat16)[0].contiguous()
                    for gname, (n, k) in groups.items()})
+    for layer in range(L):
+        model.append({gname: (torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                              torch.empty((n, k // 16), dtype=torch.int16, device=dev))
+                      for gname, (n, k) in groups.items()})
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for layer in range(L):
+        for gname in groups:
+            tqa.quantize(src[layer][gname], out=model[layer][gname])
+    e1.record(stream)
+    e1.synchronize()
+    q_ms = e0.elapsed_time(e1)
+    q_bytes = L * sum((2.0 + WEIGHT_BYTES_PER_ELEM) * n * k for n, k in groups.values())
+    del src
+    torch.cuda.empty_cache()
     torch.cuda.synchronize()
     xr_buf = {gname: torch.empty(k, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
     y_buf = {gname: torch.empty(n, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
@@ -220,7 +225,8 @@ def main():
         "per_group": per_group,
         "quantize": {"GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms_total": round(q_ms, 3),
                      "weights": int(q_bytes / (2.0 + WEIGHT_BYTES_PER_ELEM)),
-                     "bytes": "2 B bf16 in + 0.625 B out per weight"},
+                     "bytes": "2 B bf16 in + 0.625 B out per weight",
+                     "timing": "128 tensors of the bf16 model quantized back to back between two events"},
     }
 
     # ----------------------------------------------------- secondary rows
@@ -337,25 +343,28 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers):
     """27B-shaped layers: per-tensor NVFP4 or MXFP6 (seeded, ~10% MXFP6); quantize and GEMV at M = 1, 8."""
     names = ["q", "k", "v", "o", "gate", "up", "down"]
     store = []
-    q_ms = 0.0
     q_bytes = 0.0
     fmt_count = {"nvfp4": 0, "mxfp6": 0}
+    src = []
     for layer in range(layers):
         for t in names:
             fmt = wl.qwen27b_format(layer, t)
             fmt_count[fmt] += 1
-            W = wl.qwen27b_weight(t, layer, dev)
-            n, k = W.shape
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            codes, bs, ts = tqa.blockfp_quantize(fmt, W)
-            b.record(stream)
-            b.synchronize()
-            q_ms += a.elapsed_time(b)
-            reads = 2 if fmt == "nvfp4" else 1          # NVFP4 reads W twice (amax, encode)
-            q_bytes += (2.0 * reads + (0.5625 if fmt == "nvfp4" else 0.78125)) * n * k
-            store.append((fmt, codes, bs, ts, n, k))
-            del W
+            src.append((fmt, wl.qwen27b_weight(t, layer, dev)))
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)                                    # all tensors back to back between two events
+    for fmt, W in src:
+        n, k = W.shape
+        codes, bs, ts = tqa.blockfp_quantize(fmt, W)
+        reads = 2 if fmt == "nvfp4" else 1              # NVFP4 reads W twice (amax, encode)
+        q_bytes += (2.0 * reads + (0.5625 if fmt == "nvfp4" else 0.78125)) * n * k
+        store.append((fmt, codes, bs, ts, n, k))
+    b.record(stream)
+    b.synchronize()
+    q_ms = a.elapsed_time(b)
+    del src
+    torch.cuda.empty_cache()
     res = {"layers": layers, "tensors": fmt_count, "quantize_GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}
     for m in (1, 8):
         xsv = {}
