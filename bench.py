@@ -99,7 +99,24 @@ def main():
     e1.synchronize()
     q_ms = e0.elapsed_time(e1)
     q_bytes = L * sum((2.0 + WEIGHT_BYTES_PER_ELEM) * n * k for n, k in groups.values())
-    del src
+    # RSF-lite scale search over the same tensors (offline quantizer option), and its error reduction.
+    tmp = {gname: (torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((n, k // 16), dtype=torch.int16, device=dev)) for gname, (n, k) in groups.items()}
+    e0.record(stream)
+    for layer in range(L):
+        for gname in groups:
+            tqa.quantize(src[layer][gname], out=tmp[gname], rsf=True)
+    e1.record(stream)
+    e1.synchronize()
+    rsf_ms = e0.elapsed_time(e1)
+    Wt = src[0]["gate_up"]
+    Wf = Wt.float()
+    err_plain = (tqa.dequantize(*model[0]["gate_up"]) - Wf).pow(2).sum().item()
+    err_rsf = (tqa.dequantize(*tqa.quantize(Wt, rsf=True)) - Wf).pow(2).sum().item()
+    rsf_row = {"GB_s": round(q_bytes / (rsf_ms * 1e-3) / 1e9, 1), "ms_total": round(rsf_ms, 3),
+               "sq_error_vs_plain": round(err_rsf / err_plain, 4),
+               "note": "nine scale multiples per half block; sq_error on layer 0 gate|up"}
+    del src, tmp, Wf
     torch.cuda.empty_cache()
     torch.cuda.synchronize()
     xr_buf = {gname: torch.empty(k, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
@@ -226,7 +243,8 @@ def main():
         "quantize": {"GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "ms_total": round(q_ms, 3),
                      "weights": int(q_bytes / (2.0 + WEIGHT_BYTES_PER_ELEM)),
                      "bytes": "2 B bf16 in + 0.625 B out per weight",
-                     "timing": "128 tensors of the bf16 model quantized back to back between two events"},
+                     "timing": "128 tensors of the bf16 model quantized back to back between two events",
+                     "rsf": rsf_row},
     }
 
     # ----------------------------------------------------- secondary rows

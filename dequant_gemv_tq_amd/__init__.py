@@ -31,7 +31,7 @@ _STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EALIGN", 4: "TQ_ED
 
 EXPORTED = [
     "tq_abi_version", "tq_status_str", "tq_codebook", "tq_sign_mask_from_seed", "tq_default_sign_mask",
-    "tq_quantize", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
+    "tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
     "tq_blockfp_quantize", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
 ]
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
     L.tq_sign_mask_from_seed.argtypes = [ctypes.c_uint64]
     L.tq_default_sign_mask.restype = u32
     L.tq_quantize.argtypes = [p, c_int, i64, i64, i64, u32, p, p, p]
+    L.tq_quantize_rsf.argtypes = [p, c_int, i64, i64, i64, u32, p, p, p]
     L.tq_dequantize.argtypes = [p, p, i64, i64, u32, p, c_int, i64, p]
     L.tq_rotate.argtypes = [p, c_int, i64, i64, i64, u32, p, c_int, i64, p]
     L.tq_gemv.argtypes = [p, p, i64, i64, u32, p, c_int, c_int, p, p]
@@ -71,7 +72,7 @@ def lib() -> ctypes.CDLL:
     L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
     L.tq_transcode_q8.argtypes = [p, p, i64, i64, u32, p, p, p]
     L.tq_q8_gemv.argtypes = [p, p, i64, i64, p, c_int, p, p]
-    for name in ("tq_quantize", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
+    for name in ("tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
                  "tq_blockfp_quantize", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv"):
         getattr(L, name).restype = c_int
     _lib = L
@@ -132,10 +133,11 @@ DEFAULT_SIGN_MASK = 0x7B1DCDAF
 # TQ4_1S
 # ----------------------------------------------------------------------------
 
-def quantize(W: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None):
+def quantize(W: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None, rsf: bool = False):
     """W [N, K] (fp32/bf16, row stride may exceed K) -> (packed uint8 [N, K/2], scales int16 [N, K/16]).
 
     ``scales`` holds the fp16 bit patterns of d0, d1 per block (view as float16).
+    ``rsf=True`` runs the RSF-lite scale search (tq_quantize_rsf).
     """
     _dev(W, "W")
     if W.dim() != 2 or W.stride(1) != 1:
@@ -146,9 +148,10 @@ def quantize(W: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None):
         scales = torch.empty((N, K // 16), dtype=torch.int16, device=W.device)
     else:
         packed, scales = out
-    st = lib().tq_quantize(_ptr(W), _dtype_code(W, "W"), N, K, W.stride(0), sign_mask & 0xFFFFFFFF,
-                           _ptr(packed), _ptr(scales), _stream())
-    _check("tq_quantize", st)
+    fn = "tq_quantize_rsf" if rsf else "tq_quantize"
+    st = getattr(lib(), fn)(_ptr(W), _dtype_code(W, "W"), N, K, W.stride(0), sign_mask & 0xFFFFFFFF,
+                            _ptr(packed), _ptr(scales), _stream())
+    _check(fn, st)
     return packed, scales
 
 

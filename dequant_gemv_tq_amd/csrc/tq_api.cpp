@@ -59,6 +59,16 @@ tq_status tq_quantize(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t 
   return from_hip(tq::launch_quantize(W, wt == TQ_BF16, N, K, ldw, sign_mask, packed, scales, stream));
 }
 
+tq_status tq_quantize_rsf(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t ldw, uint32_t sign_mask,
+                          uint8_t* packed, uint16_t* scales, hipStream_t stream) {
+  if (!W) return TQ_EINVAL;
+  if (tq_status st = check_weights(packed, scales, N, K)) return st;
+  if (ldw < K) return TQ_EINVAL;
+  if (!float_or_bf16(wt)) return TQ_EDTYPE;
+  if (!aligned(W, 16) || (ldw * dtype_size(wt)) % 16) return TQ_EALIGN;
+  return from_hip(tq::launch_quantize(W, wt == TQ_BF16, N, K, ldw, sign_mask, packed, scales, stream, true));
+}
+
 tq_status tq_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t sign_mask,
                         void* W_out, tq_dtype ot, int64_t ldo, hipStream_t stream) {
   if (!W_out) return TQ_EINVAL;

@@ -208,7 +208,7 @@ __device__ __forceinline__ void load_block(const void* p, float (&v)[32]) {
 // ---------------------------------------------------------------------------
 
 hipError_t launch_quantize(const void* W, bool bf16, int64_t N, int64_t K, int64_t ldw, uint32_t mask,
-                           uint8_t* packed, uint16_t* scales, hipStream_t s);
+                           uint8_t* packed, uint16_t* scales, hipStream_t s, bool rsf = false);
 hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
                              uint32_t mask, void* out, bool bf16, int64_t ldo, hipStream_t s);
 hipError_t launch_rotate(const void* x, bool xbf16, int64_t M, int64_t K, int64_t ldx, uint32_t mask,

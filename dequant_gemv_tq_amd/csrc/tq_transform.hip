@@ -49,11 +49,23 @@ __device__ __forceinline__ uint32_t nearest_index(float w, const uint32_t (&U)[7
   return pos ? 8u + j : 7u - j;
 }
 
-template <bool kBf16>
+// kRsf: the RSF-lite scale search (quantizer-tool page, "RSF": search nearby
+// multiples of the scale and keep the better lattice fit).  For each half,
+// candidates d_j = fp16(dd * (1 + j/16)) are tried in the order j = 0, -1,
+// +1, -2, +2, -3, +3, -4, +4; each re-chooses its indices with the same rule
+// and scores e_i = w'_i - fl(d_j * c[idx_i]), E = pairwise tree of e_i^2 in
+// float32; only a strictly smaller E replaces the current choice, so j = 0
+// (the plain quantizer) wins ties and nothing gets worse.
+template <bool kBf16, bool kRsf>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ W, int64_t ldw_bytes,
                                                             uint32_t nb, uint32_t total, uint32_t mask,
                                                             Codebook cb, uint4* __restrict__ packed,
                                                             uint32_t* __restrict__ scales) {
+  __shared__ float lut[16];
+  if constexpr (kRsf) {
+    stage_centroids(cb, lut);
+    __syncthreads();
+  }
   uint32_t g = blockIdx.x * kThreads + threadIdx.x;
   if (g >= total) return;
   uint32_t row = g / nb;
@@ -82,13 +94,52 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
     float rms = __builtin_sqrtf(s[0] * 0.0625f);
     dbits[h] = f32_to_f16_sat_rne(rms);
     float dd = f16_bits_to_f32_exact(dbits[h]);
-    uint32_t U[7];
+    if constexpr (!kRsf) {
+      uint32_t U[7];
 #pragma unroll
-    for (int r = 0; r < 7; ++r) U[r] = __float_as_uint(dd * cb.m[8 + r]);
+      for (int r = 0; r < 7; ++r) U[r] = __float_as_uint(dd * cb.m[8 + r]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int e = 16 * h + i;
-      words[e >> 3] |= nearest_index(v[e], U) << (4 * (e & 7));
+      for (int i = 0; i < 16; ++i) {
+        int e = 16 * h + i;
+        words[e >> 3] |= nearest_index(v[e], U) << (4 * (e & 7));
+      }
+    } else {
+      constexpr int kOrder[9] = {0, -1, 1, -2, 2, -3, 3, -4, 4};
+      float best = 0.f;
+      uint32_t best_bits = 0u, best_w0 = 0u, best_w1 = 0u;
+#pragma unroll 1
+      for (int c = 0; c < 9; ++c) {
+        const float mult = 1.0f + (float)kOrder[c] * 0.0625f;
+        const uint32_t bits = f32_to_f16_sat_rne(dd * mult);      // the float32 product is exact
+        const float ddj = f16_bits_to_f32_exact(bits);
+        uint32_t U[7];
+#pragma unroll
+        for (int r = 0; r < 7; ++r) U[r] = __float_as_uint(ddj * cb.m[8 + r]);
+        uint32_t w0 = 0u, w1 = 0u;
+        float sq[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t idx = nearest_index(v[16 * h + i], U);
+          if (i < 8) w0 |= idx << (4 * i);
+          else w1 |= idx << (4 * (i - 8));
+          const float e = v[16 * h + i] - ddj * lut[idx];
+          sq[i] = e * e;
+        }
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+          for (int i = 0; i < w; ++i) sq[i] = sq[2 * i] + sq[2 * i + 1];
+        }
+        if (c == 0 || sq[0] < best) {
+          best = sq[0];
+          best_bits = bits;
+          best_w0 = w0;
+          best_w1 = w1;
+        }
+      }
+      dbits[h] = best_bits;
+      words[2 * h] = best_w0;
+      words[2 * h + 1] = best_w1;
     }
   }
   packed[g] = make_uint4(words[0], words[1], words[2], words[3]);
@@ -182,7 +233,7 @@ inline uint32_t grid_for(uint32_t total) { return (total + kThreads - 1) / kThre
 // The flat block index g = row * nb + b is kept in 32 bits; callers split
 // larger tensors into row chunks so that each launch stays below 2^31 blocks.
 hipError_t launch_quantize(const void* W, bool bf16, int64_t N, int64_t K, int64_t ldw, uint32_t mask,
-                           uint8_t* packed, uint16_t* scales, hipStream_t s) {
+                           uint8_t* packed, uint16_t* scales, hipStream_t s, bool rsf) {
   const Codebook& cb = host_codebook();
   const uint32_t nb = (uint32_t)(K / kBlock);
   const int64_t esz = bf16 ? 2 : 4;
@@ -193,12 +244,17 @@ hipError_t launch_quantize(const void* W, bool bf16, int64_t N, int64_t K, int64
     const uint8_t* w = static_cast<const uint8_t*>(W) + r0 * ldw * esz;
     uint4* pk = reinterpret_cast<uint4*>(packed + r0 * (K / 2));
     uint32_t* sc = reinterpret_cast<uint32_t*>(scales + r0 * (K / 16));
-    if (bf16)
-      hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, s, w, ldw * esz, nb,
-                         total, mask, cb, pk, sc);
-    else
-      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, s, w, ldw * esz, nb,
-                         total, mask, cb, pk, sc);
+#define TQ_QUANT(B_, R_)                                                                                   \
+  hipLaunchKernelGGL((quantize_kernel<B_, R_>), dim3(grid_for(total)), dim3(kThreads), 0, s, w, ldw * esz, nb, \
+                     total, mask, cb, pk, sc)
+    if (bf16) {
+      if (rsf) TQ_QUANT(true, true);
+      else TQ_QUANT(true, false);
+    } else {
+      if (rsf) TQ_QUANT(false, true);
+      else TQ_QUANT(false, false);
+    }
+#undef TQ_QUANT
   }
   return hipGetLastError();
 }

@@ -112,6 +112,19 @@ tq_status tq_quantize(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t 
                       uint32_t sign_mask, uint8_t* packed, uint16_t* scales,
                       hipStream_t stream);
 
+/* tq_quantize with the RSF-lite scale search (quantizer-tool page, "RSF":
+ * refined scale fitting searches nearby multiples of a scale and keeps the
+ * better lattice fit; here without importance weights).  For each half
+ * block, candidates fp16(d * (1 + j/16)), j = -4..4, with d the plain scale,
+ * re-choose the indices with the same rule and are scored by the float32
+ * squared error of fl(d_j * c[idx]) against the rotated values (pairwise sum
+ * in index order); the smallest wins, ties to the multiplier nearest 1.  The
+ * output is ordinary TQ4_1S (same layout, every other call reads it) and
+ * bit-exact against that definition.  Arguments, alignment and errors as
+ * tq_quantize; about six times its arithmetic. */
+tq_status tq_quantize_rsf(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t ldw,
+                          uint32_t sign_mask, uint8_t* packed, uint16_t* scales, hipStream_t stream);
+
 /* Dequantize TQ4_1S back to the original (unrotated) domain: per block
  * W_out = (1/sqrt 32) * D * H32 * (d_h * c[index]) (TQ4 page, paragraph after
  * "格式原理": the reference dequantizes by inverse rotation and rescaling).

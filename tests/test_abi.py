@@ -74,6 +74,7 @@ def _p(v):
 ])
 def test_quantize_rejects(args, expect):
     assert tqa.lib().tq_quantize(*args) == expect
+    assert tqa.lib().tq_quantize_rsf(*args) == expect
 
 
 def test_other_calls_reject_before_launch():
