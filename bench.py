@@ -381,9 +381,16 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers):
     b.record(stream)
     b.synchronize()
     q_ms = a.elapsed_time(b)
+    a.record(stream)                                    # the same tensors with the RSF-lite block-scale search
+    for fmt, W in src:
+        tqa.blockfp_quantize(fmt, W, rsf=True)
+    b.record(stream)
+    b.synchronize()
+    rsf_ms = a.elapsed_time(b)
     del src
     torch.cuda.empty_cache()
-    res = {"layers": layers, "tensors": fmt_count, "quantize_GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1)}
+    res = {"layers": layers, "tensors": fmt_count, "quantize_GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+           "quantize_rsf_GB_s": round(q_bytes / (rsf_ms * 1e-3) / 1e9, 1)}
     for m in (1, 8):
         xsv = {}
         for (fmt, codes, bs, ts, n, k) in store:

@@ -32,7 +32,7 @@ _STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EALIGN", 4: "TQ_ED
 EXPORTED = [
     "tq_abi_version", "tq_status_str", "tq_codebook", "tq_sign_mask_from_seed", "tq_default_sign_mask",
     "tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
-    "tq_blockfp_quantize", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
+    "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
 ]
 
 
@@ -69,11 +69,12 @@ def lib() -> ctypes.CDLL:
     L.tq_gemv.argtypes = [p, p, i64, i64, u32, p, c_int, c_int, p, p]
     L.tq_gemm.argtypes = [p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
     L.tq_blockfp_quantize.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p]
+    L.tq_blockfp_quantize_rsf.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p]
     L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
     L.tq_transcode_q8.argtypes = [p, p, i64, i64, u32, p, p, p]
     L.tq_q8_gemv.argtypes = [p, p, i64, i64, p, c_int, p, p]
     for name in ("tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
-                 "tq_blockfp_quantize", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv"):
+                 "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -212,8 +213,10 @@ def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=No
 # NVFP4 / MXFP6
 # ----------------------------------------------------------------------------
 
-def blockfp_quantize(fmt: str, W: torch.Tensor):
-    """-> (codes uint8, block_scales uint8, tensor_scale float32[1] or None)."""
+def blockfp_quantize(fmt: str, W: torch.Tensor, rsf: bool = False):
+    """-> (codes uint8, block_scales uint8, tensor_scale float32[1] or None).
+
+    ``rsf=True`` runs the RSF-lite block-scale search (tq_blockfp_quantize_rsf)."""
     _dev(W, "W")
     if not W.is_contiguous():
         raise ValueError("W must be contiguous")
@@ -227,9 +230,9 @@ def blockfp_quantize(fmt: str, W: torch.Tensor):
         codes = torch.empty((N, 3 * K // 4), dtype=torch.uint8, device=W.device)
         bs = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
         ts = None
-    st = lib().tq_blockfp_quantize(f, _ptr(W), _dtype_code(W, "W"), N, K, _ptr(codes), _ptr(bs), _ptr(ts),
-                                   _stream())
-    _check("tq_blockfp_quantize", st)
+    fn = "tq_blockfp_quantize_rsf" if rsf else "tq_blockfp_quantize"
+    st = getattr(lib(), fn)(f, _ptr(W), _dtype_code(W, "W"), N, K, _ptr(codes), _ptr(bs), _ptr(ts), _stream())
+    _check(fn, st)
     return codes, bs, ts
 
 

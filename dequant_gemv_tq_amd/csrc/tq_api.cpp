@@ -111,8 +111,8 @@ tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
   return from_hip(tq::launch_gemm(packed, scales, N, K, M, x_rot, xt == TQ_BF16, ldx, y, ldy, stream));
 }
 
-tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
-                              uint8_t* block_scales, float* tensor_scale, hipStream_t stream) {
+static tq_status blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
+                                  uint8_t* block_scales, float* tensor_scale, hipStream_t stream, bool rsf) {
   if (f != TQ_FMT_NVFP4 && f != TQ_FMT_MXFP6) return TQ_EINVAL;
   if (!W || !codes || !block_scales || N <= 0 || K <= 0) return TQ_EINVAL;
   if (f == TQ_FMT_NVFP4 && !tensor_scale) return TQ_EINVAL;
@@ -122,7 +122,17 @@ tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N
   if (!aligned(W, 16) || (K * dtype_size(wt)) % 16 || !aligned(codes, 8)) return TQ_EALIGN;
   if (f == TQ_FMT_NVFP4 && !aligned(tensor_scale, 4)) return TQ_EALIGN;
   return from_hip(tq::launch_blockfp_quantize((int)f, W, wt == TQ_BF16, N, K, codes, block_scales, tensor_scale,
-                                              stream));
+                                              stream, rsf));
+}
+
+tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
+                              uint8_t* block_scales, float* tensor_scale, hipStream_t stream) {
+  return blockfp_quantize(f, W, wt, N, K, codes, block_scales, tensor_scale, stream, false);
+}
+
+tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
+                                  uint8_t* block_scales, float* tensor_scale, hipStream_t stream) {
+  return blockfp_quantize(f, W, wt, N, K, codes, block_scales, tensor_scale, stream, true);
 }
 
 tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale,

@@ -11,6 +11,9 @@
 //   MXFP6: 32 E3M2 values per block and an E8M0 scale 2^e with
 //          e = floor(log2 amax_b) - 4 (the E3M2 emax), clamped to [-127, 127];
 //          code = E3M2(w * 2^-e).
+// The quantizers optionally run an RSF-lite search over nearby block scales
+// (quantizer-tool page, "RSF"), unweighted: the candidate with the smallest
+// float32 squared reconstruction error wins.
 // Every division is the correctly rounded float32 division, and the small
 // float encoder is exact (power-of-two scaling + round-half-even), so the
 // codes are reproducible bit for bit.
@@ -43,6 +46,32 @@ __device__ __forceinline__ uint32_t encode_mag(float a) {
 }
 
 __device__ __forceinline__ uint32_t sign_of(float v) { return __float_as_uint(v) >> 31; }
+
+// encode_mag that also returns the magnitude the code stands for (exact:
+// the rounded integer times a power of two, or the format's largest value).
+template <int kM, int kEmin, uint32_t kMaxCode>
+__device__ __forceinline__ uint32_t encode_mag_val(float a, float maxval, float& val) {
+  int e = floor_log2(a);
+  e = e < kEmin ? kEmin : e;
+  const float q = __builtin_rintf(__builtin_ldexpf(a, kM - e));
+  const uint32_t code = (uint32_t)q + ((uint32_t)(e - kEmin) << kM);
+  val = code > kMaxCode ? maxval : __builtin_ldexpf(q, e - kM);
+  return code > kMaxCode ? kMaxCode : code;
+}
+
+// ((((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)))+(((s8+s9)+(s10+s11))+((s12+s13)+(s14+s15)))) of s[o .. o+15].
+template <int kN>
+__device__ __forceinline__ float tree16(const float (&s)[kN], int o) {
+  float a[8], b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = s[o + 2 * i] + s[o + 2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = a[2 * i] + a[2 * i + 1];
+  return (b[0] + b[1]) + (b[2] + b[3]);
+}
+
+// RSF-lite candidate order: multiplier 1 + j/16 for j = 0, -1, +1, -2, +2, ...
+__device__ __forceinline__ int rsf_step(int t) { return (t & 1) ? -((t + 1) >> 1) : (t >> 1); }
 
 // --------------------------------------------------------------------------
 // NVFP4 quantizer: fill -> amax (atomicMax on the bit pattern of |w|,
@@ -90,8 +119,29 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint8_t* __restric
   }
 }
 
-// One thread per 16-element block.
-template <bool kBf16>
+// Squared float32 error of a 16-element block encoded with effective scale
+// eff (codes +0 when eff = 0), summed as tree16.
+__device__ __forceinline__ float nvfp4_block_error(const float (&v)[16], float eff) {
+  float s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float qhat = 0.0f;
+    if (eff != 0.0f) {
+      const float q = v[i] / eff;
+      float val;
+      encode_mag_val<1, 0, 7u>(fabsf(q), 6.0f, val);
+      qhat = (sign_of(q) ? -val : val) * eff;
+    }
+    const float d = v[i] - qhat;
+    s[i] = d * d;
+  }
+  return tree16(s, 0);
+}
+
+// One thread per 16-element block.  kRsf: the block scale is chosen among
+// the E4M3 roundings of dec(sb_0) * (1 + j/16), j = 0, -1, +1, ..., -4, +4,
+// by the smallest float32 squared error (ties keep the earlier candidate).
+template <bool kBf16, bool kRsf>
 __global__ __launch_bounds__(kThreads) void nvfp4_encode_kernel(const uint8_t* __restrict__ W, uint32_t total,
                                                                 const uint32_t* __restrict__ amax_bits,
                                                                 uint2* __restrict__ codes,
@@ -129,6 +179,19 @@ __global__ __launch_bounds__(kThreads) void nvfp4_encode_kernel(const uint8_t* _
     for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
     const float six_st = 6.0f * st;
     sb = encode_mag<3, -6, 0x7eu>(ab / six_st);
+    if constexpr (kRsf) {
+      const float base = e4m3_decode(sb);
+      float best = nvfp4_block_error(v, e4m3_decode(sb) * st);
+#pragma unroll 1
+      for (int t = 1; t < 9; ++t) {
+        const uint32_t c = encode_mag<3, -6, 0x7eu>(base * (1.0f + (float)rsf_step(t) * 0.0625f));
+        const float err = nvfp4_block_error(v, e4m3_decode(c) * st);
+        if (err < best) {
+          best = err;
+          sb = c;
+        }
+      }
+    }
     const float eff = e4m3_decode(sb) * st;
     if (eff != 0.0f) {
 #pragma unroll
@@ -148,9 +211,25 @@ __global__ void nvfp4_finalize(uint32_t* ts) { *ts = __float_as_uint(__uint_as_f
 
 // --------------------------------------------------------------------------
 // MXFP6 quantizer: one thread per 32-element block, 24 bytes of codes.
+// kRsf: the scale exponent is chosen among e0, e0 - 1, e0 + 1 (clamped) by
+// the smallest float32 squared error, tree16(first half) + tree16(second
+// half); ties keep the earlier candidate.
 // --------------------------------------------------------------------------
 
-template <bool kBf16>
+__device__ __forceinline__ float mxfp6_block_error(const float (&v)[32], int e) {
+  float s[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float q = __builtin_ldexpf(v[i], -e);
+    float val;
+    encode_mag_val<2, -2, 0x1fu>(fabsf(q), 28.0f, val);
+    const float d = v[i] - __builtin_ldexpf(sign_of(q) ? -val : val, e);
+    s[i] = d * d;
+  }
+  return tree16(s, 0) + tree16(s, 16);
+}
+
+template <bool kBf16, bool kRsf>
 __global__ __launch_bounds__(kThreads) void mxfp6_encode_kernel(const uint8_t* __restrict__ W, uint32_t total,
                                                                 uint2* __restrict__ codes,
                                                                 uint8_t* __restrict__ bscales) {
@@ -166,6 +245,20 @@ __global__ __launch_bounds__(kThreads) void mxfp6_encode_kernel(const uint8_t* _
   if (ab != 0.0f) {
     int e = floor_log2(ab) - 4;
     e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    if constexpr (kRsf) {
+      const int e0 = e;
+      float best = mxfp6_block_error(v, e0);
+#pragma unroll 1
+      for (int t = 1; t < 3; ++t) {
+        int ej = e0 + (t == 1 ? -1 : 1);
+        ej = ej < -127 ? -127 : (ej > 127 ? 127 : ej);
+        const float err = mxfp6_block_error(v, ej);
+        if (err < best) {
+          best = err;
+          e = ej;
+        }
+      }
+    }
     byte = (uint32_t)(e + 127);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -187,7 +280,7 @@ inline uint32_t grid_for(uint32_t total) { return (total + kThreads - 1) / kThre
 }  // namespace
 
 hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K, uint8_t* codes,
-                                   uint8_t* bscales, float* tscale, hipStream_t s) {
+                                   uint8_t* bscales, float* tscale, hipStream_t s, bool rsf) {
   const uint8_t* w = static_cast<const uint8_t*>(W);
   const int64_t esz = bf16 ? 2 : 4;
   if (fmt == TQ_FMT_NVFP4) {
@@ -205,12 +298,17 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
       const uint32_t total = (uint32_t)((blocks - b0 < per_launch) ? blocks - b0 : per_launch);
       const uint8_t* wb = w + b0 * 16 * esz;
       uint2* cb = reinterpret_cast<uint2*>(codes) + b0;
-      if (bf16)
-        hipLaunchKernelGGL(nvfp4_encode_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, ts, cb,
-                           bscales + b0);
-      else
-        hipLaunchKernelGGL(nvfp4_encode_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, ts,
-                           cb, bscales + b0);
+#define TQ_NVFP4(B, R) \
+  hipLaunchKernelGGL((nvfp4_encode_kernel<B, R>), dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, ts, cb, \
+                     bscales + b0)
+      if (bf16) {
+        if (rsf) TQ_NVFP4(true, true);
+        else TQ_NVFP4(true, false);
+      } else {
+        if (rsf) TQ_NVFP4(false, true);
+        else TQ_NVFP4(false, false);
+      }
+#undef TQ_NVFP4
     }
     hipLaunchKernelGGL(nvfp4_finalize, dim3(1), dim3(1), 0, s, ts);
   } else {
@@ -220,12 +318,17 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
       const uint32_t total = (uint32_t)((blocks - b0 < per_launch) ? blocks - b0 : per_launch);
       const uint8_t* wb = w + b0 * 32 * esz;
       uint2* cb = reinterpret_cast<uint2*>(codes) + b0 * 3;
-      if (bf16)
-        hipLaunchKernelGGL(mxfp6_encode_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, cb,
-                           bscales + b0);
-      else
-        hipLaunchKernelGGL(mxfp6_encode_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, cb,
-                           bscales + b0);
+#define TQ_MXFP6(B, R) \
+  hipLaunchKernelGGL((mxfp6_encode_kernel<B, R>), dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, cb, \
+                     bscales + b0)
+      if (bf16) {
+        if (rsf) TQ_MXFP6(true, true);
+        else TQ_MXFP6(true, false);
+      } else {
+        if (rsf) TQ_MXFP6(false, true);
+        else TQ_MXFP6(false, false);
+      }
+#undef TQ_MXFP6
     }
   }
   return hipGetLastError();

@@ -2,7 +2,7 @@
 //
 // Every kernel is written for gfx950 (CDNA4): 64-lane wavefronts, 160 KB of
 // LDS per CU, 256 CUs in 8 XCDs.  The host entry points in tq_api.cpp
-// validate arguments and call the launch_* functions declared here.
+// validate arguments and call the launch_* functions of tq_launch.hpp.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -203,33 +203,6 @@ __device__ __forceinline__ void load_block(const void* p, float (&v)[32]) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// launchers (each returns hipGetLastError() after its launches)
-// ---------------------------------------------------------------------------
-
-hipError_t launch_quantize(const void* W, bool bf16, int64_t N, int64_t K, int64_t ldw, uint32_t mask,
-                           uint8_t* packed, uint16_t* scales, hipStream_t s, bool rsf = false);
-hipError_t launch_dequantize(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K,
-                             uint32_t mask, void* out, bool bf16, int64_t ldo, hipStream_t s);
-hipError_t launch_rotate(const void* x, bool xbf16, int64_t M, int64_t K, int64_t ldx, uint32_t mask,
-                         void* xr, bool rbf16, int64_t ldr, hipStream_t s);
-hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t mask,
-                       const void* x, bool xbf16, bool rotated, float* y, hipStream_t s);
-hipError_t launch_gemm_valu(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
-                            const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
-hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
-                       const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
-hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K,
-                                   uint8_t* codes, uint8_t* bscales, float* tscale, hipStream_t s);
-hipError_t launch_blockfp_gemv(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
-                               int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
-                               hipStream_t s);
-hipError_t launch_transcode_q8(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t mask,
-                               int8_t* codes, uint16_t* qscales, hipStream_t s);
-hipError_t launch_q8_gemv(const int8_t* codes, const uint16_t* qscales, int64_t N, int64_t K, const void* x,
-                          bool xbf16, float* y, hipStream_t s);
-hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
-                               int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
-                               float* y, int64_t ldy, hipStream_t s);
-
 }  // namespace tq
+
+#include "tq_launch.hpp"

@@ -191,6 +191,25 @@ tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N
                               uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                               hipStream_t stream);
 
+/* tq_blockfp_quantize with the RSF-lite block-scale search (quantizer-tool
+ * page, "RSF": nearby multiples of a block scale are tried and the better
+ * lattice fit kept; here without importance weights).
+ *   TQ_FMT_NVFP4: per 16-element block, the E4M3 roundings of
+ *     dec(sb) * (1 + j/16), j = 0, -1, +1, ..., -4, +4 (sb the plain scale);
+ *     each re-encodes the block with the plain rule and is scored by the
+ *     float32 squared error of fl(e2m1 * eff) against w (pairwise sum in
+ *     index order).  The tensor scale is the plain one.
+ *   TQ_FMT_MXFP6: per 32-element block, exponents e, e - 1, e + 1 (clamped
+ *     to [-127, 127]) of the plain E8M0 scale, scored the same way over the
+ *     32 elements.
+ * The smallest error wins, ties to the earlier candidate (the plain scale
+ * first), so the result is never worse than tq_blockfp_quantize's and is
+ * bit-exact against that definition.  Output layout, arguments, alignment
+ * and errors as tq_blockfp_quantize. */
+tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K,
+                                  uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                                  hipStream_t stream);
+
 /* Y[m, n] = sum_k W_deq[n, k] X[m, k] for a block-float weight (fused
  * decode, float32 accumulation; the activation is used as given, there is
  * no rotation).  Codes are decoded by gfx950's scaled-convert instructions

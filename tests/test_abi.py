@@ -105,6 +105,14 @@ def test_other_calls_reject_before_launch():
     assert L.tq_blockfp_quantize(1, g, F32, 2, 40, g, g, g, None) == ESHAPE
     assert L.tq_blockfp_quantize(2, g, F32, 2, 48, g, g, None, None) == ESHAPE   # MXFP6 needs K % 32
     assert L.tq_blockfp_quantize(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
+    for fn in (L.tq_blockfp_quantize, L.tq_blockfp_quantize_rsf):
+        assert fn(3, g, F32, 2, 64, g, g, g, None) == EINVAL
+        assert fn(1, g, F32, 2, 64, g, g, None, None) == EINVAL
+        assert fn(1, g, F32, 2, 40, g, g, g, None) == ESHAPE
+        assert fn(2, g, F32, 2, 48, g, g, None, None) == ESHAPE
+        assert fn(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
+        assert fn(2, _p(GOOD + 4), F32, 2, 64, g, g, None, None) == EALIGN     # W: 16 B
+        assert fn(1, g, F32, 2, 64, _p(GOOD + 4), g, g, None) == EALIGN        # codes: 8 B
     assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 17, g, F32, 64, g, 8, None) == ESHAPE
     assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None) == EDTYPE
     assert L.tq_blockfp_gemm(1, _p(GOOD + 8), g, g, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN   # NVFP4 codes: 16 B
