@@ -278,7 +278,7 @@ def bench_gemm(torch, tqa, wl, model, groups, dev, stream):
     """Small-batch GEMM over the 32-layer stream (bf16 pre-rotated activations)."""
     res = {}
     L = len(model)
-    for m in (1, 4, 16, 32, 64):
+    for m in (1, 4, 8, 16, 32, 64):
         xr = {}
         for gi, (gname, (n, k)) in enumerate(groups.items()):
             g = wl.generator(wl.seed_of(3, m, gi), dev)
@@ -297,7 +297,7 @@ def bench_gemm(torch, tqa, wl, model, groups, dev, stream):
         flops = sum(L * 2.0 * m * n * k for n, k in groups.values())
         res[f"M{m}"] = {"ms_32_layers": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
                         "TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 2),
-                        "path": "VALU fp32" if m < 16 else "MFMA bf16"}
+                        "path": "VALU fp32" if m <= 4 else "MFMA bf16"}
     return res
 
 

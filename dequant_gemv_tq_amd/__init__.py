@@ -195,7 +195,7 @@ def gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, rotated: b
 
 
 def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=None):
-    """Y [M, N] float32 = X' Q^T with pre-rotated activations x_rot [M, K] (bf16, or fp32 for M < 16)."""
+    """Y [M, N] float32 = X' Q^T with pre-rotated activations x_rot [M, K] (bf16 or fp32)."""
     _dev(packed, "packed")
     _dev(x_rot, "x_rot")
     N, K = packed.shape[0], packed.shape[1] * 2

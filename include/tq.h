@@ -164,8 +164,9 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  *   x_rot   [M, K] pre-rotated activations (tq_rotate), row stride ldx,
  *           TQ_BF16 or TQ_F32, 16-byte aligned.
  *   y       [M, N] float32, row stride ldy (output).
- * M < 16 runs a VALU kernel with float32 FMAs.  M >= 16 runs bf16 MFMA with
- * float32 accumulation, dequantizing each weight once: one pass for bf16
+ * M <= 4 (and float32 activations with M < 16) run a VALU kernel with
+ * float32 FMAs.  Larger M runs bf16 MFMA in 16-row tiles with float32
+ * accumulation, dequantizing each weight once: one pass for bf16
  * activations (operand rounding about 2^-9, inside 1e-3 * sum|w x| once K is
  * in the hundreds), three hi/lo-split passes for float32 activations (about
  * 16 significant bits per product, any K).
