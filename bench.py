@@ -358,7 +358,8 @@ def bench_q8(torch, tqa, model, xs, groups, dev, stream, tq4_ms, no_graph):
 
 
 def bench_blockfp(torch, tqa, wl, dev, stream, layers):
-    """27B-shaped layers: per-tensor NVFP4 or MXFP6 (seeded, ~10% MXFP6); quantize and GEMV at M = 1, 8."""
+    """27B-shaped layers: per-tensor NVFP4 or MXFP6 (seeded, ~10% MXFP6); quantize, and the fused decode at
+    M = 1 (VALU GEMV), 8, 16 and 64 (bf16 MFMA)."""
     names = ["q", "k", "v", "o", "gate", "up", "down"]
     store = []
     q_bytes = 0.0
@@ -391,7 +392,7 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers):
     torch.cuda.empty_cache()
     res = {"layers": layers, "tensors": fmt_count, "quantize_GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
            "quantize_rsf_GB_s": round(q_bytes / (rsf_ms * 1e-3) / 1e9, 1)}
-    for m in (1, 8):
+    for m in (1, 8, 16, 64):
         xsv = {}
         for (fmt, codes, bs, ts, n, k) in store:
             if k not in xsv:

@@ -143,7 +143,7 @@ tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* bloc
   if (f == TQ_FMT_NVFP4 && !tensor_scale) return TQ_EINVAL;
   if (ldx < K || ldy < N) return TQ_EINVAL;
   if (K % 32) return TQ_ESHAPE;
-  if (M > 16 || K > 32768 || N > 0x7fffffff) return TQ_ESHAPE;
+  if (M > 4096 || K > 32768 || N > 0x7fffffff) return TQ_ESHAPE;
   if (!float_or_bf16(xt)) return TQ_EDTYPE;
   if (!aligned(codes, f == TQ_FMT_NVFP4 ? 16 : 8) || !aligned(x, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4))
     return TQ_EALIGN;

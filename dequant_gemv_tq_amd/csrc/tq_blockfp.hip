@@ -334,10 +334,4 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
   return hipGetLastError();
 }
 
-hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
-                               int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
-                               hipStream_t s) {
-  return launch_blockfp_gemv(fmt, codes, bscales, tscale, N, K, M, x, xbf16, ldx, y, ldy, s);
-}
-
 }  // namespace tq

@@ -336,6 +336,121 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 }
 
 // ---------------------------------------------------------------------------
+// Weight formats of the persistent kernel.  Lane (n, g) of a wavefront loads
+// block 4 q + g of weight row n for group q (four 32-element blocks) and
+// turns it into the bf16 B operands of the four MFMA steps of the group:
+//   kByBlock = true:  step s covers block 4 q + s, lane group g its elements
+//                     8 g .. 8 g + 7 (the raw dwords are transposed across
+//                     the lane groups first);
+//   kByBlock = false: step s covers elements 8 s .. 8 s + 7 of every lane
+//                     group's own block (no transpose; the activation
+//                     operands are read from LDS in the same order).
+// kLoads is the number of vector loads a group's weights take (the exact
+// wait in the prologue counts them); kLut says whether the pair table is
+// needed; kTensorScale whether the finished sums are multiplied by a
+// float32 tensor scale.
+// ---------------------------------------------------------------------------
+
+// TQ4_1S: 16 bytes of nibbles and the fp16 scale pair per block; each weight
+// is the centroid pair lookup times its fp16 scale, rounded to bf16.
+struct GemmTQ4 {
+  static constexpr bool kLut = true, kByBlock = true, kTensorScale = false;
+  static constexpr int kLoads = 2;
+  struct Raw {
+    uint4 p;
+    uint32_t sc;
+  };
+  struct Dec {
+    uint32_t w[4], sc[4];
+  };
+  __device__ __forceinline__ static void load(Raw& r, const uint8_t* codes, const uint8_t* scales, size_t blk) {
+    r.p = reinterpret_cast<const uint4*>(codes)[blk];
+    r.sc = reinterpret_cast<const uint32_t*>(scales)[blk];
+  }
+  __device__ __forceinline__ static void prepare(const Raw& r, Dec& d) {
+    transpose_groups(r.p, d.w);
+    transpose_groups(make_uint4(r.sc, r.sc, r.sc, r.sc), d.sc);
+  }
+  __device__ __forceinline__ static bf16x8 operand(const Dec& d, int s, uint32_t g, const uint8_t* lut,
+                                                   uint32_t laneoff) {
+    const float sc = f16_bits_to_f32(g < 2u ? (d.sc[s] & 0xffffu) : (d.sc[s] >> 16));
+    float v[8];
+    dequant8(d.w[s], sc, lut, laneoff, v);
+    return as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7]));
+  }
+};
+
+// NVFP4: 16 bytes of E2M1 codes and two E4M3 scales per 32-element block.
+// The scaled fp4 conversion applies only the exponent of its scale, so the
+// codes are converted with scale 1 and multiplied by the E4M3 value in
+// float32; e2m1 * e4m3 has at most 6 significant bits, so the bf16 operand
+// is exact.  The tensor scale multiplies the finished sums.
+struct GemmNVFP4 {
+  static constexpr bool kLut = false, kByBlock = false, kTensorScale = true;
+  static constexpr int kLoads = 2;
+  struct Raw {
+    uint4 p;
+    uint32_t sc;
+  };
+  typedef Raw Dec;
+  __device__ __forceinline__ static void load(Raw& r, const uint8_t* codes, const uint8_t* scales, size_t blk) {
+    r.p = reinterpret_cast<const uint4*>(codes)[blk];
+    r.sc = reinterpret_cast<const uint16_t*>(scales)[blk];
+  }
+  __device__ __forceinline__ static void prepare(const Raw& r, Dec& d) { d = r; }
+  __device__ __forceinline__ static bf16x8 operand(const Dec& d, int s, uint32_t, const uint8_t*, uint32_t) {
+    const uint32_t w = s == 0 ? d.p.x : s == 1 ? d.p.y : s == 2 ? d.p.z : d.p.w;
+    const float sc = e4m3_decode((d.sc >> (8 * (s >> 1))) & 0xffu);
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);   // byte k: elements 2k, 2k + 1
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    return as_bf16x8(pack_bf16x2(v0[0] * sc, v0[1] * sc), pack_bf16x2(v1[0] * sc, v1[1] * sc),
+                     pack_bf16x2(v2[0] * sc, v2[1] * sc), pack_bf16x2(v3[0] * sc, v3[1] * sc));
+  }
+};
+
+// MXFP6: 24 bytes of E3M2 codes and one E8M0 scale per block.  One scaled
+// conversion turns the block into 32 bf16 values times 2^(byte - 127): the
+// scale is a power of two, which the conversion applies exactly.
+struct GemmMXFP6 {
+  static constexpr bool kLut = false, kByBlock = false, kTensorScale = false;
+  static constexpr int kLoads = 3;          // 16 + 8 bytes of codes, the scale byte
+  struct Raw {
+    uint4 a;
+    uint2 b;
+    uint32_t sc;
+  };
+  typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+  struct Dec {
+    u32x16 v;
+  };
+  __device__ __forceinline__ static void load(Raw& r, const uint8_t* codes, const uint8_t* scales, size_t blk) {
+    // 24 bytes at an 8-byte aligned offset: one 16-byte and one 8-byte load
+    // (global loads need 4-byte alignment only).
+    const uint8_t* c = codes + blk * 24;
+    r.a = *reinterpret_cast<const uint4*>(c);
+    r.b = *reinterpret_cast<const uint2*>(c + 16);
+    r.sc = scales[blk];
+  }
+  __device__ __forceinline__ static void prepare(const Raw& r, Dec& d) {
+    typedef unsigned u32x6 __attribute__((ext_vector_type(6)));
+    const u32x6 bits = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y};
+    // E8M0 byte b as the float32 2^(b - 127): the conversion reads the
+    // exponent field.  The empty asm keeps the shift here, at the use: the
+    // compiler otherwise computed it right after the next tile's load was
+    // issued, which made the loop wait for that load.
+    uint32_t sc = r.sc;
+    asm volatile("" : "+v"(sc));
+    d.v = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(bits, __uint_as_float(sc << 23)));
+  }
+  __device__ __forceinline__ static bf16x8 operand(const Dec& d, int s, uint32_t, const uint8_t*, uint32_t) {
+    return as_bf16x8(d.v[4 * s], d.v[4 * s + 1], d.v[4 * s + 2], d.v[4 * s + 3]);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Persistent small-batch kernel, bf16 activations, M <= 64: one 1024-thread
 // workgroup per CU, shaped like the fused GEMV.  K is covered in passes of
 // 16 * NQ groups of four blocks (NQ * 2048 elements): in a pass, wavefront w
@@ -357,21 +472,25 @@ constexpr int kWide = 16;
 constexpr int kRingBytes = 65536;
 constexpr int kAccFloats = 8192;      // outputs of one workgroup that the pass accumulator holds
 
-template <int MT, int NQ>
-__global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __restrict__ packed,
-                                                                const uint32_t* __restrict__ scales, uint32_t N,
+template <class Fmt, int MT, int NQ>
+__global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint8_t* __restrict__ scales,
+                                                                const float* __restrict__ tscale, uint32_t N,
                                                                 uint32_t nb, const uint8_t* __restrict__ X,
                                                                 int64_t ldx, uint32_t M, float* __restrict__ Y,
                                                                 int64_t ldy, uint32_t G, uint32_t tq, uint32_t tr) {
   constexpr int kRing = kRingBytes / (kWide * 64 * 16 * MT);        // weight tiles per ring
   static_assert(kRing * 256 * MT == 64 * kWide, "one output per thread per flush");
-  // LDS: pair table | partial-tile ring | pass accumulator.  While a pass's
-  // activations are staged, the ring's space holds half of them at a time.
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLutBytes + kRingBytes + kAccFloats * 4];
+  // LDS: pair table (TQ4_1S only) | partial-tile ring | pass accumulator.
+  // While a pass's activations are staged, the ring's space holds a part of
+  // them at a time.
+  constexpr int kLutSpace = Fmt::kLut ? kLutBytes : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLutSpace + kRingBytes + kAccFloats * 4];
   uint8_t* const lut = smem;
-  f32x4 (*const ring)[kWide][MT][64] = reinterpret_cast<f32x4 (*)[kWide][MT][64]>(smem + kLutBytes);
-  float* const accum = reinterpret_cast<float*>(smem + kLutBytes + kRingBytes);
-  uint8_t* const stage = smem + kLutBytes;
+  f32x4 (*const ring)[kWide][MT][64] = reinterpret_cast<f32x4 (*)[kWide][MT][64]>(smem + kLutSpace);
+  float* const accum = reinterpret_cast<float*>(smem + kLutSpace + kRingBytes);
+  uint8_t* const stage = smem + kLutSpace;
+  const float ts = Fmt::kTensorScale ? *tscale : 1.0f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -388,8 +507,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
 
   uint4 A[NQ][4][MT];                      // this wavefront's activation operands of the pass
   struct WSet {
-    uint4 p[NQ];
-    uint32_t sc[NQ];
+    typename Fmt::Raw r[NQ];
   };
   // Group j of this wavefront in pass `pass`, block 4 q + g of the lane's
   // row (clamped: a group past the last one is skipped at compute time).
@@ -405,8 +523,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const uint32_t b = min(4u * group_of(pass, j) + g, nb - 1u);
-      w.p[j] = packed[(size_t)row * nb + b];
-      w.sc[j] = scales[(size_t)row * nb + b];
+      Fmt::load(w.r[j], codes, scales, (size_t)row * nb + b);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -447,15 +564,18 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
     __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt left alone
     __builtin_amdgcn_s_barrier();
   };
-  // The operands of part h: (j, s) of this wavefront whose 32 elements lie in it.
+  // The operands of part h: the groups j of this wavefront that lie in it
+  // (a part holds whole groups), step s in the format's element order.
+  static_assert(kPartK % 128u == 0u, "a part holds whole groups");
   auto read_ops = [&](uint32_t h) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t kl = 128u * ((uint32_t)wave + (uint32_t)(kWide * j)) + 32u * (uint32_t)s;   // wavefront-uniform
-        if (kl / kPartK == h) {
-          const uint32_t c = (kl - h * kPartK + 8u * g) / 8u;
+        const uint32_t kg = 128u * ((uint32_t)wave + (uint32_t)(kWide * j));   // wavefront-uniform
+        if (kg / kPartK == h) {
+          const uint32_t kin = Fmt::kByBlock ? 32u * (uint32_t)s + 8u * g : 32u * g + 8u * (uint32_t)s;
+          const uint32_t c = (kg - h * kPartK + kin) / 8u;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const uint32_t r = (uint32_t)(16 * mt + nl);
@@ -486,7 +606,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
         const uint32_t tt = t0 + (first + slot) * G;
         const uint32_t row = tt * 16u + (uint32_t)(l & 15);
         const uint32_t m = (uint32_t)mt * 16u + 4u * (uint32_t)(l >> 4) + (uint32_t)r;
-        if (m < M && row < N) Y[(size_t)m * ldy + row] = sum;
+        if (m < M && row < N) Y[(size_t)m * ldy + row] = Fmt::kTensorScale ? sum * ts : sum;
       }
     }
     __syncthreads();                        // the ring is rewritten next
@@ -500,7 +620,9 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
     // (The table is filled before the first DMA is issued: the compiler makes
     // LDS stores wait for any DMA into LDS still in flight.)
     load_w(pa, t0, pass);
-    if (pass == 0) fill_pair_lut(lut, tid, 64 * kWide);
+    if constexpr (Fmt::kLut) {
+      if (pass == 0) fill_pair_lut(lut, tid, 64 * kWide);
+    }
     dma_x(pass, 0);
     __syncthreads();                        // first part staged (and the table filled)
     read_ops(0);
@@ -510,10 +632,11 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
       dma_x(pass, (uint32_t)part);
       if constexpr (part == 1) {
         load_w(pb, min(t0 + G, last), pass);
-        // Wait for this wavefront's DMA, issued just before the 2 NQ
+        // Wait for this wavefront's DMA, issued just before the kLoads NQ
         // loads of pb (vector loads complete in order), so pb stays in
         // flight; then for the workgroup.
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NQ));
+        static_assert(Fmt::kLoads * NQ < 16, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (Fmt::kLoads * NQ));
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
@@ -533,18 +656,18 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
       for (int j = 0; j < NQ; ++j) {
         const uint32_t q = group_of(pass, j);
         if (q < ngroups) {                   // wavefront-uniform
-          uint32_t wt[4], sct[4];
-          transpose_groups(w.p[j], wt);
-          transpose_groups(make_uint4(w.sc[j], w.sc[j], w.sc[j], w.sc[j]), sct);
-          const uint32_t nsteps = min(4u, nb - 4u * q);
+          typename Fmt::Dec dec;
+          Fmt::prepare(w.r[j], dec);
+          // By block: steps past the last block are skipped.  By element:
+          // every step touches all four blocks, and a lane whose block lies
+          // past the last one contributes zero weights.
+          const uint32_t nsteps = Fmt::kByBlock ? min(4u, nb - 4u * q) : 4u;
+          const bool live = Fmt::kByBlock || 4u * q + g < nb;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             if ((uint32_t)s < nsteps) {
-              const float d = f16_bits_to_f32(g < 2u ? (sct[s] & 0xffffu) : (sct[s] >> 16));
-              float v[8];
-              dequant8(wt[s], d, lut, laneoff, v);
-              const bf16x8 B = as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+              bf16x8 B = Fmt::operand(dec, s, g, lut, laneoff);
+              if (!Fmt::kByBlock && !live) B = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[j][s][mt]), B,
@@ -574,9 +697,15 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint4* __r
   }
 }
 
-template <int MT, int NQ>
-void launch_small(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, const uint8_t* X, int64_t ldx,
-                  uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
+// Bytes of codes and of scales per 32-element block.
+template <class Fmt> constexpr size_t code_bytes() { return std::is_same<Fmt, GemmMXFP6>::value ? 24 : 16; }
+template <class Fmt> constexpr size_t scale_bytes() {
+  return std::is_same<Fmt, GemmTQ4>::value ? 4 : std::is_same<Fmt, GemmNVFP4>::value ? 2 : 1;
+}
+
+template <class Fmt, int MT, int NQ>
+void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb, const uint8_t* X,
+                  int64_t ldx, uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
   const uint32_t cap = (uint32_t)device_cu_count();
   const uint32_t passes = ((nb + 3u) / 4u + kWide * NQ - 1u) / (kWide * NQ);
   // With several passes a workgroup's outputs (16 * 16 * MT per tile) must
@@ -587,9 +716,20 @@ void launch_small(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, 
     const uint32_t tiles = (Nc + 15u) / 16u;
     const uint32_t per_wg = (tiles + cap - 1u) / cap;
     const uint32_t grid = (tiles + per_wg - 1u) / per_wg;
-    hipLaunchKernelGGL((gemm_small_kernel<MT, NQ>), dim3(grid), dim3(64 * kWide), 0, s, pk + r0 * nb, sc + r0 * nb,
-                       Nc, nb, X, ldx, M, Y + r0, ldy, grid, tiles / grid, tiles % grid);
+    hipLaunchKernelGGL((gemm_small_kernel<Fmt, MT, NQ>), dim3(grid), dim3(64 * kWide), 0, s,
+                       pk + r0 * nb * code_bytes<Fmt>(), sc + r0 * nb * scale_bytes<Fmt>(), ts, Nc, nb, X, ldx, M,
+                       Y + r0, ldy, grid, tiles / grid, tiles % grid);
   }
+}
+
+// The persistent kernel for one chunk of up to 64 rows: MT = 1 (two groups
+// per wavefront and pass), 2 or 4 tiles of 16 activation rows.
+template <class Fmt>
+void launch_small_mt(int mt, const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb,
+                     const uint8_t* X, int64_t ldx, uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
+  if (mt == 1) launch_small<Fmt, 1, 2>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, s);
+  else if (mt == 2) launch_small<Fmt, 2, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, s);
+  else launch_small<Fmt, 4, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, s);
 }
 
 // Weight groups in flight per wavefront: three where the registers allow.
@@ -645,13 +785,34 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
     const int mt = (int)((mc + 15) / 16);
     const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
-      if (mt == 1) launch_small<1, 2>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);   // the persistent kernel
-      else if (mt == 2) launch_small<2, 1>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
-      else launch_small<4, 1>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
+      launch_small_mt<GemmTQ4>(mt, packed, reinterpret_cast<const uint8_t*>(scales), nullptr, n, nb, Xm, ldx, mm, Ym,
+                               ldy, s);   // the persistent kernel
     } else {
       if (mt == 1) launch_mt<1, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
       else launch_mt<2, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
     }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
+                               int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y,
+                               int64_t ldy, hipStream_t s) {
+  // Up to four rows, and float32 activations, on the VALU kernel (rows in
+  // registers, any M); from five bf16 rows on, 16-row MFMA tiles with
+  // exactly converted bf16 weights.
+  if (M <= 4 || !xbf16) return launch_blockfp_gemv(fmt, codes, bscales, tscale, N, K, M, x, xbf16, ldx, y, ldy, s);
+  const uint32_t nb = (uint32_t)(K / kBlock);
+  const uint8_t* X = static_cast<const uint8_t*>(x);
+  for (int64_t m0 = 0; m0 < M; m0 += 64) {
+    const int64_t mc = (M - m0 < 64) ? M - m0 : 64;
+    const uint8_t* Xm = X + m0 * ldx * 2;
+    float* Ym = y + m0 * ldy;
+    const int mt = (int)((mc + 15) / 16);
+    if (fmt == TQ_FMT_NVFP4)
+      launch_small_mt<GemmNVFP4>(mt, codes, bscales, tscale, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, s);
+    else
+      launch_small_mt<GemmMXFP6>(mt, codes, bscales, nullptr, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, s);
   }
   return hipGetLastError();
 }

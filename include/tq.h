@@ -213,14 +213,19 @@ tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64
 
 /* Y[m, n] = sum_k W_deq[n, k] X[m, k] for a block-float weight (fused
  * decode, float32 accumulation; the activation is used as given, there is
- * no rotation).  Codes are decoded by gfx950's scaled-convert instructions
- * (E2M1 two at a time, E3M2 a whole 32-element block at a time, scale 1,
- * exact); each 16- (NVFP4) or 32-element (MXFP6) partial sum is multiplied
- * once by its scale: float32(e4m3 * tensor_scale) for NVFP4, 2^(e8m0 - 127)
- * (ldexp, exact) for MXFP6.  X [M, K] row stride ldx, TQ_F32 or TQ_BF16,
- * 16-byte aligned; Y [M, N] float32, row stride ldy.  K % 32 == 0,
- * K <= 32768, M <= 16; NVFP4 codes 16-byte aligned (MXFP6 codes 8-byte),
- * NVFP4 block_scales 2-byte aligned.
+ * no rotation).  Codes are decoded by gfx950's scaled-convert instructions.
+ *   M <= 4, or float32 X (any M): VALU kernel.  E2M1 two at a time, E3M2 a
+ *     whole 32-element block at a time, scale 1, exact; each 16- (NVFP4) or
+ *     32-element (MXFP6) partial sum is multiplied once by its scale:
+ *     float32(e4m3 * tensor_scale) for NVFP4, 2^(e8m0 - 127) (ldexp,
+ *     exact) for MXFP6.
+ *   M >= 5 with bf16 X: bf16 MFMA in 16-row tiles (up to 64 rows per
+ *     launch), every weight converted once to an exact bf16 operand
+ *     (e2m1 * e4m3 for NVFP4, the tensor scale applied to the finished sums;
+ *     e3m2 * 2^(e8m0 - 127) for MXFP6), float32 accumulation.
+ * X [M, K] row stride ldx, TQ_F32 or TQ_BF16, 16-byte aligned; Y [M, N]
+ * float32, row stride ldy.  K % 32 == 0, K <= 32768, M <= 4096; NVFP4 codes
+ * 16-byte aligned (MXFP6 codes 8-byte), NVFP4 block_scales 2-byte aligned.
  * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales,
                           const float* tensor_scale, int64_t N, int64_t K, int64_t M,

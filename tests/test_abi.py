@@ -113,7 +113,9 @@ def test_other_calls_reject_before_launch():
         assert fn(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
         assert fn(2, _p(GOOD + 4), F32, 2, 64, g, g, None, None) == EALIGN     # W: 16 B
         assert fn(1, g, F32, 2, 64, _p(GOOD + 4), g, g, None) == EALIGN        # codes: 8 B
-    assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 17, g, F32, 64, g, 8, None) == ESHAPE
+    assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 4097, g, F32, 64, g, 8, None) == ESHAPE   # M <= 4096
+    assert L.tq_blockfp_gemm(1, g, g, g, 8, 32800, 1, g, F32, 32800, g, 8, None) == ESHAPE  # K <= 32768
+    assert L.tq_blockfp_gemm(2, g, g, None, 8, 48, 1, g, F32, 64, g, 8, None) == ESHAPE     # K % 32
     assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None) == EDTYPE
     assert L.tq_blockfp_gemm(1, _p(GOOD + 8), g, g, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN   # NVFP4 codes: 16 B
     assert L.tq_blockfp_gemm(2, _p(GOOD + 4), g, None, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN  # MXFP6 codes: 8 B

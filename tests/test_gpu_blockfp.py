@@ -74,3 +74,35 @@ def test_blockfp_gemm(fmt, m):
     if m == 1:
         y1 = tqa.blockfp_gemm(fmt, codes, bs, ts, X[0].contiguous())
         assert torch.equal(y1, Y[0])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+@pytest.mark.parametrize("m", [5, 8, 17, 32, 33, 64, 65, 100])
+def test_blockfp_gemm_mfma(fmt, m):
+    """bf16 activations with M >= 5 take the MFMA kernel: exact bf16 weight operands, float32 sums (relative
+    error far below the bound).  Shapes: several passes over K (5120, 17408), a partial group of four blocks
+    (K = 96, 32), ragged row tiles."""
+    for n, k in ((300, 5120), (37, 96), (130, 32), (64, 17408)):
+        W = _outlier_weight(n, k, 700 + m + k, torch.bfloat16)
+        codes, bs, ts, Wd = _check(fmt, W)
+        X = workloads.activation(m, k, workloads.generator(910 + m + k, DEV), DEV, torch.bfloat16)
+        say(f"[{fmt} gemm mfma] M={m} {n}x{k}")
+        Y = tqa.blockfp_gemm(fmt, codes, bs, ts, X)
+        torch.cuda.synchronize()
+        yr, a = obf.gemm_deq_o64(Wd, X.float().cpu().numpy())
+        worst = assert_within(f32np(Y), yr, a, what=f"{fmt} mfma M={m} {n}x{k}")
+        assert worst < 1e-4
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+def test_blockfp_gemm_fp32_many_rows(fmt):
+    """float32 activations at any M stay on the VALU kernel (rows in chunks)."""
+    n, k, m = 70, 1024, 21
+    W = _outlier_weight(n, k, 811, torch.bfloat16)
+    codes, bs, ts, Wd = _check(fmt, W)
+    X = workloads.activation(m, k, workloads.generator(812, DEV), DEV, torch.float32)
+    say(f"[{fmt} gemm fp32] M={m}")
+    Y = tqa.blockfp_gemm(fmt, codes, bs, ts, X)
+    torch.cuda.synchronize()
+    yr, a = obf.gemm_deq_o64(Wd, X.cpu().numpy())
+    assert assert_within(f32np(Y), yr, a, what=f"{fmt} fp32 M={m}") < 1e-4
