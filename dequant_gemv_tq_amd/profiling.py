@@ -255,10 +255,12 @@ def stats(csv_path: str) -> None:
               "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 4>`.  "
               "Other kernels: the quantizer (`quantize_kernel<bf16, rsf>`, the second flag for the RSF-lite "
               "scale search), the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M <= 4, and float32 "
-              "activations below 16 rows; above, the persistent MFMA `gemm_small_kernel<MT, NQ>` with bf16 "
+              "activations below 16 rows; above, the persistent MFMA `gemm_small_kernel<format, MT, NQ>` with bf16 "
               "activations, MT = 1, 2, 4 "
-              "tiles of 16 activation rows, and `gemm_mfma_kernel` with float32 activations), dequantization "
-              "the NVFP4 / MXFP6 rows (`gemv_kernel<FmtNVFP4, ...>`, `gemv_kernel<FmtMXFP6, ...>`) and the "
+              "tiles of 16 activation rows, and `gemm_mfma_kernel` with float32 activations), dequantization, "
+              "the NVFP4 / MXFP6 rows (`gemv_kernel<FmtNVFP4, ...>`, `gemv_kernel<FmtMXFP6, ...>` up to four "
+              "activation rows, `gemm_small_kernel<GemmNVFP4, ...>`, `gemm_small_kernel<GemmMXFP6, ...>` from "
+              "five) and the "
               "load-time int8 rows (`q8_transcode_kernel`, `q8_gemv_kernel<bf16 activation, passes>`); the "
               "remaining GPU time is PyTorch drawing the synthetic weights.", ""]
     print("\n".join(lines))
