@@ -46,4 +46,4 @@ bit-compatibility with the llama.cpp fork's own files, which this package
 does not claim.
 """
 
-from . import codebook, tq4_1s, minifloat, blockfp, q8, rsf  # noqa: F401
+from . import codebook, tq4_1s, minifloat, blockfp, q8, rsf, kv  # noqa: F401
