@@ -252,6 +252,7 @@ def main():
     out["dequantize"] = bench_dequant(torch, tqa, model, groups, dev, stream)
     out["q8_transcode"] = bench_q8(torch, tqa, model, xs, groups, dev, stream, ms_per_step, args.no_graph)
     out["blockfp"] = bench_blockfp(torch, tqa, wl, dev, stream, layers=64 if args.extended else 4)
+    out["kv_attention"] = bench_kv(torch, tqa, wl, dev, stream, args.no_graph)
     if args.extended:
         del model, xs
         torch.cuda.empty_cache()
@@ -409,6 +410,63 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers):
                    for (f, _, _, _, n, k) in store)
         res[f"gemv_M{m}"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1)}
     return res
+
+
+KV_BYTES = 128 + 8 + 64 + 2      # per cached token and cache head: q8_0 key codes + scales, turbo4 nibbles + norm
+
+
+def bench_kv(torch, tqa, wl, dev, stream, no_graph, layers=32, batch=16, ctx=4096):
+    """turbo4 V / q8_0 K cache of the Llama-3-8B attention layout (32 query heads, 8 cache heads, head dim
+    128): bulk encode of every layer's cache, then one decode-attention step over all layers (split kernel +
+    combine per layer, captured in a graph), batch 16 x 4096 cached tokens."""
+    Hq, Hkv, D = 32, 8, 128
+    caches, enc_ms = [], 0.0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for layer in range(layers):
+        g = wl.generator(wl.seed_of(6, layer, 0), dev)
+        K = torch.randn((batch, Hkv, ctx, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        V = torch.randn((batch, Hkv, ctx, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        a.record(stream)
+        kc, ks = tqa.kv_quantize_k(K)
+        vp, vn = tqa.kv_quantize_v(V)
+        b.record(stream)
+        b.synchronize()
+        enc_ms += a.elapsed_time(b)
+        caches.append((kc, ks, vp, vn))
+        del K, V
+    torch.cuda.empty_cache()
+    g = wl.generator(wl.seed_of(6, 99, 1), dev)
+    qs = [torch.randn((batch, Hq, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+          for _ in range(layers)]
+    lengths = torch.full((batch,), ctx, dtype=torch.int32, device=dev)
+    outs = [torch.empty((batch, Hq, D), dtype=torch.float32, device=dev) for _ in range(layers)]
+    ws = torch.empty(tqa.attn_workspace_bytes(batch, Hq, ctx), dtype=torch.uint8, device=dev)
+    sign = tqa.kv_sign_from_seed(0)
+
+    def step():
+        for layer in range(layers):
+            kc, ks, vp, vn = caches[layer]
+            tqa.attn_decode(qs[layer], lengths, kc, ks, vp, vn, sign=sign, out=outs[layer], workspace=ws)
+
+    run = step
+    if not no_graph:
+        step()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        run = gr.replay
+    ms = _time(torch, stream, run, 10)
+    kv_bytes = layers * batch * ctx * Hkv * KV_BYTES
+    byts = kv_bytes + layers * batch * Hq * D * (2 + 4)
+    elems = layers * batch * ctx * Hkv * D
+    return {"layout": {"layers": layers, "batch": batch, "context": ctx, "q_heads": Hq, "kv_heads": Hkv,
+                       "head_dim": D},
+            "encode_GB_s": round(2 * elems * (2 + KV_BYTES / (2 * D)) / (enc_ms * 1e-3) / 1e9, 1),
+            "decode_step_ms": round(ms, 3), "decode_GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
+            "cache_bytes_per_token_head": KV_BYTES, "bf16_cache_bytes_per_token_head": 2 * 2 * D,
+            "note": "decode GB/s counts the quantized cache + q + o; the split kernel's partials are extra"}
 
 
 def bench_70b(torch, tqa, wl, dev, stream):

@@ -33,6 +33,8 @@ EXPORTED = [
     "tq_abi_version", "tq_status_str", "tq_codebook", "tq_sign_mask_from_seed", "tq_default_sign_mask",
     "tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
     "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
+    "tq_kv_sign_from_seed", "tq_kv_quantize_k", "tq_kv_quantize_v", "tq_kv_dequantize_v", "tq_attn_workspace_bytes",
+    "tq_attn_decode",
 ]
 
 
@@ -73,8 +75,17 @@ def lib() -> ctypes.CDLL:
     L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
     L.tq_transcode_q8.argtypes = [p, p, i64, i64, u32, p, p, p]
     L.tq_q8_gemv.argtypes = [p, p, i64, i64, p, c_int, p, p]
+    L.tq_kv_sign_from_seed.argtypes = [ctypes.c_uint64, p]
+    L.tq_kv_quantize_k.argtypes = [p, c_int, i64, i64, p, p, p]
+    L.tq_kv_quantize_v.argtypes = [p, c_int, i64, i64, p, p, p, p]
+    L.tq_kv_dequantize_v.argtypes = [p, p, i64, i64, p, p, p]
+    L.tq_attn_workspace_bytes.argtypes = [i64, i64, i64]
+    L.tq_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.tq_attn_decode.argtypes = [p, c_int, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
     for name in ("tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
-                 "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv"):
+                 "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
+                 "tq_kv_sign_from_seed", "tq_kv_quantize_k", "tq_kv_quantize_v", "tq_kv_dequantize_v",
+                 "tq_attn_decode"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -283,3 +294,82 @@ def q8_gemv(codes: torch.Tensor, q8_scales: torch.Tensor, x: torch.Tensor, out=N
     st = lib().tq_q8_gemv(_ptr(codes), _ptr(q8_scales), N, K, _ptr(x), _dtype_code(x, "x"), _ptr(y), _stream())
     _check("tq_q8_gemv", st)
     return y
+
+
+# ----------------------------------------------------------------------------
+# turbo4 KV cache and decode attention
+# ----------------------------------------------------------------------------
+
+def kv_sign_from_seed(seed: int = 0):
+    """The four 32-bit words of the 128 rotation sign bits (host array, ctypes)."""
+    out = (ctypes.c_uint32 * 4)()
+    _check("tq_kv_sign_from_seed", lib().tq_kv_sign_from_seed(seed, out))
+    return out
+
+
+def kv_quantize_k(K: torch.Tensor):
+    """Keys [..., d] (bf16/fp32, contiguous) -> (int8 codes [..., d], fp16 scales [..., d/32] as int16)."""
+    _dev(K, "K")
+    if not K.is_contiguous():
+        raise ValueError("K must be contiguous")
+    d = K.shape[-1]
+    n = K.numel() // d
+    codes = torch.empty(K.shape, dtype=torch.int8, device=K.device)
+    scales = torch.empty(K.shape[:-1] + (d // 32,), dtype=torch.int16, device=K.device)
+    st = lib().tq_kv_quantize_k(_ptr(K), _dtype_code(K, "K"), n, d, _ptr(codes), _ptr(scales), _stream())
+    _check("tq_kv_quantize_k", st)
+    return codes, scales
+
+
+def kv_quantize_v(V: torch.Tensor, sign=None):
+    """Values [..., 128] (bf16/fp32, contiguous) -> (packed uint8 [..., 64], fp16 norms [...] as int16)."""
+    _dev(V, "V")
+    if not V.is_contiguous():
+        raise ValueError("V must be contiguous")
+    d = V.shape[-1]
+    n = V.numel() // d
+    sign = kv_sign_from_seed(0) if sign is None else sign
+    packed = torch.empty(V.shape[:-1] + (d // 2,), dtype=torch.uint8, device=V.device)
+    norms = torch.empty(V.shape[:-1], dtype=torch.int16, device=V.device)
+    st = lib().tq_kv_quantize_v(_ptr(V), _dtype_code(V, "V"), n, d, sign, _ptr(packed), _ptr(norms), _stream())
+    _check("tq_kv_quantize_v", st)
+    return packed, norms
+
+
+def kv_dequantize_v(packed: torch.Tensor, norms: torch.Tensor, sign=None):
+    """turbo4 values back to float32 [..., 128]."""
+    _dev(packed, "packed")
+    d = packed.shape[-1] * 2
+    n = packed.numel() // (d // 2)
+    sign = kv_sign_from_seed(0) if sign is None else sign
+    out = torch.empty(packed.shape[:-1] + (d,), dtype=torch.float32, device=packed.device)
+    st = lib().tq_kv_dequantize_v(_ptr(packed), _ptr(norms), n, d, sign, _ptr(out), _stream())
+    _check("tq_kv_dequantize_v", st)
+    return out
+
+
+def attn_workspace_bytes(B: int, Hq: int, T_max: int) -> int:
+    return int(lib().tq_attn_workspace_bytes(B, Hq, T_max))
+
+
+def attn_decode(q: torch.Tensor, lengths: torch.Tensor, k_codes, k_scales, v_packed, v_norms, sign=None,
+                out=None, workspace=None):
+    """Decode attention: q [B, Hq, 128] (bf16/fp32), lengths int32 [B], head-major cache tensors
+    [B, Hkv, T_max, ...] from kv_quantize_k / kv_quantize_v -> o [B, Hq, 128] float32."""
+    for t, name in ((q, "q"), (lengths, "lengths"), (k_codes, "k_codes"), (v_packed, "v_packed")):
+        _dev(t, name)
+    B, Hq, d = q.shape
+    _, Hkv, T_max, _ = k_codes.shape
+    if lengths.dtype != torch.int32 or lengths.numel() != B:
+        raise ValueError("lengths must be int32 [B]")
+    sign = kv_sign_from_seed(0) if sign is None else sign
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    ws_bytes = attn_workspace_bytes(B, Hq, T_max)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=q.device)
+    st = lib().tq_attn_decode(_ptr(q), _dtype_code(q, "q"), B, Hq, Hkv, d, T_max, _ptr(lengths), _ptr(k_codes),
+                              _ptr(k_scales), _ptr(v_packed), _ptr(v_norms), sign, _ptr(o), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream())
+    _check("tq_attn_decode", st)
+    return o
+

@@ -25,7 +25,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 ARCH = "gfx950"
 
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_transform.hip", "tq_gemv.hip", "tq_gemm.hip", "tq_blockfp.hip",
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_transform.hip", "tq_gemv.hip", "tq_gemm.hip", "tq_blockfp.hip", "tq_kv.hip",
            "tq_q8.hip"]
 
 FLAGS = [

@@ -170,4 +170,55 @@ tq_status tq_q8_gemv(const int8_t* codes, const uint16_t* q8_scales, int64_t N, 
   return from_hip(tq::launch_q8_gemv(codes, q8_scales, N, K, x, xt == TQ_BF16, y, stream));
 }
 
+tq_status tq_kv_quantize_k(const void* K, tq_dtype kt, int64_t n, int64_t d, int8_t* codes, uint16_t* scales,
+                           hipStream_t stream) {
+  if (!K || !codes || !scales || n <= 0 || d <= 0) return TQ_EINVAL;
+  if (d % tq::kBlock) return TQ_ESHAPE;
+  if (!float_or_bf16(kt)) return TQ_EDTYPE;
+  if (!aligned(K, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return TQ_EALIGN;
+  return from_hip(tq::launch_q8_rows(K, kt == TQ_BF16, n * (d / tq::kBlock), codes, scales, stream));
+}
+
+tq_status tq_kv_quantize_v(const void* V, tq_dtype vt, int64_t n, int64_t d, const uint32_t sign[4],
+                           uint8_t* packed, uint16_t* norms, hipStream_t stream) {
+  if (!V || !sign || !packed || !norms || n <= 0 || d <= 0) return TQ_EINVAL;
+  if (d != 128) return TQ_ESHAPE;
+  if (!float_or_bf16(vt)) return TQ_EDTYPE;
+  if (!aligned(V, 16) || !aligned(packed, 8) || !aligned(norms, 2)) return TQ_EALIGN;
+  return from_hip(tq::launch_turbo4_encode(V, vt == TQ_BF16, n, sign, packed, norms, stream));
+}
+
+tq_status tq_kv_dequantize_v(const uint8_t* packed, const uint16_t* norms, int64_t n, int64_t d,
+                             const uint32_t sign[4], float* out, hipStream_t stream) {
+  if (!packed || !norms || !sign || !out || n <= 0 || d <= 0) return TQ_EINVAL;
+  if (d != 128) return TQ_ESHAPE;
+  if (!aligned(packed, 8) || !aligned(norms, 2) || !aligned(out, 16)) return TQ_EALIGN;
+  return from_hip(tq::launch_turbo4_decode(packed, norms, n, sign, out, stream));
+}
+
+size_t tq_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t T_max) {
+  if (B <= 0 || Hq <= 0 || T_max <= 0) return 0;
+  return tq::attn_workspace_bytes(B, Hq, T_max);
+}
+
+tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t T_max,
+                         const int32_t* lengths, const int8_t* k_codes, const uint16_t* k_scales,
+                         const uint8_t* v_packed, const uint16_t* v_norms, const uint32_t sign[4], float* o,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !lengths || !k_codes || !k_scales || !v_packed || !v_norms || !sign || !o || !workspace)
+    return TQ_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || T_max <= 0) return TQ_EINVAL;
+  if (d != 128 || Hq % Hkv) return TQ_ESHAPE;
+  const int64_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ESHAPE;
+  if (B > 65535 || Hkv > 65535 || Hq > 65535 || T_max > ((int64_t)1 << 31)) return TQ_ESHAPE;
+  if (ws_bytes < tq::attn_workspace_bytes(B, Hq, T_max)) return TQ_EINVAL;
+  if (!float_or_bf16(qt)) return TQ_EDTYPE;
+  if (!aligned(q, 16) || !aligned(lengths, 4) || !aligned(k_codes, 16) || !aligned(k_scales, 2) ||
+      !aligned(v_packed, 4) || !aligned(v_norms, 2) || !aligned(o, 4) || !aligned(workspace, 4))
+    return TQ_EALIGN;
+  return from_hip(tq::launch_attn_decode(q, qt == TQ_BF16, B, Hq, Hkv, T_max, lengths, k_codes, k_scales, v_packed,
+                                         v_norms, sign, o, workspace, stream));
+}
+
 }  // extern "C"

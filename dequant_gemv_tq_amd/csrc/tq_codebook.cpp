@@ -66,3 +66,19 @@ extern "C" uint32_t tq_sign_mask_from_seed(uint64_t seed) {
 }
 
 extern "C" uint32_t tq_default_sign_mask(void) { return tq_sign_mask_from_seed(0); }
+
+extern "C" tq_status tq_kv_sign_from_seed(uint64_t seed, uint32_t out[4]) {
+  if (!out) return TQ_EINVAL;
+  // The first two splitmix64 outputs: bits 0..63, then 64..127.
+  uint64_t state = seed;
+  for (int k = 0; k < 2; ++k) {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    out[2 * k] = (uint32_t)z;
+    out[2 * k + 1] = (uint32_t)(z >> 32);
+  }
+  return TQ_OK;
+}

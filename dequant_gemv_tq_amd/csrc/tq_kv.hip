@@ -1,0 +1,586 @@
+// turbo4 KV cache on gfx950: q8_0 keys, PolarQuant values (norm, random-sign
+// Hadamard rotation of the whole 128-element head vector, 16-centroid
+// indices), and decode attention over them (TQ4 page: the paragraph after
+// the "格式原理" list, on the PolarQuant steps and the structured rotation;
+// "叠加压缩：权重 + KV 缓存", asymmetric q8_0-K / turbo4-V).
+//
+// Value encode, float32 in this order (contraction off):
+//   ss = pairwise tree of w_i^2 (index order); n16 = fp16_sat(sqrt(ss));
+//   u = FWHT_128(D w) unnormalised, stages h = 1 .. 64;
+//   idx_i = #{k : u_i > fl(nn * m_k)}  (u_i / ||w|| is sqrt(128) times the
+//   rotated unit vector's coordinate, close to N(0, 1)).
+// Decode: v_hat = (nn / 128) D H c[idx].
+//
+// Attention keeps the values in the rotated domain: o = sum_t p_t v_hat_t =
+// (1/128) D H (sum_t p_t nn_t c[idx_t]), so the split kernel accumulates
+// z = sum_t p_t nn_t c[idx_t] with a centroid lookup per element, and the
+// combine kernel applies D H / 128 once per head.  The query is quantized
+// per 32-element block like the int8 GEMV's activation, so each key block's
+// dot product is an exact integer (v_dot4_i32_i8).
+#pragma clang fp contract(off)
+
+#include <algorithm>
+
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int kD = 128;                 // head dimension
+constexpr int kChunk = 256;             // tokens per split workgroup
+constexpr int kThreads = 256;
+constexpr int kLanesPerVec = 8;         // encode: 16 elements per lane
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct Signs {
+  uint32_t w[4];
+};
+
+// Sums over the 2, 4 and 8 lanes of an aligned 8-lane group with DPP: lane
+// ^ 1 and lane ^ 2 by quad permutes, the other quad of the group by the
+// half-row mirror (lane i <-> 7 - i).
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_mirror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+
+// Float32 value shuffled from lane ^ m (within the wavefront).
+__device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ int xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+
+// Elements 16 l .. 16 l + 15 of a vector held by lane l of an 8-lane group:
+// the unnormalised FWHT_128 in the oracle's stage order (in-lane stages h =
+// 1, 2, 4, 8, then lanes l ^ 1, l ^ 2, l ^ 4 for h = 16, 32, 64).  For each
+// pair (a, b) with a at the lower index the result is (a + b, a - b).
+__device__ __forceinline__ void fwht128_group(float (&v)[16], int sub) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    const bool upper = (sub & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = xor_f(v[i], m);
+      v[i] = upper ? p - v[i] : v[i] + p;
+    }
+  }
+}
+
+// Sign of element 16 sub + i: bit (16 sub + i) of the 128-bit mask.
+__device__ __forceinline__ bool sign_bit(const Signs& s, int sub, int i) {
+  return (s.w[sub >> 1] >> (16 * (sub & 1) + i)) & 1u;
+}
+
+// --------------------------------------------------------------------------
+// q8_0 rows: one thread per 32-element block.
+// --------------------------------------------------------------------------
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void q8_rows_kernel(const uint8_t* __restrict__ X, uint32_t total,
+                                                           uint4* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  float v[32];
+  load_block<kBf16>(X + (size_t)g * (kBf16 ? 64 : 128), v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t d16 = f32_to_f16_sat_rne(amax / 127.0f);
+  const float dd = f16_bits_to_f32_exact(d16);
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float c = dd > 0.f ? __builtin_rintf(v[4 * k + j] / dd) : 0.f;
+      c = fminf(fmaxf(c, -127.f), 127.f);
+      word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
+    }
+    w[k] = word;
+  }
+  codes[2 * (size_t)g] = make_uint4(w[0], w[1], w[2], w[3]);
+  codes[2 * (size_t)g + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[g] = (uint16_t)d16;
+}
+
+// --------------------------------------------------------------------------
+// turbo4 value encode / decode: an 8-lane group per vector.
+// --------------------------------------------------------------------------
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void turbo4_encode_kernel(const uint8_t* __restrict__ V, uint32_t nvec,
+                                                                 Signs sg, Codebook cb,
+                                                                 uint2* __restrict__ packed,
+                                                                 uint16_t* __restrict__ norms) {
+  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t vec = tid / kLanesPerVec;
+  const int sub = (int)(tid % kLanesPerVec);
+  // Every lane of a group takes part in the shuffles; lanes past the last
+  // vector work on a clamped one and store nothing.
+  const uint32_t vv = min(vec, nvec - 1u);
+  float w[16];
+  if constexpr (kBf16) {
+    const uint4* p = reinterpret_cast<const uint4*>(V + ((size_t)vv * kD + 16 * sub) * 2);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint4 u = p[t];
+      const uint32_t x[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        w[8 * t + 2 * k] = bf16_lo(x[k]);
+        w[8 * t + 2 * k + 1] = bf16_hi(x[k]);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(V + ((size_t)vv * kD + 16 * sub) * 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 u = p[t];
+      w[4 * t] = u.x; w[4 * t + 1] = u.y; w[4 * t + 2] = u.z; w[4 * t + 3] = u.w;
+    }
+  }
+  // Norm: the pairwise tree over 128 squares in index order (16 in the lane,
+  // then lane pairs, quads, the group).
+  float s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = w[i] * w[i];
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
+#pragma unroll
+    for (int i = 0; i < m; ++i) s[i] = s[2 * i] + s[2 * i + 1];
+  }
+  float ss = s[0];
+  ss = ss + xor_f(ss, 1);
+  ss = ss + xor_f(ss, 2);
+  ss = ss + xor_f(ss, 4);
+  const uint32_t n16 = f32_to_f16_sat_rne(__builtin_sqrtf(ss));
+  const float nn = f16_bits_to_f32_exact(n16);
+
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = sign_bit(sg, sub, i) ? -w[i] : w[i];
+  fwht128_group(w, sub);
+
+  float T[15];
+#pragma unroll
+  for (int k = 0; k < 15; ++k) T[k] = nn * cb.m[k];
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t idx = 0u;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) idx += w[i] > T[k] ? 1u : 0u;
+    if (i < 8) lo |= idx << (4 * i);
+    else hi |= idx << (4 * (i - 8));
+  }
+  if (vec < nvec) {
+    packed[(size_t)vec * 8 + sub] = make_uint2(lo, hi);
+    if (sub == 0) norms[vec] = (uint16_t)n16;
+  }
+}
+
+// v_hat = (nn / 128) D H c[idx], float32 out.
+__global__ __launch_bounds__(kThreads) void turbo4_decode_kernel(const uint2* __restrict__ packed,
+                                                                 const uint16_t* __restrict__ norms, uint32_t nvec,
+                                                                 Signs sg, Codebook cb, float* __restrict__ out) {
+  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t vec = tid / kLanesPerVec;
+  const int sub = (int)(tid % kLanesPerVec);
+  const uint32_t vv = min(vec, nvec - 1u);
+  const uint2 p = packed[(size_t)vv * 8 + sub];
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t word = i < 8 ? p.x : p.y;
+    const uint32_t idx = (word >> (4 * (i & 7))) & 15u;
+    float c = cb.c[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) c = idx == (uint32_t)k ? cb.c[k] : c;
+    v[i] = c;
+  }
+  fwht128_group(v, sub);
+  const float scale = f16_bits_to_f32_exact(norms[vv]) * (1.0f / kD);
+  if (vec < nvec) {
+    float4* o = reinterpret_cast<float4*>(out + (size_t)vec * kD + 16 * sub);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * t + j;
+        const float x = v[i] * scale;
+        r[j] = sign_bit(sg, sub, i) ? -x : x;
+      }
+      o[t] = make_float4(r[0], r[1], r[2], r[3]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Decode attention, split over the cache: workgroup (split s, cache head g,
+// sequence b) takes tokens [256 s, 256 s + 256) of sequence b and the G
+// query heads that read cache head g.  The cache is head-major ([B, Hkv,
+// T_max, ...]), so a workgroup streams contiguous key codes (32 KiB), key
+// scales, value nibbles (16 KiB) and norms.  It writes, per head, the running
+// maximum m (log2 domain), the sum l of 2^(s_t - m), and the rotated-domain
+// sum z = sum_t 2^(s_t - m) nn_t c[idx_t] (128 floats) to the workspace.
+// --------------------------------------------------------------------------
+constexpr int kPart = kD + 2;           // floats per (sequence, head, split): m, l, z[128]
+
+template <int G, bool kBf16Q>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(
+    const uint8_t* __restrict__ Q, const int32_t* __restrict__ lengths, const uint4* __restrict__ kcodes,
+    const uint16_t* __restrict__ kscales, const uint32_t* __restrict__ vpacked, const uint16_t* __restrict__ vnorms,
+    uint32_t Tmax, uint32_t Hkv, uint32_t S, Codebook cb, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) int8_t qs[G][kD];       // quantized query
+  __shared__ float dq[G][4];
+  __shared__ float lut[16][32];                                    // centroid k, copy lane % 32
+  __shared__ float sc[G][kChunk];                                  // scores, then 2^(s - m)
+  __shared__ float red[4][G][kD];                                  // per-wavefront z partials
+  __shared__ float stat[G][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int32_t Lraw = lengths[b];
+  const uint32_t L = (uint32_t)min(max(Lraw, 0), (int32_t)Tmax);
+  const uint32_t t0 = s * kChunk;
+  if (t0 >= L) return;                     // the combine reads only the splits that hold tokens
+  const uint32_t n = min((uint32_t)kChunk, L - t0);
+  const uint32_t Hq = Hkv * G;
+  const size_t kv0 = ((size_t)b * Hkv + g) * Tmax + t0;       // cache row of token t0 (head-major rows)
+
+  // Every key and value load of the chunk is issued here, before anything
+  // waits: 8 lanes per token for keys (16 bytes each, 32 tokens per
+  // workgroup pass), 16 lanes per token for values (4 bytes each, 16 tokens
+  // per pass).  Tokens past the chunk re-read its last token and are masked.
+  const int sub = lane & 7, slot = lane >> 4, e16 = lane & 15;
+  uint4 kq[kChunk / 32];
+  uint32_t kscl[kChunk / 32], vb[kChunk / 16], vnr[kChunk / 16];
+#pragma unroll
+  for (int it = 0; it < kChunk / 32; ++it) {
+    const uint32_t tl = min((uint32_t)(it * 32 + wave * 8 + (lane >> 3)), n - 1u);
+    const size_t kv = kv0 + tl;
+    kq[it] = kcodes[kv * 8 + sub];
+    kscl[it] = kscales[kv * 4 + (sub >> 1)];
+  }
+#pragma unroll
+  for (int it = 0; it < kChunk / 16; ++it) {
+    const uint32_t tl = min((uint32_t)(it * 16 + wave * 4 + slot), n - 1u);
+    const size_t kv = kv0 + tl;
+    vb[it] = vpacked[kv * 16 + e16];
+    vnr[it] = vnorms[kv];
+  }
+
+  // Query quantization: thread t < 16 G takes 8 elements of head t / 16;
+  // four threads share a 32-element block.
+  if (tid < 16 * G) {
+    const int h = tid >> 4, e0 = (tid & 15) * 8;
+    const size_t qoff = ((size_t)b * Hq + g * G + h) * kD + e0;
+    float x[8];
+    if constexpr (kBf16Q) {
+      const uint4 u = *reinterpret_cast<const uint4*>(Q + qoff * 2);
+      x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+      x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(Q + qoff * 4);
+      const float4 a = p[0], c = p[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, xor_f(amax, 1));
+    amax = fmaxf(amax, xor_f(amax, 2));
+    const float d = amax / 127.0f;
+    uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c = d > 0.f ? __builtin_rintf(x[i] / d) : 0.f;
+      c = fminf(fmaxf(c, -127.f), 127.f);
+      const uint32_t byte = (uint32_t)(int32_t)c & 0xffu;
+      if (i < 4) w0 |= byte << (8 * i);
+      else w1 |= byte << (8 * (i - 4));
+    }
+    *reinterpret_cast<uint2*>(&qs[h][e0]) = make_uint2(w0, w1);
+    if ((tid & 3) == 0) dq[h][(tid & 15) >> 2] = d;
+  }
+  for (int i = tid; i < 16 * 32; i += kThreads) lut[i >> 5][i & 31] = cb.c[i >> 5];
+  __syncthreads();
+
+  // Scores: 8 lanes per token, 16 key bytes per lane (half a q8_0 block).
+  {
+    const float scale = kLog2e * 0.08838834764831845f;     // log2(e) / sqrt(128), float32
+    uint4 qc[G];
+    float dqs[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      qc[h] = *reinterpret_cast<const uint4*>(&qs[h][16 * sub]);
+      dqs[h] = dq[h][sub >> 1];
+    }
+#pragma unroll
+    for (int it = 0; it < kChunk / 32; ++it) {
+      const uint32_t tl = (uint32_t)(it * 32 + wave * 8 + (lane >> 3));
+      const uint4 kc = kq[it];
+      const float dk = f16_bits_to_f32_exact(kscl[it]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        int isum = __builtin_amdgcn_sdot4((int)kc.x, (int)qc[h].x, 0, false);
+        isum = __builtin_amdgcn_sdot4((int)kc.y, (int)qc[h].y, isum, false);
+        isum = __builtin_amdgcn_sdot4((int)kc.z, (int)qc[h].z, isum, false);
+        isum = __builtin_amdgcn_sdot4((int)kc.w, (int)qc[h].w, isum, false);
+        isum += dpp_xor1(isum);                             // the whole 32-element block
+        float f = (float)isum * (dk * dqs[h]);
+        f = f + dpp_xor2(f);                                 // two blocks
+        f = f + dpp_mirror8(f);                              // all four
+        if (tl < n && sub == 0) sc[h][tl] = f * scale;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Softmax statistics per head: wavefront w takes heads w, w + 4.
+  for (int h = wave; h < G; h += 4) {
+    float m = -__builtin_inff();
+    for (uint32_t i = lane; i < n; i += 64) m = fmaxf(m, sc[h][i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, xor_f(m, o));
+    float l = 0.f;
+    for (uint32_t i = lane; i < n; i += 64) {
+      const float e = __builtin_amdgcn_exp2f(sc[h][i] - m);
+      sc[h][i] = e;
+      l += e;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += xor_f(l, o);
+    if (lane == 0) {
+      stat[h][0] = m;
+      stat[h][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // Values: 4 tokens per wavefront step, 16 lanes per token, 8 elements
+  // (4 bytes of nibbles) per lane.
+  {
+    const int copy = lane & 31;
+    float z[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[h][i] = 0.f;
+#pragma unroll
+    for (int it = 0; it < kChunk / 16; ++it) {
+      const uint32_t tl = (uint32_t)(it * 16 + wave * 4 + slot);
+      if (tl < n) {
+        const uint32_t bits = vb[it];
+        const float nn = f16_bits_to_f32_exact(vnr[it]);
+        float c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = lut[(bits >> (4 * i)) & 15u][copy];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float wgt = sc[h][tl] * nn;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) z[h][i] = __builtin_fmaf(wgt, c[i], z[h][i]);
+        }
+      }
+    }
+    // Sum the four token slots of the wavefront, then the wavefronts.
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = z[h][i];
+        v = v + xor_f(v, 16);
+        v = v + xor_f(v, 32);
+        z[h][i] = v;
+      }
+    if (slot == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float4* r = reinterpret_cast<float4*>(&red[wave][h][8 * e16]);
+        r[0] = make_float4(z[h][0], z[h][1], z[h][2], z[h][3]);
+        r[1] = make_float4(z[h][4], z[h][5], z[h][6], z[h][7]);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * kD; i += kThreads) {
+    const int h = i / kD, e = i % kD;
+    const float v = (red[0][h][e] + red[1][h][e]) + (red[2][h][e] + red[3][h][e]);
+    float* dst = part + (((size_t)b * Hq + g * G + h) * S + s) * kPart;
+    dst[2 + e] = v;
+    if (e == 0) {
+      dst[0] = stat[h][0];
+      dst[1] = stat[h][1];
+    }
+  }
+}
+
+// Combine the splits of (sequence b, head h) and rotate back:
+// o = (1/128) D H (Z / L_total).  Thread i computes output element i.  The
+// split maxima and sums are read by all threads at once (thread t takes
+// splits t, t + 128, ...) and reduced in LDS; the z sums are then read eight
+// splits at a time, so the loads are in flight together.
+__global__ __launch_bounds__(kD) void attn_combine_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ lengths, uint32_t Tmax,
+                                                          uint32_t Hq, uint32_t S, Signs sg, float* __restrict__ out) {
+  __shared__ float zs[kD];
+  __shared__ float red[2][2];
+  const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
+  const uint32_t h = blockIdx.x, b = blockIdx.y;
+  const uint32_t L = (uint32_t)min(max(lengths[b], 0), (int32_t)Tmax);
+  float* o = out + ((size_t)b * Hq + h) * kD;
+  if (L == 0) {
+    o[i] = 0.f;
+    return;
+  }
+  const uint32_t ns = (L + kChunk - 1) / kChunk;
+  const float* p = part + ((size_t)b * Hq + h) * S * kPart;
+  float M = -__builtin_inff();
+  for (uint32_t s = i; s < ns; s += kD) M = fmaxf(M, p[s * kPart]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, xor_f(M, m));
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  float l = 0.f;
+  for (uint32_t s = i; s < ns; s += kD) l += p[s * kPart + 1] * __builtin_amdgcn_exp2f(p[s * kPart] - M);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) l += xor_f(l, m);
+  if (lane == 0) red[1][wave] = l;
+  __syncthreads();
+  l = red[1][0] + red[1][1];
+  float z = 0.f;
+  uint32_t s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float zv[8], mv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      zv[k] = p[(s + k) * kPart + 2 + i];
+      mv[k] = p[(s + k) * kPart];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) z += zv[k] * __builtin_amdgcn_exp2f(mv[k] - M);
+  }
+  for (; s < ns; ++s) z += p[s * kPart + 2 + i] * __builtin_amdgcn_exp2f(p[s * kPart] - M);
+  zs[i] = z / l;
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < kD; ++j) {
+    const float v = zs[j];
+    acc += (__builtin_popcount(i & j) & 1) ? -v : v;
+  }
+  const float r = acc * (1.0f / kD);
+  o[i] = ((sg.w[i >> 5] >> (i & 31)) & 1u) ? -r : r;
+}
+
+inline Signs signs_of(const uint32_t* w) { return Signs{{w[0], w[1], w[2], w[3]}}; }
+inline uint32_t grid_for(uint64_t threads) { return (uint32_t)((threads + kThreads - 1) / kThreads); }
+
+template <bool kBf16Q>
+void launch_split(int G, dim3 grid, const uint8_t* q, const int32_t* len, const uint4* kc, const uint16_t* ks,
+                  const uint32_t* vp, const uint16_t* vn, uint32_t Tmax, uint32_t Hkv, uint32_t S, const Codebook& cb,
+                  float* part, hipStream_t s) {
+#define TQ_SPLIT(GG)                                                                                         \
+  hipLaunchKernelGGL((attn_split_kernel<GG, kBf16Q>), grid, dim3(kThreads), 0, s, q, len, kc, ks, vp, vn, Tmax, \
+                     Hkv, S, cb, part)
+  switch (G) {
+    case 1: TQ_SPLIT(1); break;
+    case 2: TQ_SPLIT(2); break;
+    case 4: TQ_SPLIT(4); break;
+    default: TQ_SPLIT(8); break;
+  }
+#undef TQ_SPLIT
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Tmax) {
+  const int64_t S = (Tmax + kChunk - 1) / kChunk;
+  return (size_t)(B * Hq * S * kPart) * sizeof(float);
+}
+
+hipError_t launch_q8_rows(const void* X, bool bf16, int64_t nblocks, int8_t* codes, uint16_t* scales,
+                          hipStream_t s) {
+  const int64_t per_launch = (int64_t)1 << 30;
+  const uint8_t* x = static_cast<const uint8_t*>(X);
+  for (int64_t b0 = 0; b0 < nblocks; b0 += per_launch) {
+    const uint32_t total = (uint32_t)std::min<int64_t>(nblocks - b0, per_launch);
+    uint4* c = reinterpret_cast<uint4*>(codes) + 2 * b0;
+    if (bf16)
+      hipLaunchKernelGGL(q8_rows_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, s, x + b0 * 64, total, c,
+                         scales + b0);
+    else
+      hipLaunchKernelGGL(q8_rows_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, s, x + b0 * 128, total, c,
+                         scales + b0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_turbo4_encode(const void* V, bool bf16, int64_t nvec, const uint32_t* sign, uint8_t* packed,
+                                uint16_t* norms, hipStream_t s) {
+  const Codebook& cb = host_codebook();
+  const int64_t per_launch = (int64_t)1 << 26;
+  const uint8_t* v = static_cast<const uint8_t*>(V);
+  for (int64_t v0 = 0; v0 < nvec; v0 += per_launch) {
+    const uint32_t cnt = (uint32_t)std::min<int64_t>(nvec - v0, per_launch);
+    const dim3 grid(grid_for((uint64_t)cnt * kLanesPerVec));
+    uint2* p = reinterpret_cast<uint2*>(packed) + v0 * 8;
+    if (bf16)
+      hipLaunchKernelGGL(turbo4_encode_kernel<true>, grid, dim3(kThreads), 0, s, v + v0 * kD * 2, cnt,
+                         signs_of(sign), cb, p, norms + v0);
+    else
+      hipLaunchKernelGGL(turbo4_encode_kernel<false>, grid, dim3(kThreads), 0, s, v + v0 * kD * 4, cnt,
+                         signs_of(sign), cb, p, norms + v0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_turbo4_decode(const uint8_t* packed, const uint16_t* norms, int64_t nvec, const uint32_t* sign,
+                                float* out, hipStream_t s) {
+  const Codebook& cb = host_codebook();
+  const int64_t per_launch = (int64_t)1 << 26;
+  for (int64_t v0 = 0; v0 < nvec; v0 += per_launch) {
+    const uint32_t cnt = (uint32_t)std::min<int64_t>(nvec - v0, per_launch);
+    hipLaunchKernelGGL(turbo4_decode_kernel, dim3(grid_for((uint64_t)cnt * kLanesPerVec)), dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint2*>(packed) + v0 * 8, norms + v0, cnt, signs_of(sign), cb,
+                       out + v0 * kD);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const void* q, bool qbf16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tmax,
+                              const int32_t* lengths, const int8_t* kcodes, const uint16_t* kscales,
+                              const uint8_t* vpacked, const uint16_t* vnorms, const uint32_t* sign, float* o,
+                              void* workspace, hipStream_t s) {
+  const uint32_t S = (uint32_t)((Tmax + kChunk - 1) / kChunk);
+  const int G = (int)(Hq / Hkv);
+  const dim3 grid(S, (uint32_t)Hkv, (uint32_t)B);
+  float* part = static_cast<float*>(workspace);
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  const uint4* kc = reinterpret_cast<const uint4*>(kcodes);
+  const uint32_t* vp = reinterpret_cast<const uint32_t*>(vpacked);
+  const Codebook& cb = host_codebook();
+  if (qbf16)
+    launch_split<true>(G, grid, qb, lengths, kc, kscales, vp, vnorms, (uint32_t)Tmax, (uint32_t)Hkv, S, cb, part, s);
+  else
+    launch_split<false>(G, grid, qb, lengths, kc, kscales, vp, vnorms, (uint32_t)Tmax, (uint32_t)Hkv, S, cb, part,
+                        s);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)Hq, (uint32_t)B), dim3(kD), 0, s, part, lengths,
+                     (uint32_t)Tmax, (uint32_t)Hq, S, signs_of(sign), o);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -39,4 +39,16 @@ hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bsc
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
                                float* y, int64_t ldy, hipStream_t s);
 
+// turbo4 KV cache (tq_kv.hip).
+hipError_t launch_q8_rows(const void* X, bool bf16, int64_t nblocks, int8_t* codes, uint16_t* scales, hipStream_t s);
+hipError_t launch_turbo4_encode(const void* V, bool bf16, int64_t nvec, const uint32_t* sign, uint8_t* packed,
+                                uint16_t* norms, hipStream_t s);
+hipError_t launch_turbo4_decode(const uint8_t* packed, const uint16_t* norms, int64_t nvec, const uint32_t* sign,
+                                float* out, hipStream_t s);
+size_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Tmax);
+hipError_t launch_attn_decode(const void* q, bool qbf16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tmax,
+                              const int32_t* lengths, const int8_t* kcodes, const uint16_t* kscales,
+                              const uint8_t* vpacked, const uint16_t* vnorms, const uint32_t* sign, float* o,
+                              void* workspace, hipStream_t s);
+
 }  // namespace tq

@@ -258,6 +258,77 @@ tq_status tq_transcode_q8(const uint8_t* packed, const uint16_t* scales, int64_t
 tq_status tq_q8_gemv(const int8_t* codes, const uint16_t* q8_scales, int64_t N, int64_t K,
                      const void* x, tq_dtype xt, float* y, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * turbo4 KV cache: q8_0 keys, PolarQuant values, decode attention (TQ4
+ * page: the paragraph after the "格式原理" list, on the reference code's
+ * PolarQuant steps -- norm, structured rotation of random signs and a
+ * Hadamard transform, nearest-centroid index, inverse rotation and rescale;
+ * "叠加压缩：权重 + KV 缓存", where asymmetric q8_0-K / turbo4-V is the best
+ * cache configuration).  Head dimension 128.
+ * ------------------------------------------------------------------------ */
+
+/* [host] The 128 rotation sign bits for a seed: out[w] holds bits 32 w ..
+ * 32 w + 31; bits 0..63 are the first splitmix64 output, 64..127 the
+ * second.  Bit i set flips element i.  Errors: TQ_EINVAL (out NULL). */
+tq_status tq_kv_sign_from_seed(uint64_t seed, uint32_t out[4]);
+
+/* Keys to q8_0: rows K [n, d] (TQ_F32 or TQ_BF16, dense, 16-byte aligned),
+ * per 32-element block scale = fp16(amax / 127) (RNE, saturating), code =
+ * clamp(rint(k / scale), -127, 127) (ties to even).
+ *   codes  int8 [n, d], 16-byte aligned (output).
+ *   scales fp16 bits [n, d/32], 2-byte aligned (output).
+ * Errors: TQ_EINVAL, TQ_ESHAPE (d % 32), TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_kv_quantize_k(const void* K, tq_dtype kt, int64_t n, int64_t d, int8_t* codes,
+                           uint16_t* scales, hipStream_t stream);
+
+/* Values to turbo4: rows V [n, 128] (TQ_F32 or TQ_BF16, 16-byte aligned).
+ * Per vector, float32 in this order: n16 = fp16(sqrt(pairwise sum of
+ * squares)); u = FWHT_128(D v) (unnormalised, stages 1..64); index_i =
+ * number of thresholds fl(nn * m_k) below u_i (m_k the codebook midpoints).
+ *   sign   [host] 4 words from tq_kv_sign_from_seed (the caller's choice).
+ *   packed uint8 [n, 64] (element 2j in the low nibble of byte j), 8-byte
+ *          aligned (output);  norms fp16 bits [n], 2-byte aligned (output).
+ * Bit-exact against that definition.  4.125 bits per element.
+ * Errors: TQ_EINVAL, TQ_ESHAPE (d != 128), TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_kv_quantize_v(const void* V, tq_dtype vt, int64_t n, int64_t d, const uint32_t sign[4],
+                           uint8_t* packed, uint16_t* norms, hipStream_t stream);
+
+/* turbo4 values back to float32: out [n, 128] = (nn / 128) D H c[index]
+ * (16-byte aligned).  Errors as tq_kv_quantize_v. */
+tq_status tq_kv_dequantize_v(const uint8_t* packed, const uint16_t* norms, int64_t n, int64_t d,
+                             const uint32_t sign[4], float* out, hipStream_t stream);
+
+/* Bytes of workspace tq_attn_decode needs: B * Hq * ceil(T_max / 256) *
+ * 130 floats (0 for non-positive arguments). */
+size_t tq_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t T_max);
+
+/* Decode attention for one new token per sequence over the quantized
+ * cache:  o[b, h] = sum_t p_t v_hat[b, t, h / G],  p = softmax over t <
+ * lengths[b] of s_t = q_hat . k_hat[b, t, h / G] / sqrt(128), G = Hq / Hkv.
+ * The query is quantized per 32-element block (scale fl(amax / 127) in
+ * float32, codes as tq_kv_quantize_k) so each key block's dot product is an
+ * exact integer; values are summed in the rotated domain and rotated back
+ * once per head.
+ *   q        [B, Hq, 128] TQ_BF16 or TQ_F32, 16-byte aligned.
+ *   lengths  int32 [B] device, each clamped to [0, T_max] (0 gives o = 0).
+ *   k_codes  int8 [B, Hkv, T_max, 128], k_scales fp16 [B, Hkv, T_max, 4]
+ *            (tq_kv_quantize_k rows in this order: head-major, so the
+ *            tokens of one cache head are contiguous).
+ *   v_packed uint8 [B, Hkv, T_max, 64], v_norms fp16 [B, Hkv, T_max]
+ *            (tq_kv_quantize_v rows in this order).
+ *   sign     [host] the words the values were encoded with.
+ *   o        float32 [B, Hq, 128] (output).
+ *   workspace device, >= tq_attn_workspace_bytes(B, Hq, T_max) bytes; the
+ *            call owns it until the stream reaches the end of the call.
+ * G must be 1, 2, 4 or 8; B, Hq, Hkv <= 65535.
+ * Errors: TQ_EINVAL (null, non-positive sizes, workspace too small),
+ * TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
+tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                         int64_t T_max, const int32_t* lengths, const int8_t* k_codes,
+                         const uint16_t* k_scales, const uint8_t* v_packed, const uint16_t* v_norms,
+                         const uint32_t sign[4], float* o, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

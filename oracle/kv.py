@@ -145,8 +145,8 @@ def score_scale(d: int) -> float:
 def attn_decode_o64(q, lengths, k_codes, k_scales, v_packed, v_norms, words=None, centroids32=None):
     """Decode attention over the quantized cache, float64.
 
-    q [B, Hq, 128]; lengths [B]; k_codes int8 [B, T, Hkv, 128]; k_scales fp16 bits [B, T, Hkv, 4];
-    v_packed uint8 [B, T, Hkv, 64]; v_norms fp16 bits [B, T, Hkv].
+    q [B, Hq, 128]; lengths [B]; head-major cache: k_codes int8 [B, Hkv, T, 128]; k_scales fp16 bits
+    [B, Hkv, T, 4]; v_packed uint8 [B, Hkv, T, 64]; v_norms fp16 bits [B, Hkv, T].
     Returns (o [B, Hq, 128], bound [B, Hq]) where bound = sum_t p_t (nn_t / d) sum_j |c[idx_tj]|, the
     largest magnitude any output coordinate's terms can reach (the parity bound is stated against it).
     """
@@ -154,7 +154,7 @@ def attn_decode_o64(q, lengths, k_codes, k_scales, v_packed, v_norms, words=None
     c32 = codebook.tq4_codebook_f32() if centroids32 is None else np.asarray(centroids32, np.float32)
     qa = np.asarray(q, dtype=np.float32)
     B, Hq, d = qa.shape
-    _, T, Hkv, _ = k_codes.shape
+    _, Hkv, T, _ = k_codes.shape
     G = Hq // Hkv
     nb = d // BLOCK
     o = np.zeros((B, Hq, d))
@@ -166,15 +166,15 @@ def attn_decode_o64(q, lengths, k_codes, k_scales, v_packed, v_norms, words=None
         for h in range(Hq):
             g = h // G
             qc, dq = quantize_act_q8(qa[b, h])                            # [128], [4]
-            kc = k_codes[b, :L, g].astype(np.int64).reshape(L, nb, BLOCK)
-            dk = fp16_bits_to_f32(k_scales[b, :L, g]).astype(np.float64)   # [L, 4]
+            kc = k_codes[b, g, :L].astype(np.int64).reshape(L, nb, BLOCK)
+            dk = fp16_bits_to_f32(k_scales[b, g, :L]).astype(np.float64)   # [L, 4]
             isum = (kc * qc.astype(np.int64).reshape(1, nb, BLOCK)).sum(axis=-1)
             s = (dk * dq.astype(np.float64)[None, :] * isum).sum(axis=1) * score_scale(d)
             p = np.exp(s - s.max())
             p /= p.sum()
-            vh = turbo4_dequantize_o64(v_packed[b, :L, g], v_norms[b, :L, g], words, c32)
+            vh = turbo4_dequantize_o64(v_packed[b, g, :L], v_norms[b, g, :L], words, c32)
             o[b, h] = p @ vh
-            nn = fp16_bits_to_f32(v_norms[b, :L, g]).astype(np.float64)
-            cabs = np.abs(c32.astype(np.float64)[turbo4_indices(v_packed[b, :L, g])]).sum(axis=1)
+            nn = fp16_bits_to_f32(v_norms[b, g, :L]).astype(np.float64)
+            cabs = np.abs(c32.astype(np.float64)[turbo4_indices(v_packed[b, g, :L])]).sum(axis=1)
             bound[b, h] = (p * nn / d * cabs).sum()
     return o, bound

@@ -55,6 +55,13 @@ def test_sign_mask_matches_oracle_splitmix():
     assert tqa.default_sign_mask() == otq.DEFAULT_SIGN_MASK == tqa.DEFAULT_SIGN_MASK
 
 
+def test_kv_sign_words_match_oracle_splitmix():
+    from oracle import kv as okv
+    for seed in (0, 3, 2 ** 64 - 1):
+        assert list(tqa.kv_sign_from_seed(seed)) == okv.kv_sign_words(seed)
+    assert tqa.lib().tq_kv_sign_from_seed(0, None) == EINVAL
+
+
 def _p(v):
     return ctypes.c_void_p(v)
 
@@ -129,6 +136,29 @@ def test_other_calls_reject_before_launch():
     assert L.tq_q8_gemv(g, g, 8, 32768 + 32, g, F32, g, None) == ESHAPE
     assert L.tq_q8_gemv(g, g, 8, 64, g, F16, g, None) == EDTYPE
     assert L.tq_q8_gemv(g, g, 8, 64, _p(GOOD + 8), BF16, g, None) == EALIGN      # x: 16 B
+    # turbo4 KV cache and decode attention
+    sg = tqa.kv_sign_from_seed(0)
+    assert L.tq_kv_quantize_k(g, F32, 0, 128, g, g, None) == EINVAL
+    assert L.tq_kv_quantize_k(g, F32, 4, 100, g, g, None) == ESHAPE
+    assert L.tq_kv_quantize_k(g, F16, 4, 128, g, g, None) == EDTYPE
+    assert L.tq_kv_quantize_k(g, F32, 4, 128, _p(GOOD + 8), g, None) == EALIGN    # codes: 16 B
+    assert L.tq_kv_quantize_v(g, F32, 4, 128, None, g, g, None) == EINVAL        # sign words
+    assert L.tq_kv_quantize_v(g, F32, 4, 64, sg, g, g, None) == ESHAPE           # head dim 128 only
+    assert L.tq_kv_quantize_v(g, BF16, 4, 128, sg, _p(GOOD + 4), g, None) == EALIGN   # packed: 8 B
+    assert L.tq_kv_dequantize_v(g, g, 4, 128, sg, _p(GOOD + 4), None) == EALIGN       # out: 16 B
+    assert L.tq_attn_workspace_bytes(2, 32, 1000) == 2 * 32 * 4 * 130 * 4
+    assert L.tq_attn_workspace_bytes(0, 32, 1000) == 0
+    ws = L.tq_attn_workspace_bytes(1, 32, 512)
+    args = lambda **kw: [kw.get("q", g), kw.get("qt", BF16), kw.get("B", 1), kw.get("Hq", 32), kw.get("Hkv", 8),
+                         kw.get("d", 128), kw.get("T", 512), g, g, g, g, g, sg, g, kw.get("ws", g),
+                         kw.get("wsb", ws), None]
+    assert L.tq_attn_decode(*args(Hq=12)) == ESHAPE                  # Hq % Hkv
+    assert L.tq_attn_decode(*args(Hq=128, Hkv=8)) == ESHAPE          # G = 16
+    assert L.tq_attn_decode(*args(d=64)) == ESHAPE
+    assert L.tq_attn_decode(*args(wsb=ws - 4)) == EINVAL             # workspace too small
+    assert L.tq_attn_decode(*args(T=0)) == EINVAL
+    assert L.tq_attn_decode(*args(qt=F16)) == EDTYPE
+    assert L.tq_attn_decode(*args(q=_p(GOOD + 8))) == EALIGN
 
 
 def test_binding_refuses_cpu_tensors():

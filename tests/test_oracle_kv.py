@@ -100,18 +100,18 @@ def test_q8_0_keys():
 
 def _cache(B, T, Hkv, seed):
     rng = np.random.default_rng(seed)
-    K = rng.standard_normal((B, T, Hkv, D)).astype(np.float32)
-    V = rng.standard_normal((B, T, Hkv, D)).astype(np.float32)
+    K = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
     kc, ks = kv.q8_0_quantize_o32(K.reshape(-1, D))
     vp, vn = kv.turbo4_quantize_o32(V.reshape(-1, D))
-    return (kc.reshape(B, T, Hkv, D), ks.reshape(B, T, Hkv, D // 32), vp.reshape(B, T, Hkv, D // 2),
-            vn.reshape(B, T, Hkv))
+    return (kc.reshape(B, Hkv, T, D), ks.reshape(B, Hkv, T, D // 32), vp.reshape(B, Hkv, T, D // 2),
+            vn.reshape(B, Hkv, T))
 
 
 def _attn_loops(q, lengths, kc, ks, vp, vn):
     """The definition with explicit loops (float64, math.exp)."""
     B, Hq, _ = q.shape
-    Hkv = kc.shape[2]
+    Hkv = kc.shape[1]
     G = Hq // Hkv
     o = np.zeros((B, Hq, D))
     for b in range(B):
@@ -125,12 +125,12 @@ def _attn_loops(q, lengths, kc, ks, vp, vn):
                 for blk in range(D // 32):
                     isum = 0
                     for i in range(32):
-                        isum += int(qc[32 * blk + i]) * int(kc[b, t, g, 32 * blk + i])
-                    tot += float(dq[blk]) * float(tq.fp16_bits_to_f32(ks[b, t, g, blk:blk + 1])[0]) * isum
+                        isum += int(qc[32 * blk + i]) * int(kc[b, g, t, 32 * blk + i])
+                    tot += float(dq[blk]) * float(tq.fp16_bits_to_f32(ks[b, g, t, blk:blk + 1])[0]) * isum
                 s.append(tot / math.sqrt(D))
             mx = max(s)
             e = [math.exp(x - mx) for x in s]
-            vh = kv.turbo4_dequantize_o64(vp[b, :L, g], vn[b, :L, g])
+            vh = kv.turbo4_dequantize_o64(vp[b, g, :L], vn[b, g, :L])
             for t in range(L):
                 o[b, h] += e[t] / sum(e) * vh[t]
     return o
@@ -150,20 +150,20 @@ def test_attention_closed_forms():
     B, T, Hq, Hkv = 1, 9, 8, 2
     kc, ks, vp, vn = _cache(B, T, Hkv, 7)
     q = np.random.default_rng(8).standard_normal((B, Hq, D)).astype(np.float32)
-    vh = kv.turbo4_dequantize_o64(vp.reshape(-1, D // 2), vn.reshape(-1)).reshape(B, T, Hkv, D)
+    vh = kv.turbo4_dequantize_o64(vp.reshape(-1, D // 2), vn.reshape(-1)).reshape(B, Hkv, T, D)
     # one cached token: the output is its value vector
     o, _ = kv.attn_decode_o64(q, np.array([1]), kc, ks, vp, vn)
     for h in range(Hq):
-        np.testing.assert_allclose(o[0, h], vh[0, 0, h // 4], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(o[0, h], vh[0, h // 4, 0], rtol=0, atol=1e-12)
     # a zero query: equal scores, the mean of the values
     o, _ = kv.attn_decode_o64(np.zeros_like(q), np.array([T]), kc, ks, vp, vn)
     for h in range(Hq):
-        np.testing.assert_allclose(o[0, h], vh[0, :, h // 4].mean(0), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(o[0, h], vh[0, h // 4, :].mean(0), rtol=0, atol=1e-12)
     # tokens past the length are ignored
     o1, _ = kv.attn_decode_o64(q, np.array([5]), kc, ks, vp, vn)
     kc2, ks2, vp2, vn2 = kc.copy(), ks.copy(), vp.copy(), vn.copy()
-    kc2[:, 5:] = 99
-    vp2[:, 5:] = 0xAB
+    kc2[:, :, 5:] = 99
+    vp2[:, :, 5:] = 0xAB
     o2, _ = kv.attn_decode_o64(q, np.array([5]), kc2, ks2, vp2, vn2)
     assert np.array_equal(o1, o2)
     # a zero length gives zeros
@@ -191,13 +191,13 @@ def test_mistake_wrong_head_mapping_is_caught(monkeypatch):
 
     def wrong(q, lengths, kc, ks, vp, vn, words=None, c=None):
         # cache head h % Hkv instead of h // G
-        Hq, Hkv = q.shape[1], kc.shape[2]
+        Hq, Hkv = q.shape[1], kc.shape[1]
         perm = np.array([h % Hkv for h in range(Hq)])
         o = np.zeros((q.shape[0], Hq, D))
         bd = np.zeros((q.shape[0], Hq))
         for h in range(Hq):
-            oo, bb = real(q[:, h:h + 1], lengths, kc[:, :, perm[h]:perm[h] + 1], ks[:, :, perm[h]:perm[h] + 1],
-                          vp[:, :, perm[h]:perm[h] + 1], vn[:, :, perm[h]:perm[h] + 1], words, c)
+            oo, bb = real(q[:, h:h + 1], lengths, kc[:, perm[h]:perm[h] + 1], ks[:, perm[h]:perm[h] + 1],
+                          vp[:, perm[h]:perm[h] + 1], vn[:, perm[h]:perm[h] + 1], words, c)
             o[:, h], bd[:, h] = oo[:, 0], bb[:, 0]
         return o, bd
 
