@@ -259,10 +259,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   const uint32_t Hq = Hkv * G;
   const size_t kv0 = ((size_t)b * Hkv + g) * Tmax + t0;       // cache row of token t0 (head-major rows)
 
-  // Every key and value load of the chunk is issued here, before anything
-  // waits: 8 lanes per token for keys (16 bytes each, 32 tokens per
-  // workgroup pass), 16 lanes per token for values (4 bytes each, 16 tokens
-  // per pass).  Tokens past the chunk re-read its last token and are masked.
+  // Every key load of the chunk is issued here, before anything waits (8
+  // lanes per token, 16 bytes each, 32 tokens per workgroup pass); the
+  // value loads (16 lanes per token, 4 bytes each, 16 tokens per pass) are
+  // issued after the scores, so their registers are not held through the
+  // score phase and they arrive during the softmax.  Tokens past the chunk
+  // re-read its last token and are masked.
   const int sub = lane & 7, slot = lane >> 4, e16 = lane & 15;
   uint4 kq[kChunk / 32];
   uint32_t kscl[kChunk / 32], vb[kChunk / 16], vnr[kChunk / 16];
@@ -273,13 +275,15 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     kq[it] = kcodes[kv * 8 + sub];
     kscl[it] = kscales[kv * 4 + (sub >> 1)];
   }
+  auto load_values = [&]() {
 #pragma unroll
-  for (int it = 0; it < kChunk / 16; ++it) {
-    const uint32_t tl = min((uint32_t)(it * 16 + wave * 4 + slot), n - 1u);
-    const size_t kv = kv0 + tl;
-    vb[it] = vpacked[kv * 16 + e16];
-    vnr[it] = vnorms[kv];
-  }
+    for (int it = 0; it < kChunk / 16; ++it) {
+      const uint32_t tl = min((uint32_t)(it * 16 + wave * 4 + slot), n - 1u);
+      const size_t kv = kv0 + tl;
+      vb[it] = vpacked[kv * 16 + e16];
+      vnr[it] = vnorms[kv];
+    }
+  };
 
   // Query quantization: thread t < 16 G takes 8 elements of head t / 16;
   // four threads share a 32-element block.
@@ -347,6 +351,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     }
   }
   __syncthreads();
+
+  load_values();                           // in flight during the softmax statistics
 
   // Softmax statistics per head: wavefront w takes heads w, w + 4.
   for (int h = wave; h < G; h += 4) {
