@@ -26,7 +26,7 @@ tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; 
 tq_status check_weights(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K) {
   if (!packed || !scales) return TQ_EINVAL;
   if (N <= 0 || K <= 0) return TQ_EINVAL;
-  if (K % tq::kBlock) return TQ_ESHAPE;
+  if (K % tq::kBlock || K > ((int64_t)1 << 31)) return TQ_ESHAPE;
   if (!aligned(packed, 16) || !aligned(scales, 4)) return TQ_EALIGN;
   return TQ_OK;
 }

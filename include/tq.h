@@ -106,7 +106,7 @@ uint32_t tq_default_sign_mask(void);
  * nearest even and saturated at 65504; index = number of thresholds
  * float32(d_h * m_k) the rotated value exceeds.  The float32 operation order
  * is fixed (see the oracle), so the output is bit-reproducible.
- * Errors: TQ_EINVAL (null, N or K <= 0, ldw < K), TQ_ESHAPE (K % 32),
+ * Errors: TQ_EINVAL (null, N or K <= 0, ldw < K), TQ_ESHAPE (K % 32, K > 2^31),
  * TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_quantize(const void* W, tq_dtype wt, int64_t N, int64_t K, int64_t ldw,
                       uint32_t sign_mask, uint8_t* packed, uint16_t* scales,

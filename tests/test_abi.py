@@ -136,6 +136,7 @@ def test_other_calls_reject_before_launch():
     assert L.tq_q8_gemv(g, g, 8, 32768 + 32, g, F32, g, None) == ESHAPE
     assert L.tq_q8_gemv(g, g, 8, 64, g, F16, g, None) == EDTYPE
     assert L.tq_q8_gemv(g, g, 8, 64, _p(GOOD + 8), BF16, g, None) == EALIGN      # x: 16 B
+    assert L.tq_quantize(g, F32, 1, (1 << 31) + 32, (1 << 31) + 32, 0, g, g, None) == ESHAPE   # K <= 2^31
     # turbo4 KV cache and decode attention
     sg = tqa.kv_sign_from_seed(0)
     assert L.tq_kv_quantize_k(g, F32, 0, 128, g, g, None) == EINVAL
