@@ -266,22 +266,46 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   // score phase and they arrive during the softmax.  Tokens past the chunk
   // re-read its last token and are masked.
   const int sub = lane & 7, slot = lane >> 4, e16 = lane & 15;
+  // Chunk base pointers (wavefront-uniform) and 32-bit lane offsets; a full
+  // chunk (the common case) needs no clamping.
+  const uint4* kb = kcodes + kv0 * 8;
+  const uint16_t* ksb = kscales + kv0 * 4;
+  const uint32_t* vbp = vpacked + kv0 * 16;
+  const uint16_t* vnb = vnorms + kv0;
+  const bool full = n == (uint32_t)kChunk;
+  const uint32_t ck = (uint32_t)(wave * 8 + (lane >> 3)), cv = (uint32_t)(wave * 4 + slot);
   uint4 kq[kChunk / 32];
   uint32_t kscl[kChunk / 32], vb[kChunk / 16], vnr[kChunk / 16];
+  if (full) {
 #pragma unroll
-  for (int it = 0; it < kChunk / 32; ++it) {
-    const uint32_t tl = min((uint32_t)(it * 32 + wave * 8 + (lane >> 3)), n - 1u);
-    const size_t kv = kv0 + tl;
-    kq[it] = kcodes[kv * 8 + sub];
-    kscl[it] = kscales[kv * 4 + (sub >> 1)];
+    for (int it = 0; it < kChunk / 32; ++it) {
+      const uint32_t tl = (uint32_t)(it * 32) + ck;
+      kq[it] = kb[tl * 8 + sub];
+      kscl[it] = ksb[tl * 4 + (sub >> 1)];
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kChunk / 32; ++it) {
+      const uint32_t tl = min((uint32_t)(it * 32) + ck, n - 1u);
+      kq[it] = kb[tl * 8 + sub];
+      kscl[it] = ksb[tl * 4 + (sub >> 1)];
+    }
   }
   auto load_values = [&]() {
+    if (full) {
 #pragma unroll
-    for (int it = 0; it < kChunk / 16; ++it) {
-      const uint32_t tl = min((uint32_t)(it * 16 + wave * 4 + slot), n - 1u);
-      const size_t kv = kv0 + tl;
-      vb[it] = vpacked[kv * 16 + e16];
-      vnr[it] = vnorms[kv];
+      for (int it = 0; it < kChunk / 16; ++it) {
+        const uint32_t tl = (uint32_t)(it * 16) + cv;
+        vb[it] = vbp[tl * 16 + e16];
+        vnr[it] = vnb[tl];
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < kChunk / 16; ++it) {
+        const uint32_t tl = min((uint32_t)(it * 16) + cv, n - 1u);
+        vb[it] = vbp[tl * 16 + e16];
+        vnr[it] = vnb[tl];
+      }
     }
   };
 
@@ -306,10 +330,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     amax = fmaxf(amax, xor_f(amax, 1));
     amax = fmaxf(amax, xor_f(amax, 2));
     const float d = amax / 127.0f;
+    const float dsafe = d > 0.f ? d : 1.0f;                 // the division runs unconditionally (no branch)
     uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float c = d > 0.f ? __builtin_rintf(x[i] / d) : 0.f;
+      float c = d > 0.f ? __builtin_rintf(x[i] / dsafe) : 0.f;
       c = fminf(fmaxf(c, -127.f), 127.f);
       const uint32_t byte = (uint32_t)(int32_t)c & 0xffu;
       if (i < 4) w0 |= byte << (8 * i);
@@ -335,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     for (int it = 0; it < kChunk / 32; ++it) {
       const uint32_t tl = (uint32_t)(it * 32 + wave * 8 + (lane >> 3));
       const uint4 kc = kq[it];
-      const float dk = f16_bits_to_f32_exact(kscl[it]);
+      const float dk = f16_bits_to_f32(kscl[it]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         int isum = __builtin_amdgcn_sdot4((int)kc.x, (int)qc[h].x, 0, false);
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
         float f = (float)isum * (dk * dqs[h]);
         f = f + dpp_xor2(f);                                 // two blocks
         f = f + dpp_mirror8(f);                              // all four
-        if (tl < n && sub == 0) sc[h][tl] = f * scale;
+        sc[h][tl] = f * scale;               // the token's 8 lanes store the same value; entries past n are unused
       }
     }
   }
@@ -357,12 +382,18 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   // Softmax statistics per head: wavefront w takes heads w, w + 4.
   for (int h = wave; h < G; h += 4) {
     float m = -__builtin_inff();
-    for (uint32_t i = lane; i < n; i += 64) m = fmaxf(m, sc[h][i]);
+#pragma unroll
+    for (int k = 0; k < kChunk / 64; ++k) {
+      const uint32_t i = (uint32_t)(lane + 64 * k);
+      m = fmaxf(m, i < n ? sc[h][i] : -__builtin_inff());
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, xor_f(m, o));
     float l = 0.f;
-    for (uint32_t i = lane; i < n; i += 64) {
-      const float e = __builtin_amdgcn_exp2f(sc[h][i] - m);
+#pragma unroll
+    for (int k = 0; k < kChunk / 64; ++k) {
+      const uint32_t i = (uint32_t)(lane + 64 * k);
+      const float e = i < n ? __builtin_amdgcn_exp2f(sc[h][i] - m) : 0.f;
       sc[h][i] = e;
       l += e;
     }
@@ -384,21 +415,23 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < 8; ++i) z[h][i] = 0.f;
+    // Branch-free: a token past the chunk reads the chunk's last score and
+    // gets weight 0, so the compiler can schedule the lookups of later steps
+    // early (a branch per step left every step's LDS latency exposed).
 #pragma unroll
     for (int it = 0; it < kChunk / 16; ++it) {
       const uint32_t tl = (uint32_t)(it * 16 + wave * 4 + slot);
-      if (tl < n) {
-        const uint32_t bits = vb[it];
-        const float nn = f16_bits_to_f32_exact(vnr[it]);
-        float c[8];
+      const uint32_t tc = min(tl, n - 1u);
+      const uint32_t bits = vb[it];
+      const float nn = tl < n ? f16_bits_to_f32(vnr[it]) : 0.f;
+      float c[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = lut[(bits >> (4 * i)) & 15u][copy];
+      for (int i = 0; i < 8; ++i) c[i] = lut[__builtin_amdgcn_ubfe(bits, 4 * i, 4)][copy];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float wgt = sc[h][tl] * nn;
+      for (int h = 0; h < G; ++h) {
+        const float wgt = sc[h][tc] * nn;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) z[h][i] = __builtin_fmaf(wgt, c[i], z[h][i]);
-        }
+        for (int i = 0; i < 8; ++i) z[h][i] = __builtin_fmaf(wgt, c[i], z[h][i]);
       }
     }
     // Sum the four token slots of the wavefront, then the wavefronts.
