@@ -12,6 +12,8 @@ MFMA utilisation of the small-batch GEMM:
     rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d OUT/mfma -o mfma -- python3 -m dequant_gemv_tq_amd.profiling gemm_run
     python3 -m dequant_gemv_tq_amd.profiling gemm_summarize OUT/mfma/mfma_results.db > profiles/...md
 
+HBM traffic of the turbo4 KV-cache decode attention (``kv_run`` / ``kv_summarize``, same pattern).
+
 Kernel durations of a benchmark run:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- \\
@@ -225,6 +227,98 @@ def summarize(fetch_db: str, write_db: str) -> None:
     print("\n".join(lines))
 
 
+# turbo4 KV-cache decode attention: the Llama-3-8B head layout, 16 sequences x 4096 cached tokens, four layers
+# with distinct caches (424 MB together, more than the 256 MB Infinity Cache).
+KV_LAYOUT = {"batch": 16, "context": 4096, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "layers": 4}
+KV_BYTES_PER_TOKEN_HEAD = 128 + 8 + 64 + 2
+
+
+def kv_run() -> None:
+    sys.path.insert(0, ROOT)
+    import torch
+    import dequant_gemv_tq_amd as tqa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+    L = KV_LAYOUT
+    B, T, Hq, Hkv, D = L["batch"], L["context"], L["q_heads"], L["kv_heads"], L["head_dim"]
+    caches = []
+    for layer in range(L["layers"]):
+        g = wl.generator(wl.seed_of(6, layer, 0), dev)
+        K = torch.randn((B, Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
+        V = torch.randn((B, Hkv, T, D), generator=g, device=dev).to(torch.bfloat16)
+        caches.append(tqa.kv_quantize_k(K) + tqa.kv_quantize_v(V))
+        del K, V
+    torch.cuda.empty_cache()
+    q = torch.randn((B, Hq, D), generator=wl.generator(wl.seed_of(6, 99, 1), dev), device=dev).to(torch.bfloat16)
+    lengths = torch.full((B,), T, dtype=torch.int32, device=dev)
+    o = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(tqa.attn_workspace_bytes(B, Hq, T), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for kc, ks, vp, vn in caches:
+        tqa.attn_decode(q, lengths, kc, ks, vp, vn, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    print("kv traffic run done", flush=True)
+
+
+def kv_summarize(fetch_db: str, write_db: str) -> None:
+    def split(rows):
+        copies = [v for _, name, v in rows if "neg_kernel" in name]
+        att = [(name, v) for _, name, v in rows if "attn_" in name]
+        sp = [v for name, v in att if "attn_split_kernel" in name]
+        cb = [v for name, v in att if "attn_combine_kernel" in name]
+        if not copies or len(sp) != KV_LAYOUT["layers"] or len(cb) != KV_LAYOUT["layers"]:
+            raise RuntimeError("unexpected dispatches in the KV counter run")
+        return statistics.median(copies), statistics.median(sp), statistics.median(cb)
+
+    fc, fs, fcb = split(_per_dispatch(fetch_db, "FETCH_SIZE"))
+    wc, ws, wcb = split(_per_dispatch(write_db, "WRITE_SIZE"))
+    kib = COPY_BYTES / 1024
+    f_scale, w_scale = kib / fc, kib / wc
+    L = KV_LAYOUT
+    B, T, Hq, Hkv, D = L["batch"], L["context"], L["q_heads"], L["kv_heads"], L["head_dim"]
+    cache = B * T * Hkv * KV_BYTES_PER_TOKEN_HEAD
+    alg = cache + B * Hq * D * (2 + 4)
+    splits = (T + 255) // 256
+    partials = B * Hq * splits * (D + 2) * 4
+    t_split = (fs * f_scale + ws * w_scale) * 1024
+    t_comb = (fcb * f_scale + wcb * w_scale) * 1024
+    lines = [
+        "# turbo4 KV-cache decode attention: HBM traffic (Llama-3-8B heads, 16 sequences x 4096 tokens)",
+        "",
+        "Commands (repository root on the GPU host; OUT is any scratch folder):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE -d OUT/kvf -o kvf -- python3 -m dequant_gemv_tq_amd.profiling kv_run",
+        "rocprofv3 --pmc WRITE_SIZE -d OUT/kvw -o kvw -- python3 -m dequant_gemv_tq_amd.profiling kv_run",
+        "python3 -m dequant_gemv_tq_amd.profiling kv_summarize OUT/kvf/kvf_results.db OUT/kvw/kvw_results.db",
+        "```",
+        "",
+        f"Calibration as for the GEMV: a 1 GiB elementwise copy reads FETCH_SIZE = {fc:.0f} KiB and WRITE_SIZE = "
+        f"{wc:.0f} KiB; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).",
+        "",
+        "| kernel (per layer, median of 4) | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB (scaled) |",
+        "|---|---|---|---|",
+        f"| `attn_split_kernel<4, bf16 q>` | {fs:.0f} | {ws:.0f} | {t_split / 1e6:.2f} |",
+        f"| `attn_combine_kernel` | {fcb:.0f} | {wcb:.0f} | {t_comb / 1e6:.2f} |",
+        "",
+        f"Algorithmic bytes per layer: the quantized cache {cache / 1e6:.2f} MB ({KV_BYTES_PER_TOKEN_HEAD} B per token "
+        f"and cache head) plus q and o, {alg / 1e6:.2f} MB; the split partials (m, l, z per sequence, head and "
+        f"256-token split) add {partials / 1e6:.2f} MB written and read back by design.  Measured / algorithmic: "
+        f"{(t_split + t_comb) / alg:.3f} (split + combine), {(t_split + t_comb) / (alg + 2 * partials):.3f} with the "
+        "partials counted.",
+        "",
+    ]
+    print("\n".join(lines))
+
+
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- "
                  "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline")
 
@@ -292,6 +386,10 @@ if __name__ == "__main__":
         gemm_run()
     elif len(sys.argv) == 3 and sys.argv[1] == "gemm_summarize":
         gemm_summarize(sys.argv[2])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "kv_run":
+        kv_run()
+    elif len(sys.argv) == 4 and sys.argv[1] == "kv_summarize":
+        kv_summarize(sys.argv[2], sys.argv[3])
     else:
         print(__doc__)
         sys.exit(2)
