@@ -534,10 +534,32 @@ def cpu_baseline(model, groups, seconds):
         done_bytes += gemv_bytes(rows, k)
         it += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    # The same GEMV on one thread, and the float32 quantizer, on short samples.
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        st_bytes = st_time = 0.0
+        j = 0
+        while st_time < max(2.0, seconds / 6):
+            pk, sc, x, k = samples[j % len(samples)]
+            t = time.perf_counter()
+            otq.gemv_rows_o64(pk, sc, x)
+            st_time += time.perf_counter() - t
+            st_bytes += gemv_bytes(rows, k)
+            j += 1
+    Wq = np.random.default_rng(7).standard_normal((rows, 4096)).astype(np.float32) * np.float32(4096 ** -0.5)
+    q_time = q_weights = 0.0
+    while q_time < 2.0:
+        t = time.perf_counter()
+        otq.quantize_o32(Wq)
+        q_time += time.perf_counter() - t
+        q_weights += Wq.size
     return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{it} oracle float64 GEMV calls on {rows}-row slices of the 8B decode groups "
                       f"(q|k|v, o, gate|up, down; {elapsed:.1f} s of oracle time)",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "single_thread_GB_s": round(st_bytes / st_time / 1e9, 4),
+            "quantize_GB_s": round(q_weights * (4 + WEIGHT_BYTES_PER_ELEM) / q_time / 1e9, 4),
+            "quantize_sample": f"oracle float32 quantizer on a {rows} x 4096 float32 matrix, {q_time:.1f} s"}
 
 
 if __name__ == "__main__":
