@@ -49,7 +49,6 @@ __device__ __forceinline__ float dpp_mirror8(float v) {
 
 // Float32 value shuffled from lane ^ m (within the wavefront).
 __device__ __forceinline__ float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
-__device__ __forceinline__ int xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
 // Elements 16 l .. 16 l + 15 of a vector held by lane l of an 8-lane group:
 // the unnormalised FWHT_128 in the oracle's stage order (in-lane stages h =

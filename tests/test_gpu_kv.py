@@ -99,7 +99,7 @@ def _cache(B, T, Hkv, seed, dtype=torch.bfloat16):
     return kc, ks, vp, vn
 
 
-def _check_attn(q, lengths, cache, label, heads=None):
+def _check_attn(q, lengths, cache, label):
     kc, ks, vp, vn = cache
     say(f"[attn] {label} q={tuple(q.shape)} {q.dtype} lengths={lengths.tolist()} T_max={kc.shape[2]}")
     o = tqa.attn_decode(q, lengths, kc, ks, vp, vn)
