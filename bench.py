@@ -89,6 +89,10 @@ def main():
         model.append({gname: (torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
                               torch.empty((n, k // 16), dtype=torch.int16, device=dev))
                       for gname, (n, k) in groups.items()})
+    # One untimed call of each quantizer variant first, so that loading the
+    # kernels' code objects stays out of the timed region.
+    tqa.quantize(src[0]["o"], out=model[0]["o"])
+    tqa.quantize(src[0]["o"], out=model[0]["o"], rsf=True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -371,6 +375,14 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers):
             fmt = wl.qwen27b_format(layer, t)
             fmt_count[fmt] += 1
             src.append((fmt, wl.qwen27b_weight(t, layer, dev)))
+    # An untimed pass first: it loads the kernels and leaves the outputs'
+    # blocks in torch's caching allocator, so the timed passes allocate nothing.
+    warm = [tqa.blockfp_quantize(fmt, W) for fmt, W in src]
+    for fmt in fmt_count:
+        first = next((W for f, W in src if f == fmt), None)
+        if first is not None:
+            warm.append(tqa.blockfp_quantize(fmt, first, rsf=True))
+    del warm
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)                                    # all tensors back to back between two events

@@ -29,25 +29,52 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Index of the nearest centroid: #{k in 0..14 : w > U_k} with U_k = fl(dd * m_k).
-// The thresholds are antisymmetric (U_k = -U_{14-k}, U_7 = +0), so only the
-// seven positive ones are kept.  For w > 0 the count is 8 + #{r : |w| > U_{8+r}};
-// for w <= 0 it is 7 - #{r : |w| >= U_{8+r}}.  Non-negative floats order like
-// their bit patterns, and |w| >= U  <=>  bits(|w|) + 1 > bits(U), so both
-// cases become one unsigned 3-level binary search over U_8..U_14.
-__device__ __forceinline__ uint32_t nearest_index(float w, const uint32_t (&U)[7]) {
-  uint32_t bits = __float_as_uint(w);
-  bool pos = (int32_t)bits > 0;                      // strictly positive (subnormals too)
-  uint32_t key = (bits & 0x7fffffffu) + (pos ? 0u : 1u);
-  bool c2 = key > U[3];
-  uint32_t t1 = c2 ? U[5] : U[1];
-  bool c1 = key > t1;
-  uint32_t ta = c2 ? U[4] : U[0];
-  uint32_t tb = c2 ? U[6] : U[2];
-  bool c0 = key > (c1 ? tb : ta);
-  uint32_t j = (c2 ? 4u : 0u) | (c1 ? 2u : 0u) | (c0 ? 1u : 0u);
-  return pos ? 8u + j : 7u - j;
+// Index of the nearest centroid, idx = #{k in 0..14 : w > fl(dd * m_k)}.
+//
+// A table of 42 cells over the normalised value t = w / dd replaces a
+// comparison tree: cell c covers t in [(c - 21) / 8, (c - 20) / 8) (cell 0
+// and cell 41 are open towards -inf and +inf).  Adjacent thresholds are at
+// least 0.25 apart, so a cell holds at most one of them; the entry keeps
+// how many thresholds lie below the cell and the next threshold at or above
+// its lower edge (+inf past the last).  The index is then that count plus
+// one exact float32 comparison of w with fl(dd * next), the same comparison
+// the definition makes.  The cell itself only needs to be found
+// approximately: every threshold other than m_7 = 0 sits at least 0.008
+// from a cell edge, and m_7 is the "next" threshold of both cells that meet
+// at 0, so a value that falls into a neighbouring cell through rounding of
+// w * (8 / dd) still gets the same index.  dd = 0 makes 8 / dd = +inf: a
+// nonzero w goes to an end cell, and w = +-0 gives NaN, which the clamp
+// sends to cell 0 (index 0, as 0 > -0 is false).
+constexpr int kCells = 42;
+
+__device__ __forceinline__ void build_cells(const Codebook& cb, uint2* cells) {
+  const int c = threadIdx.x;
+  if (c < kCells) {
+    const float edge = (float)(c - 21) * 0.125f;
+    float next = __builtin_inff();
+    uint32_t below = 15u;
+#pragma unroll
+    for (int k = 14; k >= 0; --k) {
+      if (cb.m[k] >= edge) {
+        next = cb.m[k];
+        below = (uint32_t)k;
+      }
+    }
+    cells[c] = make_uint2(__float_as_uint(next), below);
+  }
 }
+
+// r8 = 8 / dd (any rounding of it is fine, see above).
+__device__ __forceinline__ uint32_t nearest_index(float w, float dd, float r8, const uint2* cells) {
+  const float t = fminf(fmaxf(__builtin_fmaf(w, r8, 21.0f), 0.0f), 41.5f);
+  const uint2 e = cells[(uint32_t)t];
+  return e.y + (w > dd * __uint_as_float(e.x) ? 1u : 0u);
+}
+
+// float32 -> fp16 bits of a non-negative value, round to nearest even,
+// saturating at 65504 (hardware conversion; kernels run with IEEE rounding
+// and fp16 denormals kept).
+__device__ __forceinline__ uint32_t f16_sat(float x) { return f32_to_f16_bits(fminf(x, 65504.0f)); }
 
 // kRsf: the RSF-lite scale search (quantizer-tool page, "RSF": search nearby
 // multiples of the scale and keep the better lattice fit).  For each half,
@@ -62,10 +89,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
                                                             Codebook cb, uint4* __restrict__ packed,
                                                             uint32_t* __restrict__ scales) {
   __shared__ float lut[16];
-  if constexpr (kRsf) {
-    stage_centroids(cb, lut);
-    __syncthreads();
-  }
+  __shared__ uint2 cells[kCells];
+  build_cells(cb, cells);
+  if constexpr (kRsf) stage_centroids(cb, lut);
+  __syncthreads();
   uint32_t g = blockIdx.x * kThreads + threadIdx.x;
   if (g >= total) return;
   uint32_t row = g / nb;
@@ -92,16 +119,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
       for (int i = 0; i < w; ++i) s[i] = s[2 * i] + s[2 * i + 1];
     }
     float rms = __builtin_sqrtf(s[0] * 0.0625f);
-    dbits[h] = f32_to_f16_sat_rne(rms);
-    float dd = f16_bits_to_f32_exact(dbits[h]);
+    dbits[h] = f16_sat(rms);
+    float dd = f16_bits_to_f32(dbits[h]);
     if constexpr (!kRsf) {
-      uint32_t U[7];
-#pragma unroll
-      for (int r = 0; r < 7; ++r) U[r] = __float_as_uint(dd * cb.m[8 + r]);
+      const float r8 = 8.0f * __builtin_amdgcn_rcpf(dd);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         int e = 16 * h + i;
-        words[e >> 3] |= nearest_index(v[e], U) << (4 * (e & 7));
+        words[e >> 3] |= nearest_index(v[e], dd, r8, cells) << (4 * (e & 7));
       }
     } else {
       constexpr int kOrder[9] = {0, -1, 1, -2, 2, -3, 3, -4, 4};
@@ -110,16 +135,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
 #pragma unroll 1
       for (int c = 0; c < 9; ++c) {
         const float mult = 1.0f + (float)kOrder[c] * 0.0625f;
-        const uint32_t bits = f32_to_f16_sat_rne(dd * mult);      // the float32 product is exact
-        const float ddj = f16_bits_to_f32_exact(bits);
-        uint32_t U[7];
-#pragma unroll
-        for (int r = 0; r < 7; ++r) U[r] = __float_as_uint(ddj * cb.m[8 + r]);
+        const uint32_t bits = f16_sat(dd * mult);                  // the float32 product is exact
+        const float ddj = f16_bits_to_f32(bits);
+        const float r8 = 8.0f * __builtin_amdgcn_rcpf(ddj);
         uint32_t w0 = 0u, w1 = 0u;
         float sq[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const uint32_t idx = nearest_index(v[16 * h + i], U);
+          const uint32_t idx = nearest_index(v[16 * h + i], ddj, r8, cells);
           if (i < 8) w0 |= idx << (4 * i);
           else w1 |= idx << (4 * (i - 8));
           const float e = v[16 * h + i] - ddj * lut[idx];
@@ -195,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint4* __res
   uint32_t b = g - row * nb;
   uint4 p = packed[g];
   uint32_t sc = scales[g];
-  float d0 = f16_bits_to_f32_exact(sc & 0xffffu);
-  float d1 = f16_bits_to_f32_exact(sc >> 16);
+  float d0 = f16_bits_to_f32(sc & 0xffffu);
+  float d1 = f16_bits_to_f32(sc >> 16);
   uint32_t words[4] = {p.x, p.y, p.z, p.w};
   float v[32];
 #pragma unroll
