@@ -478,7 +478,8 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
                                                                 const float* __restrict__ tscale, uint32_t N,
                                                                 uint32_t nb, const uint8_t* __restrict__ X,
                                                                 int64_t ldx, uint32_t M, float* __restrict__ Y,
-                                                                int64_t ldy, uint32_t G, uint32_t tq, uint32_t tr) {
+                                                                int64_t ldy, uint32_t G, uint32_t tq, uint32_t tr,
+                                                                uint32_t halves) {
   constexpr int kRing = kRingBytes / (kWide * 64 * 16 * MT);        // weight tiles per ring
   static_assert(kRing * 256 * MT == 64 * kWide, "one output per thread per flush");
   // LDS: pair table (TQ4_1S only) | partial-tile ring | pass accumulator.
@@ -501,7 +502,15 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   constexpr uint32_t kPassGroups = (uint32_t)(kWide * NQ);
   const uint32_t passes = (ngroups + kPassGroups - 1u) / kPassGroups;
 
-  const uint32_t t0 = blockIdx.x;
+  // K split in two (halves == 2, few row tiles): workgroups G.. 2G - 1 take
+  // the same tiles as 0 .. G - 1 over the second half of the passes, and
+  // both halves add their sums into Y, which the launch zeroed first; with
+  // two addends onto zero the result does not depend on their order.
+  const uint32_t half = blockIdx.x / G;
+  const uint32_t t0 = blockIdx.x - half * G;
+  const uint32_t mid = (passes + 1u) / 2u;
+  const uint32_t pass_begin = halves == 2u ? half * mid : 0u;
+  const uint32_t pass_end = halves == 2u && half == 0u ? mid : passes;
   const uint32_t n = tq + (t0 < tr ? 1u : 0u);          // this workgroup's tiles
   const uint32_t last = t0 + (n - 1u) * G;
 
@@ -534,9 +543,10 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   // chunk c ^ (r % 16), so that the operand reads (16 rows x four 16-byte
   // chunks per instruction) spread over the banks; a lane of a DMA
   // instruction writes the LDS chunk at its own position, so it reads the
-  // global piece that belongs there.  Rows past M repeat row M - 1 and
-  // elements past K are clamped: both only feed outputs that are not
-  // written or steps that are skipped.  (Loading the operands straight
+  // global piece that belongs there.  Rows past M are not staged (their
+  // LDS holds stale bytes) and elements past K are clamped: both only feed
+  // outputs that are not written (an MFMA output row depends on its own
+  // activation row alone) or steps that are skipped.  (Loading the operands straight
   // from X in the MFMA layout, 16 rows x 64 bytes per instruction, took
   // about twice as long.)
   constexpr uint32_t kPassK = 16u * NQ * 128u;               // elements of K per pass
@@ -551,11 +561,11 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const uint32_t base = 1024u * (uint32_t)(i * kWide + wave);          // wavefront-uniform LDS offset
+      if (base / kRowBytes >= M) continue;   // an instruction covers part of one row; rows past M are not staged
       const uint32_t off = base + 16u * (uint32_t)lane;
       const uint32_t r = off / kRowBytes, c = ((off % kRowBytes) / 16u) ^ (r & 15u);
-      const uint32_t m = min(r, M - 1u);
       const uint32_t k = min(pass * kPassK + h * kPartK + 8u * c, K - 8u);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(X + ((size_t)m * ldx + k) * 2),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(X + ((size_t)r * ldx + k) * 2),
                                        (__attribute__((address_space(3))) void*)(stage + base), 16, 0, 0);
     }
   };
@@ -598,22 +608,26 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
       float sum = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kWide; ++w2) sum += ring[slot][w2][mt][l][r];
-      float* const acc = accum + (first + slot) * (256u * MT) + o;   // passes > 1 only
-      if (pass > 0) sum = *acc + sum;
-      if (pass + 1 < passes) {
+      float* const acc = accum + (first + slot) * (256u * MT) + o;   // several passes only
+      if (pass > pass_begin) sum = *acc + sum;
+      if (pass + 1 < pass_end) {
         *acc = sum;
       } else {
         const uint32_t tt = t0 + (first + slot) * G;
         const uint32_t row = tt * 16u + (uint32_t)(l & 15);
         const uint32_t m = (uint32_t)mt * 16u + 4u * (uint32_t)(l >> 4) + (uint32_t)r;
-        if (m < M && row < N) Y[(size_t)m * ldy + row] = Fmt::kTensorScale ? sum * ts : sum;
+        if (m < M && row < N) {
+          const float v = Fmt::kTensorScale ? sum * ts : sum;
+          if (halves == 2u) unsafeAtomicAdd(Y + (size_t)m * ldy + row, v);
+          else Y[(size_t)m * ldy + row] = v;
+        }
       }
     }
     __syncthreads();                        // the ring is rewritten next
   };
 
   WSet pa, pb;
-  for (uint32_t pass = 0; pass < passes; ++pass) {
+  for (uint32_t pass = pass_begin; pass < pass_end; ++pass) {
     // The pass's activations and first weights, in the same order on every
     // pass (the table is filled while the first pass's are in flight); the
     // waits for the activations leave the weights in flight.
@@ -621,7 +635,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     // LDS stores wait for any DMA into LDS still in flight.)
     load_w(pa, t0, pass);
     if constexpr (Fmt::kLut) {
-      if (pass == 0) fill_pair_lut(lut, tid, 64 * kWide);
+      if (pass == pass_begin) fill_pair_lut(lut, tid, 64 * kWide);
     }
     dma_x(pass, 0);
     __syncthreads();                        // first part staged (and the table filled)
@@ -703,6 +717,11 @@ template <class Fmt> constexpr size_t scale_bytes() {
   return std::is_same<Fmt, GemmTQ4>::value ? 4 : std::is_same<Fmt, GemmNVFP4>::value ? 2 : 1;
 }
 
+__global__ void zero_rows(float* __restrict__ Y, int64_t ldy, uint32_t N) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < N) Y[(size_t)blockIdx.y * ldy + i] = 0.f;
+}
+
 template <class Fmt, int MT, int NQ>
 void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb, const uint8_t* X,
                   int64_t ldx, uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
@@ -714,11 +733,17 @@ void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_
   for (uint64_t r0 = 0; r0 < N; r0 += 16u * max_tiles) {
     const uint32_t Nc = (uint32_t)std::min<uint64_t>(N - r0, 16u * max_tiles);
     const uint32_t tiles = (Nc + 15u) / 16u;
-    const uint32_t per_wg = (tiles + cap - 1u) / cap;
+    // Fewer than four row tiles per compute unit and K in several passes:
+    // split K in two, so that each workgroup works through more tiles per
+    // pass instead of paying a pass's staging and flush for one tile.
+    const uint32_t halves = passes >= 2u && tiles < 4u * cap ? 2u : 1u;
+    const uint32_t wgs = std::max(1u, cap / halves);
+    const uint32_t per_wg = (tiles + wgs - 1u) / wgs;
     const uint32_t grid = (tiles + per_wg - 1u) / per_wg;
-    hipLaunchKernelGGL((gemm_small_kernel<Fmt, MT, NQ>), dim3(grid), dim3(64 * kWide), 0, s,
+    if (halves == 2u) hipLaunchKernelGGL(zero_rows, dim3((Nc + 255u) / 256u, M), dim3(256), 0, s, Y + r0, ldy, Nc);
+    hipLaunchKernelGGL((gemm_small_kernel<Fmt, MT, NQ>), dim3(grid * halves), dim3(64 * kWide), 0, s,
                        pk + r0 * nb * code_bytes<Fmt>(), sc + r0 * nb * scale_bytes<Fmt>(), ts, Nc, nb, X, ldx, M,
-                       Y + r0, ldy, grid, tiles / grid, tiles % grid);
+                       Y + r0, ldy, grid, tiles / grid, tiles % grid, halves);
   }
 }
 

@@ -226,6 +226,25 @@ def test_gemm_bf16_large_k():
         assert_within(f32np(Y), yr, a, what=f"gemm bf16 K={k}")
 
 
+@pytest.mark.parametrize("n,k,m", [(300, 8192, 8), (4096, 14336, 16), (48, 14336, 32)])
+def test_gemm_split_k_repeat_runs_are_bit_identical(n, k, m):
+    """Few row tiles and K in several passes: K is split over two workgroups whose sums meet in Y; the
+    result must not depend on which half lands first."""
+    g = workloads.generator(n + k + m, DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    X = workloads.activation(m, k, g, DEV, torch.bfloat16)
+    packed, scales = tqa.quantize(W)
+    xr = tqa.rotate(X, dtype=torch.bfloat16)
+    say(f"[gemm] split K repeat M={m} {n}x{k}")
+    Y1 = tqa.gemm(packed, scales, xr)
+    for _ in range(3):
+        Y2 = tqa.gemm(packed, scales, xr)
+        assert torch.equal(Y1, Y2)
+    rows = np.arange(0, n, max(1, n // 64))
+    yr, a = otq.gemm_o64(packed.cpu().numpy()[rows], u16(scales)[rows], X.float().cpu().numpy())
+    assert_within(f32np(Y1)[:, rows], yr, a, what=f"gemm split K M={m} {n}x{k}")
+
+
 def test_repeat_runs_are_bit_identical():
     g = workloads.generator(77, DEV)
     W = workloads.normal_weight(300, 4096, 4096 ** -0.5, g, DEV, torch.bfloat16)
