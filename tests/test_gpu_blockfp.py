@@ -80,9 +80,9 @@ def test_blockfp_gemm(fmt, m):
 @pytest.mark.parametrize("m", [5, 8, 17, 32, 33, 64, 65, 100])
 def test_blockfp_gemm_mfma(fmt, m):
     """bf16 activations with M >= 5 take the MFMA kernel: exact bf16 weight operands, float32 sums (relative
-    error far below the bound).  Shapes: several passes over K (5120, 17408), a partial group of four blocks
-    (K = 96, 32), ragged row tiles."""
-    for n, k in ((300, 5120), (37, 96), (130, 32), (64, 17408)):
+    error far below the bound).  Shapes: several passes over K (5120, 17408), one pass in which half the
+    wavefronts take a single group (3072), a partial group of four blocks (K = 96, 32), ragged row tiles."""
+    for n, k in ((300, 5120), (37, 96), (130, 32), (64, 17408), (200, 3072)):
         W = _outlier_weight(n, k, 700 + m + k, torch.bfloat16)
         codes, bs, ts, Wd = _check(fmt, W)
         X = workloads.activation(m, k, workloads.generator(910 + m + k, DEV), DEV, torch.bfloat16)
