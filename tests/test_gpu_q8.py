@@ -60,6 +60,24 @@ def test_transcode_sign_masks_and_edge_rows():
     _transcode_check(p, s, otq.DEFAULT_SIGN_MASK, "all bytes, scale classes")
 
 
+def test_transcode_quotients_near_half_integers():
+    """Many blocks, so that a few hundred quotients w / dd fall within 1e-4 of a half-integer (a few exactly
+    on one: ties to even), where the code depends on the last bits of the quotient; all codes bit-exact."""
+    rng = np.random.default_rng(11)
+    n, k = 2048, 1024
+    pk = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    sbits = np.float16(rng.uniform(0.005, 2.0, (n, k // 16))).view(np.uint16)
+    w = oq8.dequantize_o32_blocks(pk, sbits, otq.DEFAULT_SIGN_MASK)
+    dd = otq.fp16_sat((np.abs(w).max(axis=-1) / np.float32(127)).astype(np.float32)).astype(np.float32)
+    q = (w / dd[..., None]).astype(np.float32)
+    frac = np.abs(q - np.rint(q))
+    near, ties = int((np.abs(frac - np.float32(0.5)) < 1e-4).sum()), int((frac == 0.5).sum())
+    say(f"[transcode] {near} quotients within 1e-4 of a half-integer, {ties} exactly on one")
+    assert near >= 50 and ties >= 1
+    _transcode_check(torch.from_numpy(pk).to(DEV), torch.from_numpy(sbits.view(np.int16)).to(DEV),
+                     otq.DEFAULT_SIGN_MASK, "near half-integers")
+
+
 def _gemv_check(codes, qs, x, label):
     say(f"[q8_gemv] {label} N={codes.shape[0]} K={codes.shape[1]} x={x.dtype}")
     y = tqa.q8_gemv(codes, qs, x)
