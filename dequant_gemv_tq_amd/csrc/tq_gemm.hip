@@ -798,9 +798,9 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
   const uint8_t* X = static_cast<const uint8_t*>(xr);
   const int64_t xs = xbf16 ? 2 : 4;
-  // At most 32 activation rows per launch: the persistent bf16 kernel keeps
-  // its operands in registers (two 16-row tiles fit beside the weight
-  // prefetch), and float32 activations take three MFMAs per product and
+  // At most 64 bf16 or 32 float32 activation rows per launch: the
+  // persistent bf16 kernel keeps its operands in registers (up to four
+  // 16-row tiles), and float32 activations take three MFMAs per product and
   // twice the operand registers.
   const int64_t chunk = xbf16 ? 64 : 32;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {

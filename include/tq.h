@@ -170,6 +170,13 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  * activations (operand rounding about 2^-9, inside 1e-3 * sum|w x| once K is
  * in the hundreds), three hi/lo-split passes for float32 activations (about
  * 16 significant bits per product, any K).
+ * With bf16 activations, M >= 5, fewer than four 16-row tiles of N per
+ * compute unit and K longer than one pass of the kernel (4096 elements for
+ * launches of up to 16 rows, 2048 for 17-64; M is launched 64 rows at a
+ * time), the call zeroes y's
+ * M x N elements in a kernel of its own and two sets of workgroups then add
+ * the sums of the two halves of K into them: y must not overlap x, and the
+ * result is still the same on every run (two addends onto zero).
  * Limits: M <= 256, K <= 131072.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN,
  * TQ_EDTYPE. */
 tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
@@ -222,7 +229,9 @@ tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64
  *   M >= 5 with bf16 X: bf16 MFMA in 16-row tiles (up to 64 rows per
  *     launch), every weight converted once to an exact bf16 operand
  *     (e2m1 * e4m3 for NVFP4, the tensor scale applied to the finished sums;
- *     e3m2 * 2^(e8m0 - 127) for MXFP6), float32 accumulation.
+ *     e3m2 * 2^(e8m0 - 127) for MXFP6), float32 accumulation.  Few row
+ *     tiles and K in several passes: Y zeroed first and K split in two, as
+ *     for tq_gemm (Y must not overlap X; the result does not vary by run).
  * X [M, K] row stride ldx, TQ_F32 or TQ_BF16, 16-byte aligned; Y [M, N]
  * float32, row stride ldy.  K % 32 == 0, K <= 32768, M <= 4096; NVFP4 codes
  * 16-byte aligned (MXFP6 codes 8-byte), NVFP4 block_scales 2-byte aligned.
