@@ -203,21 +203,33 @@ __global__ __launch_bounds__(kThreads) void rotate_kernel(const uint8_t* __restr
 
 // Dequantize: q_i = d_h * c[idx_i], then the inverse rotation
 // w = fl(1/sqrt 32) * D * FWHT32(q)   (H32 is symmetric and H32^2 = 32 I).
+// The sign flip rides on the scale multiply (fl(u * -s) = -fl(u * s)), with
+// the signed scales formed on the scalar unit.  The bf16 output is rounded
+// by v_cvt_pk_bf16_f32 (round to nearest even).  Each wavefront's 64 blocks
+// pass through LDS on the way out, so that every store instruction writes
+// 1 KiB of consecutive 16-byte chunks instead of 16 bytes every 64 (128 for
+// float32 output).
+typedef __bf16 bf16x2t __attribute__((ext_vector_type(2)));
+
 template <bool kOutBf16>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint4* __restrict__ packed,
                                                               const uint32_t* __restrict__ scales,
                                                               uint32_t nb, uint32_t total, uint32_t mask,
                                                               Codebook cb, uint8_t* __restrict__ out,
                                                               int64_t ldo_bytes) {
+  constexpr int kChunks = kOutBf16 ? 4 : 8;            // 16-byte chunks per block
   __shared__ float lut[16];
+  __shared__ __attribute__((aligned(16))) uint4 stage[kThreads / 64][64 * kChunks];
   stage_centroids(cb, lut);
   __syncthreads();
-  uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-  if (g >= total) return;
-  uint32_t row = g / nb;
-  uint32_t b = g - row * nb;
-  uint4 p = packed[g];
-  uint32_t sc = scales[g];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t gw = blockIdx.x * kThreads + wave * 64;         // first block of this wavefront
+  if (gw >= total) return;                                       // wavefront-uniform
+  const uint32_t g = gw + lane;
+  const bool live = g < total;
+  const uint32_t gc = live ? g : total - 1u;
+  uint4 p = packed[gc];
+  uint32_t sc = scales[gc];
   float d0 = f16_bits_to_f32(sc & 0xffffu);
   float d1 = f16_bits_to_f32(sc >> 16);
   uint32_t words[4] = {p.x, p.y, p.z, p.w};
@@ -229,23 +241,39 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint4* __res
   }
   fwht32(v);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = v[i] * kInvSqrt32;
-  apply_signs(v, mask);
-  uint8_t* dst = out + (int64_t)row * ldo_bytes + (int64_t)b * (kOutBf16 ? 64 : 128);
+  for (int i = 0; i < 32; ++i)
+    v[i] = v[i] * __uint_as_float(__float_as_uint(kInvSqrt32) ^ (((mask >> i) & 1u) << 31));
+  uint4* const st = stage[wave];
   if constexpr (kOutBf16) {
-    uint4* q = reinterpret_cast<uint4*>(dst);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        w[u] = f32_to_bf16_rne(v[8 * t + 2 * u]) | (f32_to_bf16_rne(v[8 * t + 2 * u + 1]) << 16);
-      q[t] = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int u = 0; u < 4; ++u) {
+        const bf16x2t h = {(__bf16)v[8 * t + 2 * u], (__bf16)v[8 * t + 2 * u + 1]};
+        w[u] = __builtin_bit_cast(uint32_t, h);
+      }
+      st[lane * kChunks + t] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   } else {
-    float4* q = reinterpret_cast<float4*>(dst);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) q[t] = make_float4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]);
+    for (int t = 0; t < 8; ++t)
+      st[lane * kChunks + t] = make_uint4(__float_as_uint(v[4 * t]), __float_as_uint(v[4 * t + 1]),
+                                          __float_as_uint(v[4 * t + 2]), __float_as_uint(v[4 * t + 3]));
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0): this wavefront's LDS stores done
+  __builtin_amdgcn_wave_barrier();
+  // Chunk c of the wavefront is chunk c % kChunks of block gw + c / kChunks.
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const uint32_t c = (uint32_t)(lane + 64 * j);
+    const uint32_t gb = gw + c / kChunks;
+    if (gb < total) {
+      const uint32_t row = gb / nb, b = gb - row * nb;
+      uint8_t* dst = out + (int64_t)row * ldo_bytes + (int64_t)b * (16 * kChunks) + 16 * (c % kChunks);
+      *reinterpret_cast<uint4*>(dst) = st[c];
+    }
   }
 }
 
