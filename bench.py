@@ -319,20 +319,22 @@ def bench_q8(torch, tqa, model, xs, groups, dev, stream, tq4_ms, no_graph):
     """Load-time TQ4_1S -> int8 transcode of the 32-layer model, then the int8 decode step (same launches
     and activations as the TQ4_1S step: one q8 GEMV per group and layer, captured in a graph)."""
     L = len(model)
-    q_ms, q_weights = 0.0, 0
-    q8 = []
+    # Outputs allocated first and one untimed call, so that the timed region
+    # holds the 128 transcodes back to back and nothing else.
+    q8 = [{gname: (torch.empty((n, k), dtype=torch.int8, device=dev),
+                   torch.empty((n, k // 32), dtype=torch.int16, device=dev))
+           for gname, (n, k) in groups.items()} for _ in range(L)]
+    tqa.transcode_q8(*model[0]["o"], out=q8[0]["o"])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
     for layer in range(L):
-        entry = {}
-        for gname, (n, k) in groups.items():
-            p, s = model[layer][gname]
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            entry[gname] = tqa.transcode_q8(p, s)
-            b.record(stream)
-            b.synchronize()
-            q_ms += a.elapsed_time(b)
-            q_weights += n * k
-        q8.append(entry)
+        for gname in groups:
+            tqa.transcode_q8(*model[layer][gname], out=q8[layer][gname])
+    b.record(stream)
+    b.synchronize()
+    q_ms = a.elapsed_time(b)
+    q_weights = L * sum(n * k for n, k in groups.values())
     ys = {gname: torch.empty(n, dtype=torch.float32, device=dev) for gname, (n, k) in groups.items()}
 
     def step():

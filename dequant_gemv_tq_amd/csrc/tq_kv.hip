@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "tq_internal.hpp"
+#include "tq_codes.hpp"
 
 namespace tq {
 namespace {
@@ -95,18 +96,15 @@ __global__ __launch_bounds__(kThreads) void q8_rows_kernel(const uint8_t* __rest
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t d16 = f32_to_f16_sat_rne(amax / 127.0f);
-  const float dd = f16_bits_to_f32_exact(d16);
+  const uint32_t d16 = f16_sat(amax / 127.0f);
+  const float dd = f16_bits_to_f32(d16);
+  const float r = __builtin_amdgcn_rcpf(dd);
   uint32_t w[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     uint32_t word = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float c = dd > 0.f ? __builtin_rintf(v[4 * k + j] / dd) : 0.f;
-      c = fminf(fmaxf(c, -127.f), 127.f);
-      word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
-    }
+    for (int j = 0; j < 4; ++j) word |= q8_code(v[4 * k + j], dd, r) << (8 * j);
     w[k] = word;
   }
   codes[2 * (size_t)g] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -122,6 +120,9 @@ __global__ __launch_bounds__(kThreads) void turbo4_encode_kernel(const uint8_t* 
                                                                  Signs sg, Codebook cb,
                                                                  uint2* __restrict__ packed,
                                                                  uint16_t* __restrict__ norms) {
+  __shared__ uint2 cells[kCells];
+  build_cells(cb, cells);
+  __syncthreads();
   const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
   const uint32_t vec = tid / kLanesPerVec;
   const int sub = (int)(tid % kLanesPerVec);
@@ -163,22 +164,19 @@ __global__ __launch_bounds__(kThreads) void turbo4_encode_kernel(const uint8_t* 
   ss = ss + xor_f(ss, 1);
   ss = ss + xor_f(ss, 2);
   ss = ss + xor_f(ss, 4);
-  const uint32_t n16 = f32_to_f16_sat_rne(__builtin_sqrtf(ss));
-  const float nn = f16_bits_to_f32_exact(n16);
+  const uint32_t n16 = f16_sat(__builtin_sqrtf(ss));
+  const float nn = f16_bits_to_f32(n16);
 
 #pragma unroll
   for (int i = 0; i < 16; ++i) w[i] = sign_bit(sg, sub, i) ? -w[i] : w[i];
   fwht128_group(w, sub);
 
-  float T[15];
-#pragma unroll
-  for (int k = 0; k < 15; ++k) T[k] = nn * cb.m[k];
+  // idx = #{k : u > fl(nn m_k)}, by the cell table.
+  const float r8 = 8.0f * __builtin_amdgcn_rcpf(nn);
   uint32_t lo = 0u, hi = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    uint32_t idx = 0u;
-#pragma unroll
-    for (int k = 0; k < 15; ++k) idx += w[i] > T[k] ? 1u : 0u;
+    const uint32_t idx = nearest_index(w[i], nn, r8, cells);
     if (i < 8) lo |= idx << (4 * i);
     else hi |= idx << (4 * (i - 8));
   }

@@ -37,6 +37,7 @@
 #include <tuple>
 
 #include "tq_internal.hpp"
+#include "tq_codes.hpp"
 
 namespace tq {
 namespace {
@@ -68,25 +69,12 @@ __global__ __launch_bounds__(kTcThreads) void q8_transcode_kernel(const uint4* _
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // fp16 by the hardware convert (round to nearest even, fp16 denormals
-  // kept), saturated at 65504 first.
-  const uint32_t dbits = f32_to_f16_bits(fminf(amax / 127.0f, 65504.0f));
+  const uint32_t dbits = f16_sat(amax / 127.0f);
   const float dd = f16_bits_to_f32(dbits);
-  // rint(fl(v / dd)) without a full division per element: q = v * rcp(dd)
-  // is within 3.1e-5 of fl(v / dd) for |q| <= 128 (rcp within 1 ulp, one
-  // product rounding, half an ulp of the quotient), so rint(q) is the answer
-  // unless q lies within 1e-4 of a half-integer; only those elements take
-  // the correctly rounded division.
   const float r = __builtin_amdgcn_rcpf(dd);
   uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float q = v[i] * r;
-    float t = rintf(q);
-    if (fabsf(fabsf(q - t) - 0.5f) < 1e-4f) t = rintf(v[i] / dd);
-    t = dd > 0.f ? fminf(fmaxf(t, -127.f), 127.f) : 0.f;
-    out[i >> 2] |= ((uint32_t)(int32_t)t & 0xffu) << (8 * (i & 3));
-  }
+  for (int i = 0; i < 32; ++i) out[i >> 2] |= q8_code(v[i], dd, r) << (8 * (i & 3));
   codes[2 * (size_t)g] = make_uint4(out[0], out[1], out[2], out[3]);
   codes[2 * (size_t)g + 1] = make_uint4(out[4], out[5], out[6], out[7]);
   qscales[g] = (uint16_t)dbits;
