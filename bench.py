@@ -440,10 +440,17 @@ def bench_kv(torch, tqa, wl, dev, stream, no_graph, layers=32, batch=16, ctx=409
         g = wl.generator(wl.seed_of(6, layer, 0), dev)
         K = torch.randn((batch, Hkv, ctx, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         V = torch.randn((batch, Hkv, ctx, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        kc = torch.empty(K.shape, dtype=torch.int8, device=dev)
+        ks = torch.empty(K.shape[:-1] + (D // 32,), dtype=torch.int16, device=dev)
+        vp = torch.empty(V.shape[:-1] + (D // 2,), dtype=torch.uint8, device=dev)
+        vn = torch.empty(V.shape[:-1], dtype=torch.int16, device=dev)
+        if layer == 0:                       # untimed: kernels loaded before the first timed encode
+            tqa.kv_quantize_k(K, out=(kc, ks))
+            tqa.kv_quantize_v(V, out=(vp, vn))
         torch.cuda.synchronize()
         a.record(stream)
-        kc, ks = tqa.kv_quantize_k(K)
-        vp, vn = tqa.kv_quantize_v(V)
+        tqa.kv_quantize_k(K, out=(kc, ks))
+        tqa.kv_quantize_v(V, out=(vp, vn))
         b.record(stream)
         b.synchronize()
         enc_ms += a.elapsed_time(b)

@@ -307,30 +307,42 @@ def kv_sign_from_seed(seed: int = 0):
     return out
 
 
-def kv_quantize_k(K: torch.Tensor):
-    """Keys [..., d] (bf16/fp32, contiguous) -> (int8 codes [..., d], fp16 scales [..., d/32] as int16)."""
+def kv_quantize_k(K: torch.Tensor, out=None):
+    """Keys [..., d] (bf16/fp32, contiguous) -> (int8 codes [..., d], fp16 scales [..., d/32] as int16);
+    ``out`` = (codes, scales) of those shapes to write into."""
     _dev(K, "K")
     if not K.is_contiguous():
         raise ValueError("K must be contiguous")
     d = K.shape[-1]
     n = K.numel() // d
-    codes = torch.empty(K.shape, dtype=torch.int8, device=K.device)
-    scales = torch.empty(K.shape[:-1] + (d // 32,), dtype=torch.int16, device=K.device)
+    if out is None:
+        codes = torch.empty(K.shape, dtype=torch.int8, device=K.device)
+        scales = torch.empty(K.shape[:-1] + (d // 32,), dtype=torch.int16, device=K.device)
+    else:
+        codes, scales = out
+        if codes.shape != K.shape or scales.shape != K.shape[:-1] + (d // 32,):
+            raise ValueError("out shapes do not match K")
     st = lib().tq_kv_quantize_k(_ptr(K), _dtype_code(K, "K"), n, d, _ptr(codes), _ptr(scales), _stream())
     _check("tq_kv_quantize_k", st)
     return codes, scales
 
 
-def kv_quantize_v(V: torch.Tensor, sign=None):
-    """Values [..., 128] (bf16/fp32, contiguous) -> (packed uint8 [..., 64], fp16 norms [...] as int16)."""
+def kv_quantize_v(V: torch.Tensor, sign=None, out=None):
+    """Values [..., 128] (bf16/fp32, contiguous) -> (packed uint8 [..., 64], fp16 norms [...] as int16);
+    ``out`` = (packed, norms) of those shapes to write into."""
     _dev(V, "V")
     if not V.is_contiguous():
         raise ValueError("V must be contiguous")
     d = V.shape[-1]
     n = V.numel() // d
     sign = kv_sign_from_seed(0) if sign is None else sign
-    packed = torch.empty(V.shape[:-1] + (d // 2,), dtype=torch.uint8, device=V.device)
-    norms = torch.empty(V.shape[:-1], dtype=torch.int16, device=V.device)
+    if out is None:
+        packed = torch.empty(V.shape[:-1] + (d // 2,), dtype=torch.uint8, device=V.device)
+        norms = torch.empty(V.shape[:-1], dtype=torch.int16, device=V.device)
+    else:
+        packed, norms = out
+        if packed.shape != V.shape[:-1] + (d // 2,) or norms.shape != V.shape[:-1]:
+            raise ValueError("out shapes do not match V")
     st = lib().tq_kv_quantize_v(_ptr(V), _dtype_code(V, "V"), n, d, sign, _ptr(packed), _ptr(norms), _stream())
     _check("tq_kv_quantize_v", st)
     return packed, norms

@@ -39,6 +39,20 @@ def test_kv_quantize_k_bit_exact(n, d, dtype):
     np.testing.assert_array_equal(codes.cpu().numpy(), oc)
 
 
+def test_kv_encode_into_given_outputs():
+    K = _rand((3, 2, 50, D), 15, torch.bfloat16)
+    kc, ks = tqa.kv_quantize_k(K)
+    vp, vn = tqa.kv_quantize_v(K)
+    out_k = (torch.full_like(kc, 7), torch.full_like(ks, 7))
+    out_v = (torch.full_like(vp, 7), torch.full_like(vn, 7))
+    say("[kv] encode into given outputs")
+    tqa.kv_quantize_k(K, out=out_k)
+    tqa.kv_quantize_v(K, out=out_v)
+    torch.cuda.synchronize()
+    assert torch.equal(out_k[0], kc) and torch.equal(out_k[1], ks)
+    assert torch.equal(out_v[0], vp) and torch.equal(out_v[1], vn)
+
+
 def _edge_vectors():
     V = np.zeros((8, D), np.float32)
     V[1, 17] = -3.25                                     # a single spike
