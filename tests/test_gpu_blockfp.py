@@ -45,6 +45,23 @@ def test_blockfp_quantize_bit_exact(fmt, n, k, dt):
     _check(fmt, _outlier_weight(n, k, n * 31 + k, dt))
 
 
+def test_nvfp4_quotients_near_rounding_boundaries():
+    """Enough blocks that tens of scaled quotients |w| / eff * 2^(1 - e) fall within 1e-5 of a half-integer,
+    where the E2M1 code depends on the last bits of the quotient; all codes bit-exact."""
+    W = _outlier_weight(2048, 1024, 4242, torch.float32)
+    Wh = W.cpu().numpy()
+    oc, osb, ost = obf.nvfp4_quantize_o32(Wh)
+    eff = (obf.E4M3FN.decode(osb).astype(np.float32) * np.float32(ost)).astype(np.float32)
+    q = (np.abs(Wh).reshape(2048, 64, 16) / eff[..., None]).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        e = np.maximum(np.floor(np.log2(np.where(q > 0, q, 1))), 0)
+    sc = (q * np.exp2(1 - e)).astype(np.float32)
+    near = int(((np.abs(np.abs(sc - np.rint(sc)) - 0.5) < 1e-5) & (q < 8)).sum())
+    say(f"[nvfp4] {near} scaled quotients within 1e-5 of a half-integer")
+    assert near >= 20
+    _check("nvfp4", W)
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
 def test_blockfp_edge_values(fmt):
     W = torch.zeros(6, 64)
