@@ -61,6 +61,12 @@ __device__ __forceinline__ uint32_t encode_mag_near(float a, bool& near) {
   return code > kMaxCode ? kMaxCode : code;
 }
 
+// The magnitude an E2M1 code 0..7 stands for: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const uint32_t m = code & 1u, e = code >> 1;
+  return e == 0u ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
+}
+
 // encode_mag that also returns the magnitude the code stands for (exact:
 // the rounded integer times a power of two, or the format's largest value).
 template <int kM, int kEmin, uint32_t kMaxCode>
@@ -135,16 +141,21 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint8_t* __restric
 
 // Squared float32 error of a 16-element block encoded with effective scale
 // eff (codes +0 when eff = 0), summed as tree16.
+// The code of fl(|v| / eff) comes from |v| * rcp(eff) as in the encoder,
+// with the correctly rounded division near a rounding boundary.
 __device__ __forceinline__ float nvfp4_block_error(const float (&v)[16], float eff) {
   float s[16];
+  const bool fast = eff >= 0x1p-100f;
+  const float r = __builtin_amdgcn_rcpf(eff);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float qhat = 0.0f;
     if (eff != 0.0f) {
-      const float q = v[i] / eff;
-      float val;
-      encode_mag_val<1, 0, 7u>(fabsf(q), 6.0f, val);
-      qhat = (sign_of(q) ? -val : val) * eff;
+      bool near = true;
+      uint32_t code = fast ? encode_mag_near<1, 0, 7u>(fabsf(v[i]) * r, near) : 0u;
+      if (near) code = encode_mag<1, 0, 7u>(fabsf(v[i] / eff));
+      const float val = e2m1_value(code);
+      qhat = (sign_of(v[i]) ? -val : val) * eff;
     }
     const float d = v[i] - qhat;
     s[i] = d * d;
