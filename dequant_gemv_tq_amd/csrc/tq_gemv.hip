@@ -23,17 +23,23 @@
 //     (b = lane_k + j * TK) for the whole kernel; the rotation (when the
 //     activation arrives unrotated) is done once per workgroup in the
 //     prologue.
-//   * Persistent workgroups walk row tiles with the next tile's 16-byte
-//     nibble loads and 4-byte scale loads issued before the current tile is
-//     computed (two tiles in flight per wavefront).
-//   * A wavefront ends a tile with R*MC partial sums per lane; a transposed
-//     butterfly (v_permlane32_swap, v_permlane16_swap, DPP) halves the set
-//     at every cross-lane step, ~2.5 VALU ops per row instead of ~11.
-//   * Several wavefronts along K (TK = 64 * WK lanes per row slot) combine
-//     through a small double-buffered LDS array, one barrier per tile.
+//   * Persistent workgroups walk row tiles.  A wavefront keeps up to four
+//     register sets of tile loads (16-byte nibble loads, 4-byte scale loads)
+//     in flight; only the first tile is requested before the activation has
+//     arrived, because a larger first burst of weight requests delays the
+//     activation, which every tile waits for.  Row addresses are
+//     wavefront-uniform (scalar) plus a fixed 32-bit lane offset.
+//   * The decode is VALU-bound in the steady state (counters: ~65% VALU busy
+//     per SIMD over a whole gate|up launch, LDS waits ~3%), so per-tile
+//     overhead matters: a lane keeps the partial sums of several tiles and
+//     one transposed butterfly (v_permlane32_swap, v_permlane16_swap, DPP)
+//     reduces four of them at once, ~3 VALU ops per row instead of ~10.
+//   * Several wavefronts along K (TK = 64 * WK lanes per row slot) leave
+//     their partial sums in an LDS ring that is combined every 32 tiles.
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 
 #include "tq_internal.hpp"
 
@@ -131,8 +137,12 @@ struct FmtTQ4 {
   const uint4* codes;
   const uint32_t* scales;
   __device__ __forceinline__ void prepare() {}
-  __device__ __forceinline__ Raw load(size_t row, uint32_t nb, uint32_t b) const {
-    return Raw{codes[row * nb + b], scales[row * nb + b]};
+  // Block b of row `row` (wavefront-uniform): a scalar row base plus the
+  // lane's 32-bit byte offset.
+  __device__ __forceinline__ Raw load(uint32_t row, uint32_t nb, uint32_t b) const {
+    const uint8_t* cr = reinterpret_cast<const uint8_t*>(codes) + (size_t)row * nb * 16u;
+    const uint8_t* sr = reinterpret_cast<const uint8_t*>(scales) + (size_t)row * nb * 4u;
+    return Raw{*reinterpret_cast<const uint4*>(cr + (b << 4)), *reinterpret_cast<const uint32_t*>(sr + (b << 2))};
   }
   template <int MC>
   __device__ __forceinline__ void decode(const Raw& r, const float (&x)[MC][32], const uint8_t* lut,
@@ -179,8 +189,10 @@ struct FmtNVFP4 {
   const float* tscale;
   float st;
   __device__ __forceinline__ void prepare() { st = *tscale; }
-  __device__ __forceinline__ Raw load(size_t row, uint32_t nb, uint32_t b) const {
-    return Raw{codes[row * nb + b], scales[row * nb + b]};
+  __device__ __forceinline__ Raw load(uint32_t row, uint32_t nb, uint32_t b) const {
+    const uint8_t* cr = reinterpret_cast<const uint8_t*>(codes) + (size_t)row * nb * 16u;
+    const uint8_t* sr = reinterpret_cast<const uint8_t*>(scales) + (size_t)row * nb * 2u;
+    return Raw{*reinterpret_cast<const uint4*>(cr + (b << 4)), *reinterpret_cast<const uint16_t*>(sr + (b << 1))};
   }
   template <int MC>
   __device__ __forceinline__ void decode(const Raw& r, const float (&x)[MC][32], const uint8_t*, uint32_t,
@@ -225,9 +237,10 @@ struct FmtMXFP6 {
   const uint2* codes;
   const uint8_t* scales;
   __device__ __forceinline__ void prepare() {}
-  __device__ __forceinline__ Raw load(size_t row, uint32_t nb, uint32_t b) const {
-    const uint2* src = codes + (row * nb + b) * 3;
-    return Raw{{src[0], src[1], src[2]}, scales[row * nb + b]};
+  __device__ __forceinline__ Raw load(uint32_t row, uint32_t nb, uint32_t b) const {
+    const uint8_t* cr = reinterpret_cast<const uint8_t*>(codes) + (size_t)row * nb * 24u;
+    const uint2* src = reinterpret_cast<const uint2*>(cr + b * 24u);
+    return Raw{{src[0], src[1], src[2]}, scales[(size_t)row * nb + b]};
   }
   template <int MC>
   __device__ __forceinline__ void decode(const Raw& r, const float (&x)[MC][32], const uint8_t*, uint32_t,
@@ -347,19 +360,44 @@ struct GemvGrid {
   uint32_t r;
 };
 
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
 // kMode: 0 = x' fp32, 1 = x' bf16, 2 = raw fp32 x, 3 = raw bf16 x (rotated in the prologue).
 // kStage: stage x' in LDS once per workgroup with kStage groups of 4
 // elements per thread (MC == 1, K <= kStageFloats); 0: every lane loads and
 // rotates its own blocks.
-// kDepth: tiles whose loads a wavefront keeps in flight (register sets): 1
-// = load, wait, compute; 2 and 3 issue the loads of the tiles one and two
-// steps ahead before the current tile is computed.
-template <typename Fmt, int J, int R, int MC, int kMode, int kMaxT, int kDepth, int kStage>
+// kDepth (1, 2 or 4): register sets of tile loads a wavefront keeps in
+// flight; kEarly of them are requested at kernel start, the others once the
+// wavefront has its part of the activation (a large first burst of weight
+// requests delays the activation, which every tile waits for).
+//
+// Row sums are reduced across the wavefront in groups of V values (T tiles
+// of R rows of MC activation rows, V = R MC T, usually 4): each lane keeps
+// its V partial sums and one transposed butterfly reduces them all, about 3
+// VALU operations per row instead of about 10 for a reduction of each row on
+// its own.
+template <typename Fmt, int J, int R, int MC, int kMode, int kMaxT, int kDepth, int kEarly, int kStage>
 __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32_t nb, uint32_t mask,
                                                      const uint8_t* __restrict__ x, int64_t ldx,
                                                      float* __restrict__ y, int64_t ldy, GemvGrid gg) {
-  constexpr int V = R * MC;
-  static_assert(V == 1 || V == 2 || V == 4 || V == 8, "R * MC must be 1, 2, 4 or 8");
+  constexpr int RM = R * MC;                           // values per tile and lane
+  static_assert(RM == 1 || RM == 2 || RM == 4 || RM == 8, "R * MC must be 1, 2, 4 or 8");
+  // Tiles per reduction group: up to four rows' worth (one tile when a lane
+  // owns several blocks), and no more than the register sets can hold at
+  // the end of the list (the remaining tiles of a workgroup are computed
+  // from registers only).
+  constexpr int kT0 = (RM >= 4 || J > 1) ? 1 : 4 / RM;   // J > 1: x' alone takes 32 J registers
+  constexpr int T = kT0 < (kDepth >= 4 ? 4 : 2) ? kT0 : (kDepth >= 4 ? 4 : 2);
+  constexpr int V = RM * T;                            // values per reduction group
+  static_assert(kDepth == 1 || kDepth == 2 || kDepth == 4, "kDepth must be 1, 2 or 4");
+  static_assert(kEarly >= 1 && kEarly <= kDepth, "1 <= kEarly <= kDepth");
+  constexpr int U = kDepth > T ? kDepth : T;           // tiles per loop iteration (both powers of two)
   constexpr bool kXbf16 = kMode == 1 || kMode == 3;
   static_assert(!kStage || MC == 1, "staged activations serve one row");
   // One LDS allocation with the pair table at offset 0, so a table address
@@ -367,12 +405,12 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
   // ds_read immediate and cost an add per lookup), then the staged x' and
   // the cross-wavefront partial sums.
   constexpr int kXsBytes = kStage ? kStageFloats * 4 : 0;
-  constexpr int kRedBytes = kRing * (kMaxT / 64) * V * 4;
+  constexpr int kRedBytes = kRing * (kMaxT / 64) * RM * 4;
   constexpr int kTable = Fmt::kLut ? kLutBytes : 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kTable + kXsBytes + kRedBytes];
   uint8_t* const lut = smem;
   float* const xs = reinterpret_cast<float*>(smem + kTable);
-  float (*const red)[kMaxT / 64][V] = reinterpret_cast<float (*)[kMaxT / 64][V]>(smem + kTable + kXsBytes);
+  float (*const red)[kMaxT / 64][RM] = reinterpret_cast<float (*)[kMaxT / 64][RM]>(smem + kTable + kXsBytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -390,31 +428,32 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
   // Loads are branch-free: indices are clamped into the tensor, so a lane
   // past the last block or row reads valid memory whose contribution is
   // discarded (x' is zero past the last block; rows past N are not written).
-  static_assert(kDepth >= 1 && kDepth <= 3, "kDepth must be 1, 2 or 3");
-  constexpr int RB = kDepth >= 2 ? R : 1, RC = kDepth >= 3 ? R : 1;
+  // The row is wavefront-uniform and the lane's block offset is fixed, so a
+  // load is a scalar base plus one 32-bit lane offset.
   using Raw = typename Fmt::Raw;
-  Raw pa[R][J], pb[RB][J], pc[RC][J];
+  Raw ps[kDepth][R][J];
+  uint32_t boff[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) boff[j] = min((uint32_t)(lk + j * TK), nb - 1);
   fmt.prepare();
-  auto load_tile = [&](uint32_t t, auto& p) {
+  auto load_tile = [&](uint32_t t, Raw (&p)[R][J]) {
     const uint32_t row0 = (t * S + slot) * R;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t row = min(row0 + r, N - 1);
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const uint32_t b = min((uint32_t)(lk + j * TK), nb - 1);
-        p[r][j] = fmt.load(row, nb, b);
-      }
+      for (int j = 0; j < J; ++j)   // several blocks per lane: offsets recomputed (registers are scarce)
+        p[r][j] = fmt.load(row, nb, J == 1 ? boff[j] : min((uint32_t)(lk + j * TK), nb - 1));
     }
   };
 
-  // The first kDepth tiles' weights and the activation are requested before
-  // anything else so that their latency overlaps the table fill.
   const uint32_t G = gg.G;
   uint32_t t = blockIdx.x;
   const uint32_t n = gg.q + (t < gg.r ? 1u : 0u);      // this workgroup's tile count
   const uint32_t last = t + (n - 1) * G;               // and its last tile
 
+  // The activation and the first kEarly tiles' weights are requested before
+  // anything else so that their latency overlaps the table fill.
   float xr[J][MC][32];
   ActivationStage<kMode, kStage ? kStage : 1> xst;
   if constexpr (kStage) {
@@ -422,25 +461,27 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
   } else {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const uint32_t b = min((uint32_t)(lk + j * TK), nb - 1);
 #pragma unroll
-      for (int m = 0; m < MC; ++m) load_block<kXbf16>(x + m * ldx + (size_t)b * (kXbf16 ? 64 : 128), xr[j][m]);
+      for (int m = 0; m < MC; ++m) load_block<kXbf16>(x + m * ldx + (size_t)boff[j] * (kXbf16 ? 64 : 128), xr[j][m]);
     }
   }
-  load_tile(t, pa);
-  if constexpr (kDepth >= 2) load_tile(min(t + G, last), pb);
-  if constexpr (kDepth >= 3) load_tile(min(t + 2 * G, last), pc);
+  static_for<kEarly>([&](auto ic) { load_tile(min(t + (uint32_t)ic.value * G, last), ps[ic.value]); });
 
   if constexpr (Fmt::kLut) fill_pair_lut(lut, tid, nthreads);
 
   if constexpr (kStage) {
     xst.store(nb * 32, mask, xs, tid, nthreads);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<kDepth - kEarly>([&](auto ic) {
+      load_tile(min(t + (uint32_t)(kEarly + ic.value) * G, last), ps[kEarly + ic.value]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const uint32_t b0 = (uint32_t)(lk + j * TK);
       const bool inside = b0 < nb;
-      const uint32_t b = min(b0, nb - 1);
+      const uint32_t b = boff[j];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float4 u = *reinterpret_cast<const float4*>(xs + 32 * b + 4 * (q ^ (b & 7)));
@@ -467,6 +508,11 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
         for (int i = 0; i < 32; ++i) xr[j][m][i] = inside ? xr[j][m][i] : 0.f;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<kDepth - kEarly>([&](auto ic) {
+      load_tile(min(t + (uint32_t)(kEarly + ic.value) * G, last), ps[kEarly + ic.value]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
   constexpr float kOutScale = kMode >= 2 ? kInvSqrt32 : 1.0f;
@@ -479,12 +525,11 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
   // workgroup's loads).  The tile count is uniform over the workgroup, so
   // every wavefront reaches the same barriers.
   const uint32_t t0 = t;
-  uint32_t ti = 0;
   auto flush = [&](uint32_t first, uint32_t cnt) {
     __syncthreads();
-    for (uint32_t e = tid; e < cnt * (uint32_t)(S * V); e += (uint32_t)nthreads) {
-      const uint32_t jl = e / (uint32_t)(S * V), rem = e - jl * (uint32_t)(S * V);
-      const int s2 = (int)rem / V, v2 = (int)rem % V;
+    for (uint32_t e = tid; e < cnt * (uint32_t)(S * RM); e += (uint32_t)nthreads) {
+      const uint32_t jl = e / (uint32_t)(S * RM), rem = e - jl * (uint32_t)(S * RM);
+      const int s2 = (int)rem / RM, v2 = (int)rem % RM;
       const uint32_t li = first + jl;
       const uint32_t row = ((t0 + li * G) * S + s2) * R + v2 / MC;
       if (row < N) {
@@ -496,84 +541,92 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
     __syncthreads();                        // the ring slots are rewritten next
   };
 
-  auto do_tile = [&](uint32_t tt, const auto& p) {
-    float v[V];
+  // Tiles i .. i + U - 1 of this workgroup's list in one pass of the loop:
+  // tile i + u is computed from register set u % kDepth (when it exists),
+  // which is then reloaded with tile i + u + kDepth.  The reloads are
+  // unconditional, with the tile index clamped to `last` (the clamped loads
+  // at the end re-read the last tile, cache hits, and are discarded), so
+  // every path into a use of a register set carries the same loads and the
+  // compiler's wait counts stay exact.
+  // Tiles i .. i + U - 1 of this workgroup's list in one pass of the loop:
+  // tile i + u is computed from register set u % kDepth, which is then
+  // reloaded with tile i + u + kDepth.  The reloads are unconditional, with
+  // the tile index clamped to `last` (the clamped loads at the end re-read
+  // the last tile, cache hits, and are discarded), so every path into a use
+  // of a register set carries the same loads and the compiler's wait counts
+  // stay exact.
+  float acc[V];
+  uint32_t i = 0;
+  for (; i + U <= n; i += U) {
+    static_for<U>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int set = u % kDepth, g = u % T;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float acc[MC];
+      for (int r = 0; r < R; ++r) {
+        float a[MC];
 #pragma unroll
-      for (int m = 0; m < MC; ++m) acc[m] = 0.f;
+        for (int m = 0; m < MC; ++m) a[m] = 0.f;
 #pragma unroll
-      for (int j = 0; j < J; ++j) fmt.template decode<MC>(p[r][j], xr[j], lut, laneoff, acc);
+        for (int j = 0; j < J; ++j) fmt.template decode<MC>(ps[set][r][j], xr[j], lut, laneoff, a);
 #pragma unroll
-      for (int m = 0; m < MC; ++m) v[r * MC + m] = acc[m];
-    }
-    wave_reduce<V>(v, lane);
-    const uint32_t row0 = (tt * S + slot) * R;
-    const bool writer = (lane & (64 / V - 1)) == 0;
-    const int vi = lane / (64 / V);
-    if (WK == 1) {
-      if (writer) {
-        const uint32_t row = row0 + vi / MC;
-        if (row < N) y[(vi % MC) * ldy + row] = v[0] * kOutScale;
+        for (int m = 0; m < MC; ++m) acc[(g * R + r) * MC + m] = a[m];
       }
-    } else {
-      if (writer) red[ti % kRing][slot * WK + wk][vi] = v[0];
-      ++ti;
-      if (ti % kRing == 0) flush(ti - kRing, kRing);
-    }
-  };
-
-  // Every wavefront walks its n tiles t0, t0 + G, ..., last and keeps the
-  // loads of the next kDepth - 1 tiles in flight: a register set is
-  // reloaded as soon as its tile has been computed.  The loads are
-  // unconditional, with the tile index clamped to `last`, and the loop runs a
-  // trip count fixed up front with the remainder after it (no exit from the
-  // middle of the body): every path that reaches a use of a register set then
-  // carries the same loads, so the compiler's wait counts stay exact.  (A
-  // conditional load or a mid-body exit makes it wait for every outstanding
-  // load, the prefetches included.)  The clamped loads at the end re-read the
-  // last tile (cache hits) and are discarded.
-  if constexpr (kDepth == 1) {
-    for (uint32_t i = 1; i < n; ++i) {
-      do_tile(t, pa);
-      t += G;
-      load_tile(t, pa);
-    }
-    do_tile(t, pa);
-  } else if constexpr (kDepth == 2) {
-    uint32_t i = 0;
-    for (; i + 2 <= n; i += 2) {
-      do_tile(t, pa);
-      load_tile(min(t + 2 * G, last), pa);
+      load_tile(min(t + (uint32_t)(u + kDepth) * G, last), ps[set]);
       __builtin_amdgcn_sched_barrier(0);     // keep the reload ahead of the next tile's math
-      t += G;
-      do_tile(t, pb);
-      load_tile(min(t + 2 * G, last), pb);
-      __builtin_amdgcn_sched_barrier(0);
-      t += G;
-    }
-    if (i < n) do_tile(t, pa);
-  } else {
-    uint32_t i = 0;
-    for (; i + 3 <= n; i += 3) {
-      do_tile(t, pa);
-      load_tile(min(t + 3 * G, last), pa);
-      __builtin_amdgcn_sched_barrier(0);
-      t += G;
-      do_tile(t, pb);
-      load_tile(min(t + 3 * G, last), pb);
-      __builtin_amdgcn_sched_barrier(0);
-      t += G;
-      do_tile(t, pc);
-      load_tile(min(t + 3 * G, last), pc);
-      __builtin_amdgcn_sched_barrier(0);
-      t += G;
-    }
-    if (i < n) do_tile(t, pa);
-    if (i + 1 < n) do_tile(t + G, pb);
+      if constexpr (g == T - 1) {
+        // v[0] of lane l now holds value vi of the group (V = 8: (l >> 3) & 7,
+        // V = 4: (l >> 4) & 3): tile g0 + vi / RM, row (vi / MC) % R,
+        // activation row vi % MC.
+        wave_reduce<V>(acc, lane);
+        const uint32_t g0 = i + (uint32_t)(u - (T - 1));   // first tile of the group
+        const int vi = (lane / (64 / V)) & (V - 1);
+        const uint32_t tile_i = g0 + (uint32_t)(vi / RM);
+        const int rv = vi % RM;
+        if ((lane & (64 / V - 1)) == 0) {
+          const uint32_t row = ((t0 + tile_i * G) * S + slot) * R + rv / MC;
+          if (WK == 1) {
+            if (row < N) y[(rv % MC) * ldy + row] = acc[0] * kOutScale;
+          } else {
+            red[tile_i % kRing][slot * WK + wk][rv] = acc[0];
+          }
+        }
+        if (WK > 1 && (g0 + (uint32_t)T) % kRing == 0) flush(g0 + (uint32_t)T - kRing, kRing);
+      }
+    });
+    t += (uint32_t)U * G;
   }
-  if (WK > 1 && ti % kRing != 0) flush(ti - ti % kRing, ti % kRing);
+  // The remaining tiles (fewer than U <= kDepth + 1, so all of them are in
+  // registers already: set s holds tile i + s), each reduced on its own.
+  static_assert(U <= kDepth + 1, "the tail must be in registers");
+  static_for<U - 1>([&](auto sc) {
+    constexpr int s2 = decltype(sc)::value;
+    if (i + s2 < n) {
+      float v[RM];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float a[MC];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) a[m] = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) fmt.template decode<MC>(ps[s2][r][j], xr[j], lut, laneoff, a);
+#pragma unroll
+        for (int m = 0; m < MC; ++m) v[r * MC + m] = a[m];
+      }
+      wave_reduce<RM>(v, lane);
+      const uint32_t ti = i + s2;
+      const int vi = lane / (64 / RM);
+      if ((lane & (64 / RM - 1)) == 0) {
+        const uint32_t row = ((t + (uint32_t)s2 * G) * S + slot) * R + vi / MC;
+        if (WK == 1) {
+          if (row < N) y[(vi % MC) * ldy + row] = v[0] * kOutScale;
+        } else {
+          red[ti % kRing][slot * WK + wk][vi] = v[0];
+        }
+      }
+      if (WK > 1 && (ti + 1) % kRing == 0) flush(ti + 1 - kRing, kRing);
+    }
+  });
+  if (WK > 1 && n % kRing != 0) flush(n - n % kRing, n % kRing);
 }
 
 // ---------------------------------------------------------------------------
@@ -634,7 +687,7 @@ uint32_t resident_grid(const void* kernel, int threads) {
   return g;
 }
 
-template <typename Fmt, int J, int R, int MC, int kMaxT, int kDepth, int kStage = 0>
+template <typename Fmt, int J, int R, int MC, int kMaxT, int kDepth, int kEarly, int kStage = 0>
 void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int64_t ldx, int mode,
                 float* y, int64_t ldy, const Plan& pl, hipStream_t s) {
   const int S = pl.threads / pl.TK;
@@ -645,10 +698,10 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
   // leave half the chip idle for the second half of the launch).
   const void* kern = nullptr;
   switch (mode) {
-    case 0: kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 0, kMaxT, kDepth, kStage>; break;
-    case 1: kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 1, kMaxT, kDepth, kStage>; break;
-    case 2: if constexpr (Fmt::kLut) kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 2, kMaxT, kDepth, kStage>; break;
-    default: if constexpr (Fmt::kLut) kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 3, kMaxT, kDepth, kStage>; break;
+    case 0: kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 0, kMaxT, kDepth, kEarly, kStage>; break;
+    case 1: kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 1, kMaxT, kDepth, kEarly, kStage>; break;
+    case 2: if constexpr (Fmt::kLut) kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 2, kMaxT, kDepth, kEarly, kStage>; break;
+    default: if constexpr (Fmt::kLut) kern = (const void*)&gemv_kernel<Fmt, J, R, MC, 3, kMaxT, kDepth, kEarly, kStage>; break;
   }
   if (!kern) return;                         // rotation modes exist for TQ4_1S only (the entry points check)
   const uint32_t cap = resident_grid(kern, pl.threads);
@@ -662,7 +715,7 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
   gg.q = tiles / grid;
   gg.r = tiles % grid;
 #define TQ_GEMV_LAUNCH(M_)                                                                                     \
-  hipLaunchKernelGGL((gemv_kernel<Fmt, J, R, MC, M_, kMaxT, kDepth, kStage>), dim3(grid), dim3(pl.threads), 0, s, \
+  hipLaunchKernelGGL((gemv_kernel<Fmt, J, R, MC, M_, kMaxT, kDepth, kEarly, kStage>), dim3(grid), dim3(pl.threads), 0, s, \
                      fmt, N, nb, mask, x, ldx, y, ldy, gg)
   switch (mode) {
     case 0: TQ_GEMV_LAUNCH(0); break;
@@ -674,14 +727,14 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
 }
 
 // Decode GEMV shape, measured on MI355X over the Llama-3-8B and 70B decode
-// layers: one tile of loads in flight ahead of the one being computed, x'
-// staged in LDS, the fewest K-blocks per lane that fit a row into a
-// 1024-thread workgroup, and one row per wavefront per tile -- except when a
-// single round of two-row tiles already covers the matrix (one tile per
-// workgroup, nothing to pipeline), where two rows per wavefront halve the
-// per-row reduction work.  (Llama-3-8B decode groups, graph-timed: q|k|v
-// 7.4 -> 6.6 us, gate|up 16.8 -> 15.6 us with one row; o 5.7 us with two.)
-constexpr int kGemvDepth = 2;
+// layers: x' staged in LDS, the fewest K-blocks per lane that fit a row into
+// a 1024-thread workgroup, and one row per wavefront per tile with four
+// register sets of tile loads, only the first requested before the
+// activation has arrived (graph-timed, Llama-3-8B groups: q|k|v 6.7 -> 5.8
+// us, gate|up 15.6 -> 15.0 us, down 10.8 -> 10.3 us against two sets both
+// requested at the start) -- except when a single round of two-row tiles
+// already covers the matrix (one tile per workgroup, nothing to pipeline),
+// where two rows per wavefront and one register set are used.
 constexpr bool kGemvStage = true;
 constexpr int kGemvMinJ = 1;
 
@@ -691,19 +744,20 @@ void launch_gemv_jr(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, cons
   // Groups of 4 elements each thread stages (a power of two, at most 8).
   const uint32_t K = nb * 32, per = 4u * (uint32_t)pl.threads;
   const uint32_t passes = (K + per - 1) / per;
-  constexpr int D = kGemvDepth;
+  constexpr int D = R == 1 ? 4 : 1;
   if constexpr (J <= 2) {
     if (kGemvStage && K <= (uint32_t)kStageFloats && passes <= 8) {
-      if (passes <= 1) launch_cfg<Fmt, J, R, 1, 1024, D, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
-      else if (passes <= 2) launch_cfg<Fmt, J, R, 1, 1024, D, 2>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
-      else if (passes <= 4) launch_cfg<Fmt, J, R, 1, 1024, D, 4>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
-      else launch_cfg<Fmt, J, R, 1, 1024, D, 8>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      if (passes <= 1) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else if (passes <= 2) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 2>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else if (passes <= 4) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 4>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+      else launch_cfg<Fmt, J, R, 1, 1024, D, 1, 8>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
       return;
     }
   }
   // Larger K: every lane loads (and rotates) its own blocks; the loads of the
-  // next tile only fit in registers (without spills) at one block per lane.
-  launch_cfg<Fmt, J, R, 1, 1024, J == 1 ? D : 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
+  // next tiles only fit in registers (without spills) at one block per lane.
+  constexpr int DJ = J == 1 ? D : 1;
+  launch_cfg<Fmt, J, R, 1, 1024, DJ, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
 }
 
 template <typename Fmt, int J>
@@ -743,23 +797,23 @@ void launch_gemm_valu_fmt(const Fmt& fmt, uint32_t N, uint32_t nb, int64_t M, co
     float* ym = y + m0 * ldy;
     if (left >= 4 && nb <= 256) {
       const Plan pl = plan_for(nb, 256, 1);
-      launch_cfg<Fmt, 1, 2, 4, 256, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      launch_cfg<Fmt, 1, 2, 4, 256, 2, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
       m0 += 4;
     } else if (left >= 2 && nb <= 512) {
       const Plan pl = plan_for(nb, 512, 1);
-      launch_cfg<Fmt, 1, 2, 2, 512, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      launch_cfg<Fmt, 1, 2, 2, 512, 2, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
       m0 += 2;
     } else if (left >= 2 && nb <= 1024) {
       const Plan pl = plan_for(nb, 1024, 1);
-      launch_cfg<Fmt, 1, 1, 2, 1024, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
+      launch_cfg<Fmt, 1, 1, 2, 1024, 2, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s);
       m0 += 2;
     } else {
       const Plan pl = plan_for(nb, 1024, min_j(nb, 1024));
       switch (pl.J) {
-        case 1: launch_cfg<Fmt, 1, 2, 1, 1024, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
-        case 2: launch_cfg<Fmt, 2, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
-        case 3: launch_cfg<Fmt, 3, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
-        default: launch_cfg<Fmt, 4, 2, 1, 1024, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        case 1: launch_cfg<Fmt, 1, 2, 1, 1024, 2, 2>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        case 2: launch_cfg<Fmt, 2, 2, 1, 1024, 1, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        case 3: launch_cfg<Fmt, 3, 2, 1, 1024, 1, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
+        default: launch_cfg<Fmt, 4, 2, 1, 1024, 1, 1>(fmt, N, nb, 0u, xm, ldx_bytes, mode, ym, ldy, pl, s); break;
       }
       m0 += 1;
     }
