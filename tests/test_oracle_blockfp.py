@@ -126,3 +126,79 @@ def test_blockfp_reconstruction_error_scale():
     assert 0.005 < e4 < 0.02          # 4-bit float with E4M3 block scales
     assert e6 < e4 / 2                # 6 bits: two more mantissa/exponent bits
     assert bf.bytes_per_weight("nvfp4") == 0.5625 and bf.bytes_per_weight("mxfp6") == 0.78125
+
+
+# ----------------------------------------------------------------------------
+# gemm_deq_o64: the float64 product that judges every NVFP4 / MXFP6 GEMV/GEMM
+# (quantizer-tool page, "目前能实现的部分功能": the weights are stored in these
+# formats and multiplied as their dequantized values).  Pinned by special
+# cases that do not restate its formula: one-hot activations select columns,
+# rows scale linearly, zero weights give zero, and a tiny explicit loop.
+# ----------------------------------------------------------------------------
+
+def _bf_weights(fmt, n, k, seed):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
+    W[0, 3] = 4.0 / np.sqrt(k)                                 # one outlier so the block scales differ
+    if fmt == "nvfp4":
+        c, s, st = bf.nvfp4_quantize_o32(W)
+        return bf.nvfp4_dequantize_o64(c, s, st)
+    c, s = bf.mxfp6_quantize_o32(W)
+    return bf.mxfp6_dequantize_o64(c, s)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+def test_gemm_deq_one_hot_selects_columns(fmt):
+    n, k = 24, 96                                               # non-square: a transposed product cannot pass
+    Wd = _bf_weights(fmt, n, k, 1)
+    cols = [0, 5, 31, 64, 95]
+    X = np.zeros((len(cols), k))
+    for m, j in enumerate(cols):
+        X[m, j] = 1.0
+    Y, A = bf.gemm_deq_o64(Wd, X)
+    assert Y.shape == (len(cols), n) and A.shape == (len(cols), n)
+    for m, j in enumerate(cols):
+        np.testing.assert_array_equal(Y[m], Wd[:, j])           # exact: one product per output
+        np.testing.assert_array_equal(A[m], np.abs(Wd[:, j]))   # the tolerance scale keeps the magnitude
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+def test_gemm_deq_rows_scale_and_m1(fmt):
+    n, k = 40, 64
+    Wd = _bf_weights(fmt, n, k, 2)
+    x = np.random.default_rng(3).standard_normal(k)
+    y1, a1 = bf.gemm_deq_o64(Wd, x)                              # a vector is one activation row
+    assert y1.shape == (1, n)
+    Y2, A2 = bf.gemm_deq_o64(Wd, np.stack([x, 2.0 * x, -x]))
+    tol = 1e-13 * a1[0]                                         # BLAS may sum one row and three rows in different orders
+    np.testing.assert_allclose(Y2[0], y1[0], rtol=0, atol=tol.max())
+    np.testing.assert_allclose(Y2[1], 2.0 * y1[0], rtol=0, atol=2 * tol.max())
+    np.testing.assert_allclose(Y2[2], -y1[0], rtol=0, atol=tol.max())
+    np.testing.assert_allclose(A2[2], a1[0], rtol=1e-13)        # |-x| = |x|
+    np.testing.assert_allclose(A2[1], 2.0 * a1[0], rtol=1e-13)
+
+
+def test_gemm_deq_zero_weights_and_scale_bounds():
+    c, s, st = bf.nvfp4_quantize_o32(np.zeros((6, 32), np.float32))
+    Wz = bf.nvfp4_dequantize_o64(c, s, st)
+    Y, A = bf.gemm_deq_o64(Wz, np.random.default_rng(4).standard_normal((3, 32)))
+    assert not Y.any() and not A.any()
+    Wd = _bf_weights("mxfp6", 16, 64, 5)
+    X = np.random.default_rng(6).standard_normal((4, 64))
+    Y, A = bf.gemm_deq_o64(Wd, X)
+    assert np.all(A >= np.abs(Y))                               # triangle inequality
+    assert np.any(A > np.abs(Y) * (1 + 1e-6))                   # mixed signs cancel in Y, not in A
+    Yp, Ap = bf.gemm_deq_o64(np.abs(Wd), np.abs(X))
+    np.testing.assert_allclose(Ap, Yp, rtol=1e-15)              # nonnegative operands: A equals Y
+
+
+def test_gemm_deq_tiny_explicit_loop():
+    Wd = _bf_weights("nvfp4", 3, 32, 7)
+    X = np.random.default_rng(8).standard_normal((2, 32))
+    Y, A = bf.gemm_deq_o64(Wd, X)
+    import math
+    for m in range(2):
+        for nn in range(3):
+            terms = [float(X[m, kk]) * float(Wd[nn, kk]) for kk in range(32)]
+            assert Y[m, nn] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-15)
+            assert A[m, nn] == pytest.approx(math.fsum(abs(t) for t in terms), rel=1e-13)

@@ -77,3 +77,26 @@ def test_nvfp4_wrong_tensor_scale_is_caught(monkeypatch):
 def test_mxfp6_wrong_emax_is_caught(monkeypatch):
     monkeypatch.setattr(bf, "E3M2_EMAX", 2)
     assert _fails(tbf.test_mxfp6_closed_form_scale)
+
+
+def test_gemm_deq_transposed_product_is_caught(monkeypatch):
+    real = bf.gemm_deq_o64
+
+    def wrong(W_deq, X):                # W_deq used untransposed (a square-only mistake)
+        Xa = np.atleast_2d(np.asarray(X, dtype=np.float64))
+        Wt = np.asarray(W_deq).reshape(W_deq.shape[1], W_deq.shape[0])
+        return Xa @ Wt, np.abs(Xa) @ np.abs(Wt)
+
+    monkeypatch.setattr(bf, "gemm_deq_o64", wrong)
+    assert _fails(tbf.test_gemm_deq_tiny_explicit_loop,
+                  lambda: tbf.test_gemm_deq_one_hot_selects_columns("nvfp4"))
+    monkeypatch.setattr(bf, "gemm_deq_o64", real)
+
+
+def test_gemm_deq_dropped_abs_is_caught(monkeypatch):
+    def wrong(W_deq, X):                # the tolerance scale without absolute values
+        Xa = np.atleast_2d(np.asarray(X, dtype=np.float64))
+        return Xa @ W_deq.T, np.abs(Xa @ W_deq.T)
+
+    monkeypatch.setattr(bf, "gemm_deq_o64", wrong)
+    assert _fails(tbf.test_gemm_deq_zero_weights_and_scale_bounds, tbf.test_gemm_deq_tiny_explicit_loop)
