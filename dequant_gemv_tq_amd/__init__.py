@@ -117,6 +117,47 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(ok: bool, msg: str):
+    if not ok:
+        raise ValueError(msg)
+
+
+def _dense(t: torch.Tensor, name: str, dtypes, shape):
+    """Check a tensor the C ABI reads as dense rows: dtype, exact shape, contiguity."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.dtype in dtypes, f"{name}: dtype {t.dtype} not accepted ({', '.join(str(d) for d in dtypes)})")
+    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _same_device(ref: torch.Tensor, *named):
+    for t, name in named:
+        if t is not None:
+            _need(t.device == ref.device, f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _rows(t: torch.Tensor, name: str, dtypes, rows: int, cols: int):
+    """Check a 2-D tensor passed with a leading dimension: [rows, cols], unit column stride."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.dtype in dtypes, f"{name}: dtype {t.dtype} not accepted")
+    _need(t.dim() == 2 and tuple(t.shape) == (rows, cols), f"{name}: shape {tuple(t.shape)}, expected {(rows, cols)}")
+    _need(t.stride(1) == 1 and t.stride(0) >= cols, f"{name} must have unit column stride and row stride >= {cols}")
+
+
+_SCALE16 = (torch.int16, torch.float16)
+
+
+def _tq4_weights(packed: torch.Tensor, scales: torch.Tensor):
+    """(N, K) of a TQ4_1S pair: packed uint8 [N, K/2], scales fp16 bits [N, K/16], both dense."""
+    _need(isinstance(packed, torch.Tensor) and packed.dim() == 2, "packed must be a 2-D uint8 tensor [N, K/2]")
+    N, K = packed.shape[0], packed.shape[1] * 2
+    _dense(packed, "packed", (torch.uint8,), (N, K // 2))
+    _dense(scales, "scales", _SCALE16, (N, K // 16))
+    _same_device(packed, (scales, "scales"))
+    _dev(packed, "packed")
+    return N, K
+
+
 # ----------------------------------------------------------------------------
 # host constants
 # ----------------------------------------------------------------------------
@@ -160,6 +201,9 @@ def quantize(W: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None, rsf:
         scales = torch.empty((N, K // 16), dtype=torch.int16, device=W.device)
     else:
         packed, scales = out
+        _dense(packed, "out[0]", (torch.uint8,), (N, K // 2))
+        _dense(scales, "out[1]", _SCALE16, (N, K // 16))
+        _same_device(W, (packed, "out[0]"), (scales, "out[1]"))
     fn = "tq_quantize_rsf" if rsf else "tq_quantize"
     st = getattr(lib(), fn)(_ptr(W), _dtype_code(W, "W"), N, K, W.stride(0), sign_mask & 0xFFFFFFFF,
                             _ptr(packed), _ptr(scales), _stream())
@@ -169,9 +213,10 @@ def quantize(W: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None, rsf:
 
 def dequantize(packed: torch.Tensor, scales: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK,
                dtype=torch.float32, out=None):
-    _dev(packed, "packed")
-    N, K = packed.shape[0], packed.shape[1] * 2
+    N, K = _tq4_weights(packed, scales)
     W = torch.empty((N, K), dtype=dtype, device=packed.device) if out is None else out
+    _rows(W, "out", (torch.float32, torch.bfloat16), N, K)
+    _same_device(packed, (W, "out"))
     st = lib().tq_dequantize(_ptr(packed), _ptr(scales), N, K, sign_mask & 0xFFFFFFFF, _ptr(W),
                              _dtype_code(W, "out"), W.stride(0), _stream())
     _check("tq_dequantize", st)
@@ -193,12 +238,13 @@ def rotate(x: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, dtype=torch.floa
 def gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, rotated: bool = False,
          sign_mask: int = DEFAULT_SIGN_MASK, out=None):
     """y [N] float32 = W_deq x.  x: [K] raw (fp32/bf16) or, with rotated=True, x' fp32."""
-    _dev(packed, "packed")
+    N, K = _tq4_weights(packed, scales)
     _dev(x, "x")
-    N, K = packed.shape[0], packed.shape[1] * 2
     if x.numel() != K or not x.is_contiguous():
         raise ValueError("x must be a contiguous vector of length K")
     y = torch.empty(N, dtype=torch.float32, device=packed.device) if out is None else out
+    _dense(y, "out", (torch.float32,), (N,))
+    _same_device(packed, (x, "x"), (y, "out"))
     st = lib().tq_gemv(_ptr(packed), _ptr(scales), N, K, sign_mask & 0xFFFFFFFF, _ptr(x), _dtype_code(x, "x"),
                        1 if rotated else 0, _ptr(y), _stream())
     _check("tq_gemv", st)
@@ -207,13 +253,14 @@ def gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, rotated: b
 
 def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=None):
     """Y [M, N] float32 = X' Q^T with pre-rotated activations x_rot [M, K] (bf16 or fp32)."""
-    _dev(packed, "packed")
+    N, K = _tq4_weights(packed, scales)
     _dev(x_rot, "x_rot")
-    N, K = packed.shape[0], packed.shape[1] * 2
     M = x_rot.shape[0]
     if x_rot.dim() != 2 or x_rot.shape[1] != K or x_rot.stride(1) != 1:
         raise ValueError("x_rot must be [M, K] with unit column stride")
     y = torch.empty((M, N), dtype=torch.float32, device=packed.device) if out is None else out
+    _rows(y, "out", (torch.float32,), M, N)
+    _same_device(packed, (x_rot, "x_rot"), (y, "out"))
     st = lib().tq_gemm(_ptr(packed), _ptr(scales), N, K, M, _ptr(x_rot), _dtype_code(x_rot, "x_rot"),
                        x_rot.stride(0), _ptr(y), y.stride(0), _stream())
     _check("tq_gemm", st)
@@ -229,8 +276,8 @@ def blockfp_quantize(fmt: str, W: torch.Tensor, rsf: bool = False):
 
     ``rsf=True`` runs the RSF-lite block-scale search (tq_blockfp_quantize_rsf)."""
     _dev(W, "W")
-    if not W.is_contiguous():
-        raise ValueError("W must be contiguous")
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D tensor")
     f = FORMATS[fmt]
     N, K = W.shape
     if fmt == "nvfp4":
@@ -250,16 +297,28 @@ def blockfp_quantize(fmt: str, W: torch.Tensor, rsf: bool = False):
 def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale, x: torch.Tensor,
                  out=None):
     """Y [M, N] float32 = X W_deq^T (x: [M, K] or [K], fp32/bf16)."""
-    _dev(codes, "codes")
-    _dev(x, "x")
     f = FORMATS[fmt]
+    _need(isinstance(codes, torch.Tensor) and codes.dim() == 2, "codes must be a 2-D uint8 tensor")
     N = codes.shape[0]
     K = codes.shape[1] * 2 if fmt == "nvfp4" else codes.shape[1] * 4 // 3
+    _dense(codes, "codes", (torch.uint8,), (N, K // 2 if fmt == "nvfp4" else 3 * K // 4))
+    _dense(block_scales, "block_scales", (torch.uint8,), (N, K // 16 if fmt == "nvfp4" else K // 32))
+    if fmt == "nvfp4":
+        _need(tensor_scale is not None, "NVFP4 needs its tensor scale")
+        _dense(tensor_scale, "tensor_scale", (torch.float32,), (1,))
+    _same_device(codes, (block_scales, "block_scales"), (tensor_scale, "tensor_scale"))
+    _dev(codes, "codes")
+    _dev(x, "x")
     x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    _need(x2.shape[1] == K and x2.stride(1) == 1, f"x must be [M, {K}] or [{K}] with unit column stride")
     M = x2.shape[0]
     y = torch.empty((M, N), dtype=torch.float32, device=codes.device) if out is None else out
+    y2 = y if y.dim() == 2 else y.reshape(1, -1)
+    _rows(y2, "out", (torch.float32,), M, N)
+    _same_device(codes, (x2, "x"), (y2, "out"))
+    y = y2 if y.dim() == 2 else y
     st = lib().tq_blockfp_gemm(f, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), N, K, M, _ptr(x2),
-                               _dtype_code(x2, "x"), x2.stride(0), _ptr(y), y.stride(0), _stream())
+                               _dtype_code(x2, "x"), x2.stride(0), _ptr(y2), y2.stride(0), _stream())
     _check("tq_blockfp_gemm", st)
     return y if x.dim() == 2 else y.reshape(-1)
 
@@ -270,13 +329,15 @@ def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tens
 
 def transcode_q8(packed: torch.Tensor, scales: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, out=None):
     """TQ4_1S (packed, scales) -> (codes int8 [N, K], q8_scales int16 [N, K/32] = fp16 bits per block)."""
-    _dev(packed, "packed")
-    N, K = packed.shape[0], packed.shape[1] * 2
+    N, K = _tq4_weights(packed, scales)
     if out is None:
         codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
         qs = torch.empty((N, K // 32), dtype=torch.int16, device=packed.device)
     else:
         codes, qs = out
+        _dense(codes, "out[0]", (torch.int8,), (N, K))
+        _dense(qs, "out[1]", _SCALE16, (N, K // 32))
+        _same_device(packed, (codes, "out[0]"), (qs, "out[1]"))
     st = lib().tq_transcode_q8(_ptr(packed), _ptr(scales), N, K, sign_mask & 0xFFFFFFFF, _ptr(codes), _ptr(qs),
                                _stream())
     _check("tq_transcode_q8", st)
@@ -285,12 +346,18 @@ def transcode_q8(packed: torch.Tensor, scales: torch.Tensor, sign_mask: int = DE
 
 def q8_gemv(codes: torch.Tensor, q8_scales: torch.Tensor, x: torch.Tensor, out=None):
     """y [N] float32 from transcoded int8 weights and the activation x [K] (fp32/bf16, not rotated)."""
+    _need(isinstance(codes, torch.Tensor) and codes.dim() == 2, "codes must be a 2-D int8 tensor [N, K]")
+    N, K = codes.shape
+    _dense(codes, "codes", (torch.int8,), (N, K))
+    _dense(q8_scales, "q8_scales", _SCALE16, (N, K // 32))
+    _same_device(codes, (q8_scales, "q8_scales"))
     _dev(codes, "codes")
     _dev(x, "x")
-    N, K = codes.shape
     if x.numel() != K or not x.is_contiguous():
         raise ValueError("x must be a contiguous vector of length K")
     y = torch.empty(N, dtype=torch.float32, device=codes.device) if out is None else out
+    _dense(y, "out", (torch.float32,), (N,))
+    _same_device(codes, (x, "x"), (y, "out"))
     st = lib().tq_q8_gemv(_ptr(codes), _ptr(q8_scales), N, K, _ptr(x), _dtype_code(x, "x"), _ptr(y), _stream())
     _check("tq_q8_gemv", st)
     return y
@@ -353,6 +420,9 @@ def kv_dequantize_v(packed: torch.Tensor, norms: torch.Tensor, sign=None):
     _dev(packed, "packed")
     d = packed.shape[-1] * 2
     n = packed.numel() // (d // 2)
+    _dense(packed, "packed", (torch.uint8,), packed.shape)
+    _dense(norms, "norms", _SCALE16, packed.shape[:-1])
+    _same_device(packed, (norms, "norms"))
     sign = kv_sign_from_seed(0) if sign is None else sign
     out = torch.empty(packed.shape[:-1] + (d,), dtype=torch.float32, device=packed.device)
     st = lib().tq_kv_dequantize_v(_ptr(packed), _ptr(norms), n, d, sign, _ptr(out), _stream())
@@ -370,15 +440,27 @@ def attn_decode(q: torch.Tensor, lengths: torch.Tensor, k_codes, k_scales, v_pac
     [B, Hkv, T_max, ...] from kv_quantize_k / kv_quantize_v -> o [B, Hq, 128] float32."""
     for t, name in ((q, "q"), (lengths, "lengths"), (k_codes, "k_codes"), (v_packed, "v_packed")):
         _dev(t, name)
+    _need(q.dim() == 3 and q.is_contiguous(), "q must be a contiguous [B, Hq, 128] tensor")
     B, Hq, d = q.shape
+    _need(k_codes.dim() == 4 and k_codes.shape[0] == B and k_codes.shape[-1] == d,
+          "k_codes must be [B, Hkv, T_max, 128]")
     _, Hkv, T_max, _ = k_codes.shape
-    if lengths.dtype != torch.int32 or lengths.numel() != B:
-        raise ValueError("lengths must be int32 [B]")
+    if lengths.dtype != torch.int32 or lengths.numel() != B or not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous int32 [B] tensor")
+    _dense(k_codes, "k_codes", (torch.int8,), (B, Hkv, T_max, d))
+    _dense(k_scales, "k_scales", _SCALE16, (B, Hkv, T_max, d // 32))
+    _dense(v_packed, "v_packed", (torch.uint8,), (B, Hkv, T_max, d // 2))
+    _dense(v_norms, "v_norms", _SCALE16, (B, Hkv, T_max))
     sign = kv_sign_from_seed(0) if sign is None else sign
     o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    _dense(o, "out", (torch.float32,), (B, Hq, d))
     ws_bytes = attn_workspace_bytes(B, Hq, T_max)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=q.device)
+    _need(workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= ws_bytes,
+          f"workspace must be a contiguous buffer of at least {ws_bytes} bytes")
+    _same_device(q, (lengths, "lengths"), (k_codes, "k_codes"), (k_scales, "k_scales"), (v_packed, "v_packed"),
+                 (v_norms, "v_norms"), (o, "out"), (workspace, "workspace"))
     st = lib().tq_attn_decode(_ptr(q), _dtype_code(q, "q"), B, Hq, Hkv, d, T_max, _ptr(lengths), _ptr(k_codes),
                               _ptr(k_scales), _ptr(v_packed), _ptr(v_norms), sign, _ptr(o), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream())

@@ -211,7 +211,7 @@ tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int6
   if (d != 128 || Hq % Hkv) return TQ_ESHAPE;
   const int64_t G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ESHAPE;
-  if (B > 65535 || Hkv > 65535 || Hq > 65535 || T_max > ((int64_t)1 << 31)) return TQ_ESHAPE;
+  if (B > 65535 || Hkv > 65535 || Hq > 65535 || T_max > (int64_t)INT32_MAX) return TQ_ESHAPE;
   if (ws_bytes < tq::attn_workspace_bytes(B, Hq, T_max)) return TQ_EINVAL;
   if (!float_or_bf16(qt)) return TQ_EDTYPE;
   if (!aligned(q, 16) || !aligned(lengths, 4) || !aligned(k_codes, 16) || !aligned(k_scales, 2) ||

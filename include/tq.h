@@ -329,7 +329,8 @@ size_t tq_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t T_max);
  *   o        float32 [B, Hq, 128] (output).
  *   workspace device, >= tq_attn_workspace_bytes(B, Hq, T_max) bytes; the
  *            call owns it until the stream reaches the end of the call.
- * G must be 1, 2, 4 or 8; B, Hq, Hkv <= 65535.
+ * G must be 1, 2, 4 or 8; B, Hq, Hkv <= 65535; T_max <= 2^31 - 1 (the kernels
+ * index tokens with 32-bit signed integers).
  * Errors: TQ_EINVAL (null, non-positive sizes, workspace too small),
  * TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,

@@ -158,6 +158,8 @@ def test_other_calls_reject_before_launch():
     assert L.tq_attn_decode(*args(d=64)) == ESHAPE
     assert L.tq_attn_decode(*args(wsb=ws - 4)) == EINVAL             # workspace too small
     assert L.tq_attn_decode(*args(T=0)) == EINVAL
+    big = L.tq_attn_workspace_bytes(1, 32, 1 << 31)
+    assert L.tq_attn_decode(*args(T=1 << 31, wsb=big)) == ESHAPE      # T_max > INT32_MAX
     assert L.tq_attn_decode(*args(qt=F16)) == EDTYPE
     assert L.tq_attn_decode(*args(q=_p(GOOD + 8))) == EALIGN
 
@@ -169,3 +171,40 @@ def test_binding_refuses_cpu_tensors():
         tqa.quantize(w)
     with pytest.raises(ValueError):
         tqa.gemv(torch.zeros(4, 32, dtype=torch.uint8), torch.zeros(4, 4, dtype=torch.int16), torch.zeros(64))
+
+
+def test_binding_checks_tensor_shapes_before_any_call():
+    """Mis-shaped, strided or mistyped weight tensors are refused by the binding itself (CPU tensors:
+    the shape check comes first, so nothing reaches libtq)."""
+    import torch
+    N, K = 8, 64
+    packed = torch.zeros(N, K // 2, dtype=torch.uint8)
+    scales = torch.zeros(N, K // 16, dtype=torch.int16)
+    x = torch.zeros(K)
+    with pytest.raises(ValueError, match="scales: shape"):
+        tqa.gemv(packed, torch.zeros(N, K // 32, dtype=torch.int16), x)
+    with pytest.raises(ValueError, match="scales: dtype"):
+        tqa.gemv(packed, torch.zeros(N, K // 16, dtype=torch.int32), x)
+    with pytest.raises(ValueError, match="packed: dtype"):
+        tqa.gemv(packed.to(torch.int8), scales, x)
+    with pytest.raises(ValueError, match="packed must be contiguous"):
+        tqa.gemv(torch.zeros(N, K, dtype=torch.uint8)[:, ::2], scales, x)
+    with pytest.raises(ValueError, match="packed must be a 2-D"):
+        tqa.dequantize(torch.zeros(N * K // 2, dtype=torch.uint8), scales)
+    with pytest.raises(ValueError, match="GPU tensor"):          # well-formed, but on the CPU
+        tqa.gemv(packed, scales, x)
+    with pytest.raises(ValueError, match="scales: shape"):
+        tqa.gemm(packed, scales[:, :2].contiguous(), torch.zeros(4, K))
+    with pytest.raises(ValueError, match="scales: shape"):
+        tqa.transcode_q8(packed, scales[:4])
+    with pytest.raises(ValueError, match="q8_scales: shape"):
+        tqa.q8_gemv(torch.zeros(N, K, dtype=torch.int8), torch.zeros(N, K // 16, dtype=torch.int16), x)
+    with pytest.raises(ValueError, match="block_scales: shape"):
+        tqa.blockfp_gemm("nvfp4", torch.zeros(N, K // 2, dtype=torch.uint8), torch.zeros(N, K // 32, dtype=torch.uint8),
+                         torch.ones(1), x)
+    with pytest.raises(ValueError, match="tensor scale"):
+        tqa.blockfp_gemm("nvfp4", torch.zeros(N, K // 2, dtype=torch.uint8), torch.zeros(N, K // 16, dtype=torch.uint8),
+                         None, x)
+    with pytest.raises(ValueError, match="codes: shape"):
+        tqa.blockfp_gemm("mxfp6", torch.zeros(N, 3 * K // 4 + 1, dtype=torch.uint8),
+                         torch.zeros(N, K // 32, dtype=torch.uint8), None, x)
