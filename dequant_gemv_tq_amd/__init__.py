@@ -20,7 +20,7 @@ import torch  # imported before libtq so both bind to the same HIP runtime
 __all__ = [
     "TQError", "lib", "codebook", "sign_mask_from_seed", "DEFAULT_SIGN_MASK",
     "quantize", "dequantize", "rotate", "gemv", "gemm",
-    "blockfp_quantize", "blockfp_gemm", "transcode_q8", "q8_gemv", "LIB_PATH",
+    "blockfp_quantize", "blockfp_gemm", "transcode_q8", "q8_gemv", "LIB_PATH", "workspace_bytes", "stream_read",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
@@ -34,7 +34,7 @@ EXPORTED = [
     "tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
     "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
     "tq_kv_sign_from_seed", "tq_kv_quantize_k", "tq_kv_quantize_v", "tq_kv_dequantize_v", "tq_attn_workspace_bytes",
-    "tq_attn_decode",
+    "tq_attn_decode", "tq_workspace_bytes", "tq_stream_read",
 ]
 
 
@@ -70,8 +70,12 @@ def lib() -> ctypes.CDLL:
     L.tq_rotate.argtypes = [p, c_int, i64, i64, i64, u32, p, c_int, i64, p]
     L.tq_gemv.argtypes = [p, p, i64, i64, u32, p, c_int, c_int, p, p]
     L.tq_gemm.argtypes = [p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
-    L.tq_blockfp_quantize.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p]
-    L.tq_blockfp_quantize_rsf.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p]
+    L.tq_blockfp_quantize.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p, ctypes.c_size_t, p]
+    L.tq_blockfp_quantize_rsf.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p, ctypes.c_size_t, p]
+    L.tq_workspace_bytes.argtypes = [c_int, i64, i64, i64]
+    L.tq_workspace_bytes.restype = ctypes.c_size_t
+    L.tq_stream_read.argtypes = [p, ctypes.c_size_t, p, p]
+    L.tq_stream_read.restype = c_int
     L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
     L.tq_transcode_q8.argtypes = [p, p, i64, i64, u32, p, p, p]
     L.tq_q8_gemv.argtypes = [p, p, i64, i64, p, c_int, p, p]
@@ -271,25 +275,51 @@ def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=No
 # NVFP4 / MXFP6
 # ----------------------------------------------------------------------------
 
-def blockfp_quantize(fmt: str, W: torch.Tensor, rsf: bool = False):
+OPS = {"quantize": 1, "dequantize": 2, "rotate": 3, "gemv": 4, "gemm": 5, "nvfp4_quantize": 6,
+       "mxfp6_quantize": 7, "blockfp_gemm": 8, "transcode_q8": 9, "q8_gemv": 10, "attn_decode": 11}
+
+
+def workspace_bytes(op: str, N: int, K: int, M: int = 0) -> int:
+    """Device workspace bytes of a call (tq_workspace_bytes); 0 when it takes none."""
+    return int(lib().tq_workspace_bytes(OPS[op], N, K, M))
+
+
+def blockfp_quantize(fmt: str, W: torch.Tensor, rsf: bool = False, workspace=None, out=None):
     """-> (codes uint8, block_scales uint8, tensor_scale float32[1] or None).
 
-    ``rsf=True`` runs the RSF-lite block-scale search (tq_blockfp_quantize_rsf)."""
+    ``rsf=True`` runs the RSF-lite block-scale search (tq_blockfp_quantize_rsf).  NVFP4 needs a
+    workspace of workspace_bytes("nvfp4_quantize", N, K) bytes; one is taken from torch's allocator
+    when none is given.  ``out`` = (codes, block_scales, tensor_scale) to write into."""
     _dev(W, "W")
     if W.dim() != 2 or not W.is_contiguous():
         raise ValueError("W must be a contiguous 2-D tensor")
     f = FORMATS[fmt]
     N, K = W.shape
-    if fmt == "nvfp4":
-        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
-        bs = torch.empty((N, K // 16), dtype=torch.uint8, device=W.device)
-        ts = torch.empty(1, dtype=torch.float32, device=W.device)
+    cshape = (N, K // 2) if fmt == "nvfp4" else (N, 3 * K // 4)
+    sshape = (N, K // 16) if fmt == "nvfp4" else (N, K // 32)
+    if out is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=W.device)
+        bs = torch.empty(sshape, dtype=torch.uint8, device=W.device)
+        ts = torch.empty(1, dtype=torch.float32, device=W.device) if fmt == "nvfp4" else None
     else:
-        codes = torch.empty((N, 3 * K // 4), dtype=torch.uint8, device=W.device)
-        bs = torch.empty((N, K // 32), dtype=torch.uint8, device=W.device)
-        ts = None
+        codes, bs, ts = out
+        _dense(codes, "out[0]", (torch.uint8,), cshape)
+        _dense(bs, "out[1]", (torch.uint8,), sshape)
+        if fmt == "nvfp4":
+            _need(ts is not None, "NVFP4 needs a tensor-scale output")
+            _dense(ts, "out[2]", (torch.float32,), (1,))
+        _same_device(W, (codes, "out[0]"), (bs, "out[1]"), (ts, "out[2]"))
+    ws, wsb = None, 0
+    if fmt == "nvfp4":
+        need = workspace_bytes("nvfp4_quantize", N, K)
+        ws = torch.empty(need, dtype=torch.uint8, device=W.device) if workspace is None else workspace
+        _need(ws.is_contiguous() and ws.numel() * ws.element_size() >= need,
+              f"workspace must be a contiguous buffer of at least {need} bytes")
+        _same_device(W, (ws, "workspace"))
+        wsb = ws.numel() * ws.element_size()
     fn = "tq_blockfp_quantize_rsf" if rsf else "tq_blockfp_quantize"
-    st = getattr(lib(), fn)(f, _ptr(W), _dtype_code(W, "W"), N, K, _ptr(codes), _ptr(bs), _ptr(ts), _stream())
+    st = getattr(lib(), fn)(f, _ptr(W), _dtype_code(W, "W"), N, K, _ptr(codes), _ptr(bs), _ptr(ts), _ptr(ws), wsb,
+                            _stream())
     _check(fn, st)
     return codes, bs, ts
 
@@ -467,3 +497,25 @@ def attn_decode(q: torch.Tensor, lengths: torch.Tensor, k_codes, k_scales, v_pac
     _check("tq_attn_decode", st)
     return o
 
+
+# ----------------------------------------------------------------------------
+# measurement helper
+# ----------------------------------------------------------------------------
+
+STREAM_READ_SINK_WORDS = 16384
+
+
+def stream_read(buf: torch.Tensor, nbytes: int | None = None, sink: torch.Tensor | None = None):
+    """Read the first ``nbytes`` bytes of ``buf`` with the plain streaming-read kernel (tq_stream_read);
+    returns the sink of per-wavefront XOR folds."""
+    _dev(buf, "buf")
+    _need(buf.is_contiguous(), "buf must be contiguous")
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else nbytes
+    _need(0 < nbytes <= total, "nbytes out of range")
+    if sink is None:
+        sink = torch.empty(STREAM_READ_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    _dense(sink, "sink", (torch.int32,), (STREAM_READ_SINK_WORDS,))
+    _same_device(buf, (sink, "sink"))
+    _check("tq_stream_read", lib().tq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream()))
+    return sink

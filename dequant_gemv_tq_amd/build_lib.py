@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libtq.so")
 ARCH = "gfx950"
 
 SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_transform.hip", "tq_gemv.hip", "tq_gemm.hip", "tq_blockfp.hip", "tq_kv.hip",
-           "tq_q8.hip"]
+           "tq_q8.hip", "tq_measure.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

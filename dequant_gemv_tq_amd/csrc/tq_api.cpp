@@ -112,27 +112,44 @@ tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
 }
 
 static tq_status blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
-                                  uint8_t* block_scales, float* tensor_scale, hipStream_t stream, bool rsf) {
+                                  uint8_t* block_scales, float* tensor_scale, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream, bool rsf) {
   if (f != TQ_FMT_NVFP4 && f != TQ_FMT_MXFP6) return TQ_EINVAL;
   if (!W || !codes || !block_scales || N <= 0 || K <= 0) return TQ_EINVAL;
-  if (f == TQ_FMT_NVFP4 && !tensor_scale) return TQ_EINVAL;
+  if (f == TQ_FMT_NVFP4 && (!tensor_scale || !workspace || ws_bytes < TQ_NVFP4_WORKSPACE_BYTES)) return TQ_EINVAL;
   if (K % (f == TQ_FMT_NVFP4 ? 16 : 32)) return TQ_ESHAPE;
   if (N > 0x7fffffff) return TQ_ESHAPE;
   if (!float_or_bf16(wt)) return TQ_EDTYPE;
   if (!aligned(W, 16) || (K * dtype_size(wt)) % 16 || !aligned(codes, 8)) return TQ_EALIGN;
-  if (f == TQ_FMT_NVFP4 && !aligned(tensor_scale, 4)) return TQ_EALIGN;
+  if (f == TQ_FMT_NVFP4 && (!aligned(tensor_scale, 4) || !aligned(workspace, 4))) return TQ_EALIGN;
   return from_hip(tq::launch_blockfp_quantize((int)f, W, wt == TQ_BF16, N, K, codes, block_scales, tensor_scale,
-                                              stream, rsf));
+                                              workspace, stream, rsf));
 }
 
 tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
-                              uint8_t* block_scales, float* tensor_scale, hipStream_t stream) {
-  return blockfp_quantize(f, W, wt, N, K, codes, block_scales, tensor_scale, stream, false);
+                              uint8_t* block_scales, float* tensor_scale, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  return blockfp_quantize(f, W, wt, N, K, codes, block_scales, tensor_scale, workspace, ws_bytes, stream, false);
 }
 
 tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
-                                  uint8_t* block_scales, float* tensor_scale, hipStream_t stream) {
-  return blockfp_quantize(f, W, wt, N, K, codes, block_scales, tensor_scale, stream, true);
+                                  uint8_t* block_scales, float* tensor_scale, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return blockfp_quantize(f, W, wt, N, K, codes, block_scales, tensor_scale, workspace, ws_bytes, stream, true);
+}
+
+size_t tq_workspace_bytes(int op, int64_t N, int64_t K, int64_t M) {
+  switch (op) {
+    case TQ_OP_QUANTIZE: case TQ_OP_DEQUANTIZE: case TQ_OP_ROTATE: case TQ_OP_GEMV: case TQ_OP_GEMM:
+    case TQ_OP_MXFP6_QUANTIZE: case TQ_OP_BLOCKFP_GEMM: case TQ_OP_TRANSCODE_Q8: case TQ_OP_Q8_GEMV:
+      return 0;
+    case TQ_OP_NVFP4_QUANTIZE:
+      return TQ_NVFP4_WORKSPACE_BYTES;
+    case TQ_OP_ATTN_DECODE:
+      if (N <= 0 || K <= 0 || M <= 0) return SIZE_MAX;
+      return tq::attn_workspace_bytes(N, K, M);
+  }
+  return SIZE_MAX;
 }
 
 tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale,
@@ -219,6 +236,13 @@ tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int6
     return TQ_EALIGN;
   return from_hip(tq::launch_attn_decode(q, qt == TQ_BF16, B, Hq, Hkv, T_max, lengths, k_codes, k_scales, v_packed,
                                          v_norms, sign, o, workspace, stream));
+}
+
+tq_status tq_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!p || !sink || bytes == 0) return TQ_EINVAL;
+  if (bytes % 16) return TQ_ESHAPE;
+  if (!aligned(p, 16) || !aligned(sink, 4)) return TQ_EALIGN;
+  return from_hip(tq::launch_stream_read(p, bytes, sink, stream));
 }
 
 }  // extern "C"

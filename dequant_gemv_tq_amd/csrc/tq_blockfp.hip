@@ -94,11 +94,16 @@ __device__ __forceinline__ float tree16(const float (&s)[kN], int o) {
 __device__ __forceinline__ int rsf_step(int t) { return (t & 1) ? -((t + 1) >> 1) : (t >> 1); }
 
 // --------------------------------------------------------------------------
-// NVFP4 quantizer: fill -> amax (atomicMax on the bit pattern of |w|,
-// which orders like the value for non-negative floats) -> encode -> finalize.
+// NVFP4 quantizer, two launches: amax (one partial maximum per workgroup
+// into the caller's workspace) -> encode (each workgroup reduces the
+// partials, so nothing has to be zeroed first and no atomics are needed;
+// workgroup 0 writes the tensor scale).  The maxima are taken on the bit
+// patterns of |w|, which order like the values for non-negative floats.
 // --------------------------------------------------------------------------
 
-__global__ void fill_u32(uint32_t* p, uint32_t v) { *p = v; }
+// Partial maxima the amax pass leaves in the workspace (at most).
+constexpr uint32_t kAmaxPartials = 1024;
+static_assert(kAmaxPartials * 4 == TQ_NVFP4_WORKSPACE_BYTES, "workspace size in the header");
 
 // |w| bit patterns of one 16-byte chunk (the sign bit cleared).
 template <bool kBf16>
@@ -114,10 +119,10 @@ __device__ __forceinline__ uint32_t chunk_max(const uint4& u) {
 }
 
 // Grid-stride max with four 16-byte loads in flight per thread, reduced
-// across the workgroup in LDS, then one atomicMax per workgroup.
+// across the workgroup in LDS; workgroup g writes partial[g].
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint8_t* __restrict__ W, size_t n16,
-                                                        uint32_t* __restrict__ out) {
+                                                        uint32_t* __restrict__ partial) {
   __shared__ uint32_t red[kThreads / 64];
   const uint4* src = reinterpret_cast<const uint4*>(W);
   const size_t stride = (size_t)gridDim.x * kThreads;
@@ -135,8 +140,23 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint8_t* __restric
   if (threadIdx.x == 0) {
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
-    atomicMax(out, m);
+    partial[blockIdx.x] = m;
   }
+}
+
+// The tensor amax from the amax pass's partials, reduced by the calling
+// workgroup (every thread returns it).
+__device__ __forceinline__ float reduce_amax(const uint32_t* __restrict__ partial, uint32_t count) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t m = 0u;
+  for (uint32_t i = threadIdx.x; i < count; i += kThreads) m = max(m, partial[i]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, s, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) m = max(m, red[w]);
+  return __uint_as_float(m);
 }
 
 // Squared float32 error of a 16-element block encoded with effective scale
@@ -163,16 +183,13 @@ __device__ __forceinline__ float nvfp4_block_error(const float (&v)[16], float e
   return tree16(s, 0);
 }
 
-// One thread per 16-element block.  kRsf: the block scale is chosen among
-// the E4M3 roundings of dec(sb_0) * (1 + j/16), j = 0, -1, +1, ..., -4, +4,
-// by the smallest float32 squared error (ties keep the earlier candidate).
+// One thread per 16-element block, grid-stride over the blocks.  kRsf: the
+// block scale is chosen among the E4M3 roundings of dec(sb_0) * (1 + j/16),
+// j = 0, -1, +1, ..., -4, +4, by the smallest float32 squared error (ties
+// keep the earlier candidate).
 template <bool kBf16, bool kRsf>
-__global__ __launch_bounds__(kThreads) void nvfp4_encode_kernel(const uint8_t* __restrict__ W, uint32_t total,
-                                                                const uint32_t* __restrict__ amax_bits,
-                                                                uint2* __restrict__ codes,
-                                                                uint8_t* __restrict__ bscales) {
-  uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-  if (g >= total) return;
+__device__ __forceinline__ void nvfp4_encode_block(const uint8_t* __restrict__ W, uint32_t g, float st,
+                                                   uint2* __restrict__ codes, uint8_t* __restrict__ bscales) {
   float v[16];
   if constexpr (kBf16) {
     const uint4* q = reinterpret_cast<const uint4*>(W + (size_t)g * 32);
@@ -194,8 +211,6 @@ __global__ __launch_bounds__(kThreads) void nvfp4_encode_kernel(const uint8_t* _
       v[4 * t] = u.x; v[4 * t + 1] = u.y; v[4 * t + 2] = u.z; v[4 * t + 3] = u.w;
     }
   }
-  const float amax = __uint_as_float(*amax_bits);
-  const float st = amax / 2688.0f;
   uint32_t sb = 0u;
   uint32_t lo = 0u, hi = 0u;
   if (st != 0.0f) {
@@ -242,7 +257,20 @@ __global__ __launch_bounds__(kThreads) void nvfp4_encode_kernel(const uint8_t* _
   bscales[g] = (uint8_t)sb;
 }
 
-__global__ void nvfp4_finalize(uint32_t* ts) { *ts = __float_as_uint(__uint_as_float(*ts) / 2688.0f); }
+// s_t = fl(amax / 2688) from the partial maxima; workgroup 0 of the first
+// launch stores it as the tensor scale.
+template <bool kBf16, bool kRsf>
+__global__ __launch_bounds__(kThreads) void nvfp4_encode_kernel(const uint8_t* __restrict__ W, uint32_t total,
+                                                                const uint32_t* __restrict__ partial,
+                                                                uint32_t npartial, float* __restrict__ tscale,
+                                                                uint2* __restrict__ codes,
+                                                                uint8_t* __restrict__ bscales) {
+  const float st = reduce_amax(partial, npartial) / 2688.0f;
+  if (tscale && blockIdx.x == 0 && threadIdx.x == 0) *tscale = st;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t g = blockIdx.x * kThreads + threadIdx.x; g < total; g += stride)
+    nvfp4_encode_block<kBf16, kRsf>(W, g, st, codes, bscales);
+}
 
 // --------------------------------------------------------------------------
 // MXFP6 quantizer: one thread per 32-element block, 24 bytes of codes.
@@ -315,27 +343,32 @@ inline uint32_t grid_for(uint32_t total) { return (total + kThreads - 1) / kThre
 }  // namespace
 
 hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K, uint8_t* codes,
-                                   uint8_t* bscales, float* tscale, hipStream_t s, bool rsf) {
+                                   uint8_t* bscales, float* tscale, void* workspace, hipStream_t s, bool rsf) {
   const uint8_t* w = static_cast<const uint8_t*>(W);
   const int64_t esz = bf16 ? 2 : 4;
   if (fmt == TQ_FMT_NVFP4) {
-    uint32_t* ts = reinterpret_cast<uint32_t*>(tscale);
-    hipLaunchKernelGGL(fill_u32, dim3(1), dim3(1), 0, s, ts, 0u);
+    uint32_t* partial = static_cast<uint32_t*>(workspace);
     const size_t n16 = (size_t)(N * K * esz / 16);
     const size_t want = (n16 + kThreads - 1) / kThreads;
-    const size_t cap = (size_t)(4 * device_cu_count());
-    const uint32_t grid = (uint32_t)(want < cap ? want : cap);
-    if (bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid), dim3(kThreads), 0, s, w, n16, ts);
-    else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid), dim3(kThreads), 0, s, w, n16, ts);
+    size_t cap = (size_t)(4 * device_cu_count());
+    cap = cap < kAmaxPartials ? cap : kAmaxPartials;
+    const uint32_t parts = (uint32_t)(want < cap ? want : cap);
+    if (bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(parts), dim3(kThreads), 0, s, w, n16, partial);
+    else hipLaunchKernelGGL(amax_kernel<false>, dim3(parts), dim3(kThreads), 0, s, w, n16, partial);
+    // Encode: a grid-stride launch of at most 16 workgroups per compute
+    // unit, so the partials are reduced by a bounded number of workgroups.
     const int64_t blocks = N * K / 16;
     const int64_t per_launch = (int64_t)1 << 30;
+    const uint32_t gcap = (uint32_t)(16 * device_cu_count());
     for (int64_t b0 = 0; b0 < blocks; b0 += per_launch) {
       const uint32_t total = (uint32_t)((blocks - b0 < per_launch) ? blocks - b0 : per_launch);
+      const uint32_t grid = grid_for(total) < gcap ? grid_for(total) : gcap;
       const uint8_t* wb = w + b0 * 16 * esz;
       uint2* cb = reinterpret_cast<uint2*>(codes) + b0;
+      float* ts = b0 == 0 ? tscale : nullptr;
 #define TQ_NVFP4(B, R) \
-  hipLaunchKernelGGL((nvfp4_encode_kernel<B, R>), dim3(grid_for(total)), dim3(kThreads), 0, s, wb, total, ts, cb, \
-                     bscales + b0)
+  hipLaunchKernelGGL((nvfp4_encode_kernel<B, R>), dim3(grid), dim3(kThreads), 0, s, wb, total, partial, parts, ts, \
+                     cb, bscales + b0)
       if (bf16) {
         if (rsf) TQ_NVFP4(true, true);
         else TQ_NVFP4(true, false);
@@ -345,7 +378,6 @@ hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N,
       }
 #undef TQ_NVFP4
     }
-    hipLaunchKernelGGL(nvfp4_finalize, dim3(1), dim3(1), 0, s, ts);
   } else {
     const int64_t blocks = N * K / 32;
     const int64_t per_launch = (int64_t)1 << 30;

@@ -23,9 +23,9 @@
 //     (b = lane_k + j * TK) for the whole kernel; the rotation (when the
 //     activation arrives unrotated) is done once per workgroup in the
 //     prologue.
-//   * Persistent workgroups walk row tiles.  A wavefront keeps up to four
-//     register sets of tile loads (16-byte nibble loads, 4-byte scale loads)
-//     in flight; only the first tile is requested before the activation has
+//   * Persistent workgroups walk row tiles.  A wavefront keeps two register
+//     sets of tile loads (16-byte nibble loads, 4-byte scale loads) in
+//     flight; only the first tile is requested before the activation has
 //     arrived, because a larger first burst of weight requests delays the
 //     activation, which every tile waits for.  Row addresses are
 //     wavefront-uniform (scalar) plus a fixed 32-bit lane offset.
@@ -33,7 +33,7 @@
 //     per SIMD over a whole gate|up launch, LDS waits ~3%), so per-tile
 //     overhead matters: a lane keeps the partial sums of several tiles and
 //     one transposed butterfly (v_permlane32_swap, v_permlane16_swap, DPP)
-//     reduces four of them at once, ~3 VALU ops per row instead of ~10.
+//     reduces them at once, ~3-5 VALU ops per row instead of ~10.
 //   * Several wavefronts along K (TK = 64 * WK lanes per row slot) leave
 //     their partial sums in an LDS ring that is combined every 32 tiles.
 #include <map>
@@ -728,13 +728,15 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
 
 // Decode GEMV shape, measured on MI355X over the Llama-3-8B and 70B decode
 // layers: x' staged in LDS, the fewest K-blocks per lane that fit a row into
-// a 1024-thread workgroup, and one row per wavefront per tile with four
+// a 1024-thread workgroup, and one row per wavefront per tile with two
 // register sets of tile loads, only the first requested before the
-// activation has arrived (graph-timed, Llama-3-8B groups: q|k|v 6.7 -> 5.8
-// us, gate|up 15.6 -> 15.0 us, down 10.8 -> 10.3 us against two sets both
-// requested at the start) -- except when a single round of two-row tiles
+// activation has arrived -- except when a single round of two-row tiles
 // already covers the matrix (one tile per workgroup, nothing to pipeline),
-// where two rows per wavefront and one register set are used.
+// where two rows per wavefront and one register set are used.  Graph-timed
+// 32-layer Llama-3-8B step on two boxes: 1.215 / 1.206 ms with both sets
+// requested at the start, 1.164 / 1.147 ms with one; four sets (one early)
+// measured 1.317 / 1.140 ms -- deeper queues help on some boxes and cost 8%
+// on others, so two are kept.
 constexpr bool kGemvStage = true;
 constexpr int kGemvMinJ = 1;
 
@@ -744,7 +746,7 @@ void launch_gemv_jr(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, cons
   // Groups of 4 elements each thread stages (a power of two, at most 8).
   const uint32_t K = nb * 32, per = 4u * (uint32_t)pl.threads;
   const uint32_t passes = (K + per - 1) / per;
-  constexpr int D = R == 1 ? 4 : 1;
+  constexpr int D = R == 1 ? 2 : 1;
   if constexpr (J <= 2) {
     if (kGemvStage && K <= (uint32_t)kStageFloats && passes <= 8) {
       if (passes <= 1) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);

@@ -26,8 +26,8 @@ hipError_t launch_gemm_valu(const uint8_t* packed, const uint16_t* scales, int64
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
                        const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K,
-                                   uint8_t* codes, uint8_t* bscales, float* tscale, hipStream_t s,
-                                   bool rsf = false);
+                                   uint8_t* codes, uint8_t* bscales, float* tscale, void* workspace,
+                                   hipStream_t s, bool rsf = false);
 hipError_t launch_blockfp_gemv(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale, int64_t N,
                                int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y, int64_t ldy,
                                hipStream_t s);
@@ -38,6 +38,9 @@ hipError_t launch_q8_gemv(const int8_t* codes, const uint16_t* qscales, int64_t 
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
                                float* y, int64_t ldy, hipStream_t s);
+
+// plain streaming read (tq_measure.hip).
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // turbo4 KV cache (tq_kv.hip).
 hipError_t launch_q8_rows(const void* X, bool bf16, int64_t nblocks, int8_t* codes, uint16_t* scales, hipStream_t s);

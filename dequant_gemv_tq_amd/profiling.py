@@ -47,7 +47,7 @@ MEMBERS = {"qkv": ["q", "k", "v"], "o": ["o"], "gate_up": ["gate", "up"], "down"
 COPIES = 8
 COPY_BYTES = 1 << 30
 DOMINANT = ("qkv", "gate_up")               # groups served by the dominant instantiation
-DOMINANT_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1>"   # K = 4096, one row per wavefront
+DOMINANT_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 1>"   # K = 4096, one row per wavefront
 SOURCES = ("csrc/tq_gemv.hip", "csrc/tq_internal.hpp")
 
 
@@ -321,6 +321,16 @@ def kv_summarize(fetch_db: str, write_db: str) -> None:
 
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- "
                  "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline")
+STATS_SOURCES = ("csrc/tq_gemv.hip", "csrc/tq_internal.hpp", "csrc/tq_gemm.hip", "csrc/tq_blockfp.hip",
+                 "csrc/tq_transform.hip", "csrc/tq_q8.hip", "csrc/tq_kv.hip", "csrc/tq_measure.hip")
+
+
+def stats_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in STATS_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def stats(csv_path: str) -> None:
@@ -329,6 +339,7 @@ def stats(csv_path: str) -> None:
     import re
     rows = list(csv.DictReader(open(csv_path)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
+    averages = {}
     lines = ["# Kernel durations of the benchmark (Llama-3-8B decode stream and secondary rows)", "",
              "Command (repository root on the GPU host; OUT is any scratch folder):", "", "```",
              TRACE_COMMAND, "python3 -m dequant_gemv_tq_amd.profiling stats OUT/trace/bench_kernel_stats.csv",
@@ -340,13 +351,14 @@ def stats(csv_path: str) -> None:
         if not m:
             continue
         name = m.group(1).replace("tq::(anonymous namespace)::", "")
+        averages[name] = round(float(r["AverageNs"]) / 1e3, 3)
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.2f}% |")
-    lines += ["", "Decode GEMV instantiations `gemv_kernel<format, J, R, MC, mode, threads, depth, stage>`: "
+    lines += ["", "Decode GEMV instantiations `gemv_kernel<format, J, R, MC, mode, threads, depth, early, stage>`: "
               "q|k|v and gate|up (K = 4096, bf16 activation, rotation fused, one row per wavefront) run "
-              f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 2, 1>`; down "
-              "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 4>`.  "
+              f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 1, 1, 1>`; down "
+              "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 4>`.  "
               "Other kernels: the quantizer (`quantize_kernel<bf16, rsf>`, the second flag for the RSF-lite "
               "scale search), the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M <= 4, and float32 "
               "activations below 16 rows; above, the persistent MFMA `gemm_small_kernel<format, MT, NQ>` with bf16 "
@@ -357,9 +369,24 @@ def stats(csv_path: str) -> None:
               "five) and the "
               "load-time int8 rows (`q8_transcode_kernel`, `q8_gemv_kernel<bf16 activation, passes>`), the turbo4 KV "
               "cache (`q8_rows_kernel` keys, `turbo4_encode_kernel` values, `attn_split_kernel<G, bf16 q>` + "
-              "`attn_combine_kernel` for decode attention); the "
-              "remaining GPU time is PyTorch drawing the synthetic weights.", ""]
+              "`attn_combine_kernel` for decode attention), `stream_read_kernel` (the read envelope); the "
+              "remaining GPU time is PyTorch drawing the synthetic weights.", "",
+              "Average durations (microseconds) as the benchmark reads them:", "",
+              "stats-json: " + json.dumps({"kernels": averages, "source_sha256": stats_source_hash()}), ""]
     print("\n".join(lines))
+
+
+def read_stats_record(path: str) -> dict | None:
+    """The kernel averages of a stats summary, or None when absent or taken from other sources."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("stats-json: "):
+                    rec = json.loads(line[len("stats-json: "):])
+                    return rec if rec.get("source_sha256") == stats_source_hash() else None
+    except OSError:
+        return None
+    return None
 
 
 def read_record(path: str) -> dict | None:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -183,21 +183,52 @@ tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
                   const void* x_rot, tq_dtype xt, int64_t ldx, float* y, int64_t ldy,
                   hipStream_t stream);
 
+/* Workspace bytes of NVFP4 quantization: the amax pass leaves one partial
+ * maximum per workgroup (at most 1024) for the encode pass. */
+#define TQ_NVFP4_WORKSPACE_BYTES 4096
+
+/* Operations for tq_workspace_bytes. */
+typedef enum tq_op {
+  TQ_OP_QUANTIZE = 1,          /* tq_quantize, tq_quantize_rsf: none            */
+  TQ_OP_DEQUANTIZE = 2,        /* none                                          */
+  TQ_OP_ROTATE = 3,            /* none                                          */
+  TQ_OP_GEMV = 4,              /* none                                          */
+  TQ_OP_GEMM = 5,              /* none (split K writes into y itself)           */
+  TQ_OP_NVFP4_QUANTIZE = 6,    /* tq_blockfp_quantize(_rsf) with TQ_FMT_NVFP4   */
+  TQ_OP_MXFP6_QUANTIZE = 7,    /* tq_blockfp_quantize(_rsf) with TQ_FMT_MXFP6: none */
+  TQ_OP_BLOCKFP_GEMM = 8,      /* none                                          */
+  TQ_OP_TRANSCODE_Q8 = 9,      /* none                                          */
+  TQ_OP_Q8_GEMV = 10,          /* none                                          */
+  TQ_OP_ATTN_DECODE = 11       /* N = B, K = Hq, M = T_max: as tq_attn_workspace_bytes */
+} tq_op;
+
+/* Device workspace bytes a call of `op` needs for an [N, K] weight and M
+ * activation rows (TQ_OP_ATTN_DECODE: N = sequences, K = query heads, M =
+ * T_max).  0 when the call takes no workspace; SIZE_MAX for an unknown op
+ * or a non-positive size where one is used.  The caller allocates the
+ * workspace (the library allocates nothing) and owns it again once the
+ * stream has passed the call. */
+size_t tq_workspace_bytes(int op, int64_t N, int64_t K, int64_t M);
+
 /* Quantize W [N, K] (TQ_F32 or TQ_BF16, dense rows) to a block float format
  * (quantizer-tool page, "目前能实现的部分功能" / "MXFP6 的未来"):
  *   TQ_FMT_NVFP4: codes [N, K/2] (E2M1, element 2j in the low nibble of byte
  *     j), block_scales [N, K/16] (E4M3fn), *tensor_scale = amax|W| / 2688
- *     (one float32, device memory; also used as the amax accumulator while
- *     the call runs).  K % 16 == 0.
+ *     (one float32, device memory).  K % 16 == 0.  Two launches: an amax
+ *     pass that leaves partial maxima in `workspace` (device, 4-byte
+ *     aligned, ws_bytes >= tq_workspace_bytes(TQ_OP_NVFP4_QUANTIZE, N, K, 0)
+ *     = TQ_NVFP4_WORKSPACE_BYTES; no initial contents needed), then the
+ *     encode, which reduces them and writes the tensor scale.
  *   TQ_FMT_MXFP6: codes [N, 3K/4] (E3M2, 4 codes per little-endian 24-bit
- *     word), block_scales [N, K/32] (E8M0); tensor_scale ignored (may be
- *     NULL).  K % 32 == 0.
+ *     word), block_scales [N, K/32] (E8M0); tensor_scale and workspace
+ *     ignored (may be NULL).  K % 32 == 0.  One launch.
  * Rounding is to nearest even with saturation; the sign of a value that
  * rounds to zero is kept.  W 16-byte aligned, codes 8-byte aligned.
- * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
+ * Errors: TQ_EINVAL (also: NVFP4 without tensor_scale or workspace, or a
+ * workspace smaller than needed), TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K,
                               uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
-                              hipStream_t stream);
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* tq_blockfp_quantize with the RSF-lite block-scale search (quantizer-tool
  * page, "RSF": nearby multiples of a block scale are tried and the better
@@ -212,11 +243,11 @@ tq_status tq_blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N
  *     32 elements.
  * The smallest error wins, ties to the earlier candidate (the plain scale
  * first), so the result is never worse than tq_blockfp_quantize's and is
- * bit-exact against that definition.  Output layout, arguments, alignment
- * and errors as tq_blockfp_quantize. */
+ * bit-exact against that definition.  Output layout, arguments (the
+ * workspace included), alignment and errors as tq_blockfp_quantize. */
 tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K,
                                   uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
-                                  hipStream_t stream);
+                                  void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Y[m, n] = sum_k W_deq[n, k] X[m, k] for a block-float weight (fused
  * decode, float32 accumulation; the activation is used as given, there is
@@ -338,6 +369,18 @@ tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int6
                          const uint16_t* k_scales, const uint8_t* v_packed, const uint16_t* v_norms,
                          const uint32_t sign[4], float* o, void* workspace, size_t ws_bytes,
                          hipStream_t stream);
+
+/* Measurement helper: read `bytes` bytes at p (device, 16-byte aligned, bytes
+ * a positive multiple of 16) through a plain streaming-read kernel with the
+ * decode GEMV's launch shape (one 1024-thread workgroup per compute unit),
+ * and store one XOR fold per wavefront in sink (device, at least
+ * TQ_STREAM_READ_SINK_WORDS words; the folds carry no meaning beyond keeping
+ * the loads).  Timing it on the bytes of a GEMV launch
+ * gives the read envelope that launch is compared with (TQ4 page,
+ * "解码速度：分硬件汇总": decode is bound by memory bandwidth).
+ * Errors: TQ_EINVAL (null, zero bytes), TQ_ESHAPE (bytes % 16), TQ_EALIGN. */
+#define TQ_STREAM_READ_SINK_WORDS 16384
+tq_status tq_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

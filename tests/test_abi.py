@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = tqa.lib()
-    assert L.tq_abi_version() == 1
+    assert L.tq_abi_version() == 2
     for s in range(6):
         assert L.tq_status_str(s)
     assert b"unknown" in L.tq_status_str(99)
@@ -107,19 +107,39 @@ def test_other_calls_reject_before_launch():
     assert L.tq_dequantize(g, g, 2, 64, 0, None, F32, 64, None) == EINVAL
     assert L.tq_dequantize(g, g, 2, 64, 0, g, F16, 64, None) == EDTYPE
     # block float
-    assert L.tq_blockfp_quantize(3, g, F32, 2, 64, g, g, g, None) == EINVAL
-    assert L.tq_blockfp_quantize(1, g, F32, 2, 64, g, g, None, None) == EINVAL   # NVFP4 needs tensor_scale
-    assert L.tq_blockfp_quantize(1, g, F32, 2, 40, g, g, g, None) == ESHAPE
-    assert L.tq_blockfp_quantize(2, g, F32, 2, 48, g, g, None, None) == ESHAPE   # MXFP6 needs K % 32
-    assert L.tq_blockfp_quantize(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
+    W4 = 4096                                                                     # TQ_NVFP4_WORKSPACE_BYTES
+    assert L.tq_blockfp_quantize(3, g, F32, 2, 64, g, g, g, g, W4, None) == EINVAL
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 64, g, g, None, g, W4, None) == EINVAL   # NVFP4 needs tensor_scale
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 64, g, g, g, None, W4, None) == EINVAL   # ... and a workspace
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 64, g, g, g, g, W4 - 4, None) == EINVAL  # ... of the full size
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 64, g, g, g, _p(GOOD + 2), W4, None) == EALIGN
+    assert L.tq_blockfp_quantize(1, g, F32, 2, 40, g, g, g, g, W4, None) == ESHAPE
+    assert L.tq_blockfp_quantize(2, g, F32, 2, 48, g, g, None, None, 0, None) == ESHAPE   # MXFP6 needs K % 32
+    assert L.tq_blockfp_quantize(2, g, F16, 2, 64, g, g, None, None, 0, None) == EDTYPE
+    # workspace sizes: only NVFP4 quantization and decode attention take one
+    smax = ctypes.c_size_t(-1).value
+    assert L.tq_workspace_bytes(6, 17408, 5120, 0) == W4
+    for op in (1, 2, 3, 4, 5, 7, 8, 9, 10):
+        assert L.tq_workspace_bytes(op, 4096, 4096, 16) == 0
+    assert L.tq_workspace_bytes(11, 2, 32, 1000) == L.tq_attn_workspace_bytes(2, 32, 1000)
+    assert L.tq_workspace_bytes(11, 0, 32, 1000) == smax
+    assert L.tq_workspace_bytes(99, 1, 1, 1) == smax
+    assert tqa.workspace_bytes("nvfp4_quantize", 8, 64) == W4
+    # the plain streaming-read helper
+    assert L.tq_stream_read(None, 64, g, None) == EINVAL
+    assert L.tq_stream_read(g, 0, g, None) == EINVAL
+    assert L.tq_stream_read(g, 72, g, None) == ESHAPE
+    assert L.tq_stream_read(_p(GOOD + 8), 64, g, None) == EALIGN
+    assert L.tq_stream_read(g, 64, _p(GOOD + 2), None) == EALIGN
     for fn in (L.tq_blockfp_quantize, L.tq_blockfp_quantize_rsf):
-        assert fn(3, g, F32, 2, 64, g, g, g, None) == EINVAL
-        assert fn(1, g, F32, 2, 64, g, g, None, None) == EINVAL
-        assert fn(1, g, F32, 2, 40, g, g, g, None) == ESHAPE
-        assert fn(2, g, F32, 2, 48, g, g, None, None) == ESHAPE
-        assert fn(2, g, F16, 2, 64, g, g, None, None) == EDTYPE
-        assert fn(2, _p(GOOD + 4), F32, 2, 64, g, g, None, None) == EALIGN     # W: 16 B
-        assert fn(1, g, F32, 2, 64, _p(GOOD + 4), g, g, None) == EALIGN        # codes: 8 B
+        assert fn(3, g, F32, 2, 64, g, g, g, g, W4, None) == EINVAL
+        assert fn(1, g, F32, 2, 64, g, g, None, g, W4, None) == EINVAL
+        assert fn(1, g, F32, 2, 64, g, g, g, None, W4, None) == EINVAL
+        assert fn(1, g, F32, 2, 40, g, g, g, g, W4, None) == ESHAPE
+        assert fn(2, g, F32, 2, 48, g, g, None, None, 0, None) == ESHAPE
+        assert fn(2, g, F16, 2, 64, g, g, None, None, 0, None) == EDTYPE
+        assert fn(2, _p(GOOD + 4), F32, 2, 64, g, g, None, None, 0, None) == EALIGN     # W: 16 B
+        assert fn(1, g, F32, 2, 64, _p(GOOD + 4), g, g, g, W4, None) == EALIGN        # codes: 8 B
     assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 4097, g, F32, 64, g, 8, None) == ESHAPE   # M <= 4096
     assert L.tq_blockfp_gemm(1, g, g, g, 8, 32800, 1, g, F32, 32800, g, 8, None) == ESHAPE  # K <= 32768
     assert L.tq_blockfp_gemm(2, g, g, None, 8, 48, 1, g, F32, 64, g, 8, None) == ESHAPE     # K % 32
