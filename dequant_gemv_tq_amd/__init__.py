@@ -34,7 +34,7 @@ EXPORTED = [
     "tq_quantize", "tq_quantize_rsf", "tq_dequantize", "tq_rotate", "tq_gemv", "tq_gemm",
     "tq_blockfp_quantize", "tq_blockfp_quantize_rsf", "tq_blockfp_gemm", "tq_transcode_q8", "tq_q8_gemv",
     "tq_kv_sign_from_seed", "tq_kv_quantize_k", "tq_kv_quantize_v", "tq_kv_dequantize_v", "tq_attn_workspace_bytes",
-    "tq_attn_decode", "tq_workspace_bytes", "tq_stream_read",
+    "tq_attn_decode", "tq_workspace_bytes", "tq_stream_read", "tq_attn_decode_noalloc",
 ]
 
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.tq_blockfp_quantize_rsf.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p, ctypes.c_size_t, p]
     L.tq_workspace_bytes.argtypes = [c_int, i64, i64, i64]
     L.tq_workspace_bytes.restype = ctypes.c_size_t
+    L.tq_attn_decode_noalloc.argtypes = [p, c_int, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p]
+    L.tq_attn_decode_noalloc.restype = c_int
     L.tq_stream_read.argtypes = [p, ctypes.c_size_t, p, p]
     L.tq_stream_read.restype = c_int
     L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]

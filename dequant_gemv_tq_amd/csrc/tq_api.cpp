@@ -238,6 +238,25 @@ tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int6
                                          v_norms, sign, o, workspace, stream));
 }
 
+tq_status tq_attn_decode_noalloc(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                 int64_t T_max, const int32_t* lengths, const int8_t* k_codes,
+                                 const uint16_t* k_scales, const uint8_t* v_packed, const uint16_t* v_norms,
+                                 const uint32_t sign[4], float* o, hipStream_t stream) {
+  if (!q || !lengths || !k_codes || !k_scales || !v_packed || !v_norms || !sign || !o) return TQ_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || T_max <= 0) return TQ_EINVAL;
+  if (d != 128 || Hq % Hkv) return TQ_ESHAPE;
+  const int64_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_ESHAPE;
+  if (B > 65535 || Hkv > 65535 || Hq > 65535 || T_max > (int64_t)INT32_MAX) return TQ_ESHAPE;
+  if (tq::attn_workspace_bytes(B, Hq, T_max) > (size_t)TQ_ATTN_NOALLOC_SCRATCH_BYTES) return TQ_ESHAPE;
+  if (!float_or_bf16(qt)) return TQ_EDTYPE;
+  if (!aligned(q, 16) || !aligned(lengths, 4) || !aligned(k_codes, 16) || !aligned(k_scales, 2) ||
+      !aligned(v_packed, 4) || !aligned(v_norms, 2) || !aligned(o, 4))
+    return TQ_EALIGN;
+  return from_hip(tq::launch_attn_decode_noalloc(q, qt == TQ_BF16, B, Hq, Hkv, T_max, lengths, k_codes, k_scales,
+                                                 v_packed, v_norms, sign, o, stream));
+}
+
 tq_status tq_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream) {
   if (!p || !sink || bytes == 0) return TQ_EINVAL;
   if (bytes % 16) return TQ_ESHAPE;

@@ -21,8 +21,13 @@
 
 #include <algorithm>
 
+#include <mutex>
+
 #include "tq_internal.hpp"
 #include "tq_codes.hpp"
+
+// Split partials of tq_attn_decode_noalloc (TQ_ATTN_NOALLOC_SCRATCH_BYTES).
+static __device__ __align__(256) float scratch[TQ_ATTN_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace tq {
 namespace {
@@ -617,6 +622,48 @@ hipError_t launch_attn_decode(const void* q, bool qbf16, int64_t B, int64_t Hq, 
   hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)Hq, (uint32_t)B), dim3(kD), 0, s, part, lengths,
                      (uint32_t)Tmax, (uint32_t)Hq, S, signs_of(sign), o);
   return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Decode attention for callers that cannot allocate (code under graph
+// capture, serving loops): the split partials go to a file-scope device
+// array instead of a caller workspace.  Every device the library runs on
+// holds its own copy until the process ends; calls on one device share it,
+// so calls that overlap on one device race.  Nothing in it needs clearing:
+// the combine kernel reads only the partials the split kernel wrote in the
+// same call.
+// --------------------------------------------------------------------------
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_dev[64] = {nullptr};    // device address of `scratch`, per device ordinal
+}  // namespace
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (the host-side name is only a stand-in).
+hipError_t attn_scratch_ptr(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_attn_decode_noalloc(const void* q, bool qbf16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tmax,
+                                      const int32_t* lengths, const int8_t* kcodes, const uint16_t* kscales,
+                                      const uint8_t* vpacked, const uint16_t* vnorms, const uint32_t* sign, float* o,
+                                      hipStream_t s) {
+  float* ws = nullptr;
+  const hipError_t e = attn_scratch_ptr(&ws);
+  if (e != hipSuccess) return e;
+  return launch_attn_decode(q, qbf16, B, Hq, Hkv, Tmax, lengths, kcodes, kscales, vpacked, vnorms, sign, o, ws, s);
 }
 
 }  // namespace tq

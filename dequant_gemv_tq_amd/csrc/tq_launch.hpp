@@ -53,5 +53,9 @@ hipError_t launch_attn_decode(const void* q, bool qbf16, int64_t B, int64_t Hq, 
                               const int32_t* lengths, const int8_t* kcodes, const uint16_t* kscales,
                               const uint8_t* vpacked, const uint16_t* vnorms, const uint32_t* sign, float* o,
                               void* workspace, hipStream_t s);
+hipError_t launch_attn_decode_noalloc(const void* q, bool qbf16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tmax,
+                                      const int32_t* lengths, const int8_t* kcodes, const uint16_t* kscales,
+                                      const uint8_t* vpacked, const uint16_t* vnorms, const uint32_t* sign, float* o,
+                                      hipStream_t s);
 
 }  // namespace tq

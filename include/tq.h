@@ -370,6 +370,23 @@ tq_status tq_attn_decode(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int6
                          const uint32_t sign[4], float* o, void* workspace, size_t ws_bytes,
                          hipStream_t stream);
 
+/* tq_attn_decode for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments, layout, limits and errors without the
+ * workspace.  The split partials go to a device array inside the library
+ * (TQ_ATTN_NOALLOC_SCRATCH_BYTES, held by every device the library runs on
+ * until the process ends); a call whose tq_attn_workspace_bytes(B, Hq,
+ * T_max) exceeds it is rejected with TQ_ESHAPE before anything launches.
+ * Calls on one device share that array, so calls that overlap on one device
+ * (other streams, other threads) race; calls in stream order do not.  The
+ * call allocates nothing; its first call on a device looks up the array's
+ * device address (TQ_EDEVICE if that fails). */
+#define TQ_ATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
+tq_status tq_attn_decode_noalloc(const void* q, tq_dtype qt, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                 int64_t T_max, const int32_t* lengths, const int8_t* k_codes,
+                                 const uint16_t* k_scales, const uint8_t* v_packed, const uint16_t* v_norms,
+                                 const uint32_t sign[4], float* o, hipStream_t stream);
+
 /* Measurement helper: read `bytes` bytes at p (device, 16-byte aligned, bytes
  * a positive multiple of 16) through a plain streaming-read kernel with the
  * decode GEMV's launch shape (one 1024-thread workgroup per compute unit),

@@ -182,6 +182,14 @@ def test_other_calls_reject_before_launch():
     assert L.tq_attn_decode(*args(T=1 << 31, wsb=big)) == ESHAPE      # T_max > INT32_MAX
     assert L.tq_attn_decode(*args(qt=F16)) == EDTYPE
     assert L.tq_attn_decode(*args(q=_p(GOOD + 8))) == EALIGN
+    # decode attention without a workspace: the same checks, and problems beyond its scratch array
+    nargs = lambda **kw: [kw.get("q", g), kw.get("qt", BF16), kw.get("B", 1), kw.get("Hq", 32), kw.get("Hkv", 8),
+                          kw.get("d", 128), kw.get("T", 512), g, g, g, g, g, sg, g, None]
+    assert L.tq_attn_decode_noalloc(*nargs(q=None)) == EINVAL
+    assert L.tq_attn_decode_noalloc(*nargs(Hq=12)) == ESHAPE
+    assert L.tq_attn_decode_noalloc(*nargs(B=64, T=32768)) == ESHAPE          # 34 MB of partials > 8 MiB
+    assert L.tq_attn_decode_noalloc(*nargs(qt=F16)) == EDTYPE
+    assert L.tq_attn_decode_noalloc(*nargs(q=_p(GOOD + 8))) == EALIGN
 
 
 def test_binding_refuses_cpu_tensors():
