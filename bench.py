@@ -574,6 +574,22 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers, no_graph):
     rsf_ms = _time(torch, stream, lambda: quant(True), 1)
     q_ms = _time(torch, stream, lambda: quant(False), 1)        # last, so the outputs hold the plain codes
     store = [(fmt, c, bs, ts, W.shape[0], W.shape[1]) for (fmt, W), (c, bs, ts) in zip(src, outs)]
+    # The fused layout: per layer, the members of q|k|v and of gate|up that share a format are stored as
+    # one row-concatenated tensor (one NVFP4 tensor scale for the concatenation), as one decode launch
+    # reads them; o and down stay alone.  Quantized here untimed, one layer at a time.
+    fused = []
+    fgroups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    for layer in range(layers):
+        mine = dict(zip(names, src[layer * len(names):(layer + 1) * len(names)]))
+        for grp in fgroups:
+            for fmt in ("nvfp4", "mxfp6"):
+                parts = [mine[t][1] for t in grp if mine[t][0] == fmt]
+                if not parts:
+                    continue
+                Wc = torch.cat(parts, dim=0) if len(parts) > 1 else parts[0]
+                c, bs, ts = tqa.blockfp_quantize(fmt, Wc, workspace=ws)
+                fused.append((fmt, c, bs, ts, Wc.shape[0], Wc.shape[1]))
+                del Wc
     del src
     torch.cuda.empty_cache()
     res = {"layers": layers, "tensors": fmt_count, "quantize_GB_s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
@@ -596,7 +612,19 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers, no_graph):
         byts = sum((BF_BYTES[f] * n * k + 2 * m * k + 4 * m * n) for (f, _, _, _, n, k) in store)
         res[f"gemv_M{m}"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
                              "launches": len(store)}
-    del store
+        if m in (1, 8):
+            yf = [torch.empty((m, n), dtype=torch.float32, device=dev) for (_, _, _, _, n, _) in fused]
+
+            def run_fused():
+                for i, (fmt, codes, bs, ts, n, k) in enumerate(fused):
+                    tqa.blockfp_gemm(fmt, codes, bs, ts, xsv[k], out=yf[i])
+
+            ms = _time_graph(torch, stream, run_fused, 3, no_graph)
+            byts = sum((BF_BYTES[f] * n * k + 2 * m * k + 4 * m * n) for (f, _, _, _, n, k) in fused)
+            res[f"gemv_M{m}_fused"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
+                                       "launches": len(fused),
+                                       "layout": "same-format members of q|k|v and of gate|up row-concatenated"}
+    del store, fused
     torch.cuda.empty_cache()
     return res
 

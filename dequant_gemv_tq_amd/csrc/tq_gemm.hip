@@ -32,12 +32,14 @@
 // Arithmetic intensity stays below the bf16 ridge for M <= 64 (about 3.2 M
 // flop per byte of packed weight), so HBM remains the bound.
 //
-// Precision: with bf16 activations both operands carry a 2^-9 relative
-// rounding, so |dy| is about 2^-9 * ||w o x||_2, inside 1e-3 * sum|w x| once K
-// is in the hundreds.  With float32 activations each operand is split into
-// bf16 hi + lo (hi by truncation, lo = bf16(v - hi), exact residual) and three
-// MFMAs (hi*hi + hi*lo + lo*hi) keep about 16 significant bits per product,
-// which holds the bound at any K.
+// Precision: with bf16 activations both operands carry up to 2^-8 relative
+// rounding, so each rotated-domain product q_k x'_k is off by at most 2^-7 of
+// its size; for dense activations the errors average out to about
+// 2^-9 * ||w o x||_2, inside 1e-3 * sum|w x| once K is in the hundreds.  With
+// float32 activations each operand is split into bf16 hi + lo (hi by
+// truncation, lo = bf16(v - hi)) and three MFMAs (hi*hi + hi*lo + lo*hi) leave
+// at most 2^-13 per product.  Both are bounds on sum_k |q_k x'_k|: a one-hot x,
+// whose 32 rotated products cancel to one weight, can exceed 1e-3 * sum|w x|.
 #include <algorithm>
 #include <type_traits>
 

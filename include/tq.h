@@ -167,9 +167,18 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  * M <= 4 (and float32 activations with M < 16) run a VALU kernel with
  * float32 FMAs.  Larger M runs bf16 MFMA in 16-row tiles with float32
  * accumulation, dequantizing each weight once: one pass for bf16
- * activations (operand rounding about 2^-9, inside 1e-3 * sum|w x| once K is
- * in the hundreds), three hi/lo-split passes for float32 activations (about
- * 16 significant bits per product, any K).
+ * activations, three hi/lo-split passes for float32 activations.
+ * Precision of the MFMA path: the products are formed in the rotated domain,
+ * so what is guaranteed is a bound on sum_k |q_k x'_k| (q = d * c[idx]):
+ * per product at most 2^-7 of |q x'| with bf16 x' (bf16 x' and the bf16
+ * weight round by up to 2^-8 each), at most 2^-13 with float32 x' (hi/lo
+ * split without the lo*lo term), plus float32 accumulation over K.  The
+ * original-domain bound 1e-3 * sum_k |W_deq[n,k] x_k| is only statistical:
+ * it holds for dense activations (bf16 once K is in the hundreds, float32 at
+ * any K) but not for one-hot or very sparse rows, whose 32 rotated products
+ * per block cancel down to a single weight.  Callers with such activations
+ * who need that bound pass float32 x' in launches of at most 15 rows, which
+ * run float32 FMAs.
  * With bf16 activations, M >= 5, fewer than four 16-row tiles of N per
  * compute unit and K longer than one pass of the kernel (4096 elements for
  * launches of up to 16 rows, 2048 for 17-64; M is launched 64 rows at a

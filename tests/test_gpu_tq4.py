@@ -255,3 +255,41 @@ def test_repeat_runs_are_bit_identical():
     y1 = tqa.gemv(p1, s1, x)
     y2 = tqa.gemv(p1, s1, x)
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("k", [32, 96])
+def test_gemm_one_hot_rows_rotated_domain_bound(k, xdtype):
+    """One-hot activation rows at M = 16 (MFMA path): the rotated-domain bound holds.
+
+    The kernels multiply q = d * c[idx] by x' = (1/sqrt 32) H D x, so the
+    rounding of their operands is bounded by sum_k |q_k x'_k|.  For a one-hot
+    x that sum can be far larger than sum_k |W_deq[n,k] x_k| (the 32 products
+    of one block cancel down to a single weight), so the original-domain
+    1e-3 bound is not guaranteed here.  Operand rounding per product:
+    bf16 x' and bf16 weights, 2^-8 each; float32 x' through the three-pass
+    hi/lo split, at most 2^-13.  Plus float32 accumulation over K.
+    """
+    m, n = 16, 37
+    g = workloads.generator(31 * k + (xdtype == torch.float32), DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    vals = workloads.activation(1, m, g, DEV, torch.bfloat16)[0].float()
+    X = torch.zeros(m, k, device=DEV, dtype=torch.float32)
+    cols = torch.arange(m, device=DEV) * 7 % k
+    X[torch.arange(m, device=DEV), cols] = vals
+    X = X.to(xdtype)
+    packed, scales = tqa.quantize(W)
+    say(f"[gemm] one-hot M={m} K={k} x'={xdtype}")
+    Y = f32np(tqa.gemm(packed, scales, tqa.rotate(X, dtype=xdtype)))
+    Xh = X.float().cpu().numpy().astype(np.float64)
+    yr, a = otq.gemm_o64(packed.cpu().numpy(), u16(scales), Xh)
+    q = otq.rotated_weights_f64(packed.cpu().numpy(), u16(scales))
+    xr = otq.rotate_f64(Xh.reshape(m, k // 32, 32), otq.DEFAULT_SIGN_MASK).reshape(m, k)
+    rot = np.abs(xr) @ np.abs(q).T                         # sum_k |q_k x'_k|
+    per_product = 2.0 ** -7 + 2.0 ** -15 if xdtype == torch.bfloat16 else 2.0 ** -13
+    bound = (per_product + k * 2.0 ** -23) * rot
+    err = np.abs(Y - yr)
+    bad = err > bound
+    assert not bad.any(), (f"{bad.sum()} outside the rotated-domain bound; worst ratio "
+                           f"{float((err / np.maximum(rot, 1e-300)).max())!r}")
+    assert np.all(rot >= a * (1 - 1e-12))                  # the rotated sum dominates the original one
