@@ -371,13 +371,24 @@ struct GemmTQ4 {
   }
   __device__ __forceinline__ static void prepare(const Raw& r, Dec& d) {
     transpose_groups(r.p, d.w);
-    transpose_groups(make_uint4(r.sc, r.sc, r.sc, r.sc), d.sc);
+    // Lane groups 0, 1 take elements 0..15 of every block (scale d0, the low
+    // half), groups 2, 3 elements 16..31 (d1): the sender shifts d1 down for
+    // them, so every receiver finds its scale in the low half.
+    transpose_groups(make_uint4(r.sc, r.sc, r.sc >> 16, r.sc >> 16), d.sc);
   }
-  __device__ __forceinline__ static bf16x8 operand(const Dec& d, int s, uint32_t g, const uint8_t* lut,
+  __device__ __forceinline__ static bf16x8 operand(const Dec& d, int s, uint32_t, const uint8_t* lut,
                                                    uint32_t laneoff) {
-    const float sc = f16_bits_to_f32(g < 2u ? (d.sc[s] & 0xffffu) : (d.sc[s] >> 16));
+    // c * d with d read as fp16 straight from its register (v_fma_mix_f32:
+    // no separate conversion; + 0 keeps it a fused multiply-add, whose
+    // single rounding equals that of the product).
+    const float sc = (float)__builtin_bit_cast(_Float16, (unsigned short)(d.sc[s] & 0xffffu));
     float v[8];
-    dequant8(d.w[s], sc, lut, laneoff, v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 c = *reinterpret_cast<const float2*>(lut + pair_addr(d.w[s], laneoff, k));
+      v[2 * k] = __builtin_fmaf(c.x, sc, 0.0f);
+      v[2 * k + 1] = __builtin_fmaf(c.y, sc, 0.0f);
+    }
     return as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                      pack_bf16x2(v[6], v[7]));
   }
@@ -520,20 +531,40 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   struct WSet {
     typename Fmt::Raw r[NQ];
   };
-  // Group j of this wavefront in pass `pass`, block 4 q + g of the lane's
-  // row (clamped: a group past the last one is skipped at compute time).
+  // Group j of this wavefront in pass `pass` (clamped: a group past the last
+  // one is skipped at compute time).
   auto group_of = [&](uint32_t pass, int j) { return pass * kPassGroups + (uint32_t)wave + (uint32_t)(kWide * j); };
+  // A group's weights are loaded in row-major lane order: lane 4 r + b reads
+  // block 4 q + b of tile row r, so each row's four blocks are contiguous
+  // over four neighbouring lanes.  (With lane = r + 16 b, the order the MFMA
+  // operands use, neighbouring lanes read different rows and the loads of
+  // the whole tile loop ran at about two thirds of the rate.)  One
+  // ds_bpermute per loaded dword then hands block 4 q + g of row n to lane
+  // n + 16 g: a fixed rotation of the 6-bit lane index by two places.
+  const uint32_t lrow = (uint32_t)lane >> 2, lblk = (uint32_t)lane & 3u;
+  const int perm_addr = 4 * (((lane & 15) << 2) | (lane >> 4));
+  auto to_mfma_lanes = [&](const typename Fmt::Raw& r) {
+    static_assert(sizeof(typename Fmt::Raw) % 4 == 0, "whole dwords");
+    constexpr int kWords = (int)(sizeof(typename Fmt::Raw) / 4);
+    uint32_t wd[kWords];
+    __builtin_memcpy(wd, &r, sizeof(wd));
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) wd[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)wd[i]);
+    typename Fmt::Raw out;
+    __builtin_memcpy(&out, wd, sizeof(wd));
+    return out;
+  };
   // The scheduling barriers keep each register set's loads together, and a
   // workgroup barrier separates the two sets before the tile loop (the
   // compiler interleaved them otherwise), so every path into the loop
   // carries the same load order and the wait for a set never covers the set
   // loaded after it.
   auto load_w = [&](WSet& w, uint32_t tile, uint32_t pass) {
-    const uint32_t row = min(tile * 16u + (uint32_t)nl, N - 1u);
+    const uint32_t row = min(tile * 16u + lrow, N - 1u);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const uint32_t b = min(4u * group_of(pass, j) + g, nb - 1u);
+      const uint32_t b = min(4u * group_of(pass, j) + lblk, nb - 1u);
       Fmt::load(w.r[j], codes, scales, (size_t)row * nb + b);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -664,26 +695,30 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     uint32_t ti = 0;                        // tiles of this pass done
     // Tile tt from register set w; w is refilled with tile `next` as soon
     // as its registers are consumed (not for the last tile of the pass).
-    auto do_tile = [&](WSet& w, uint32_t next, auto reload) {
+    // kFull: every group of the pass exists and has four blocks, so the
+    // steps need no guards and the compiler may overlap one step's table
+    // reads with the previous step's arithmetic.
+    auto do_tile = [&](WSet& w, uint32_t next, auto reload, auto full) {
+      constexpr bool kFull = decltype(full)::value;
       f32x4 acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         const uint32_t q = group_of(pass, j);
-        if (q < ngroups) {                   // wavefront-uniform
+        if (kFull || q < ngroups) {          // wavefront-uniform
           typename Fmt::Dec dec;
-          Fmt::prepare(w.r[j], dec);
+          Fmt::prepare(to_mfma_lanes(w.r[j]), dec);
           // By block: steps past the last block are skipped.  By element:
           // every step touches all four blocks, and a lane whose block lies
           // past the last one contributes zero weights.
-          const uint32_t nsteps = Fmt::kByBlock ? min(4u, nb - 4u * q) : 4u;
-          const bool live = Fmt::kByBlock || 4u * q + g < nb;
+          const uint32_t nsteps = Fmt::kByBlock && !kFull ? min(4u, nb - 4u * q) : 4u;
+          const bool live = kFull || Fmt::kByBlock || 4u * q + g < nb;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            if ((uint32_t)s < nsteps) {
+            if (kFull || (uint32_t)s < nsteps) {
               bf16x8 B = Fmt::operand(dec, s, g, lut, laneoff);
-              if (!Fmt::kByBlock && !live) B = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+              if (!kFull && !Fmt::kByBlock && !live) B = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[j][s][mt]), B,
@@ -700,15 +735,21 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
       if (ti % (uint32_t)kRing == 0u) flush(ti - (uint32_t)kRing, (uint32_t)kRing, pass);
     };
     // Fixed trip count with clamped, unconditional prefetches (exact waits).
-    uint32_t t = t0;
-    uint32_t i = 0;
-    for (; i + 2 <= n; i += 2) {
-      do_tile(pa, min(t + 2 * G, last), std::true_type{});
-      t += G;
-      do_tile(pb, min(t + 2 * G, last), std::true_type{});
-      t += G;
-    }
-    if (i < n) do_tile(pa, last, std::false_type{});
+    auto run_tiles = [&](auto full) {
+      uint32_t t = t0;
+      uint32_t i = 0;
+      for (; i + 2 <= n; i += 2) {
+        do_tile(pa, min(t + 2 * G, last), std::true_type{}, full);
+        t += G;
+        do_tile(pb, min(t + 2 * G, last), std::true_type{}, full);
+        t += G;
+      }
+      if (i < n) do_tile(pa, last, std::false_type{}, full);
+    };
+    // (With four 16-row tiles the guard-free copy of the loop costs registers
+    // the kernel does not have: it spilled and ran slower.)
+    if (MT <= 2 && (pass + 1u) * kPassGroups * 4u <= nb) run_tiles(std::true_type{});
+    else run_tiles(std::false_type{});
     if (ti % (uint32_t)kRing != 0u) flush(ti - ti % (uint32_t)kRing, ti % (uint32_t)kRing, pass);
   }
 }
