@@ -33,8 +33,9 @@
 // flop per byte of packed weight), so HBM remains the bound.
 //
 // Precision: with bf16 activations both operands carry up to 2^-8 relative
-// rounding, so each rotated-domain product q_k x'_k is off by at most 2^-7 of
-// its size; for dense activations the errors average out to about
+// rounding (the persistent kernel's weights 2^-8 + 2^-11: fp16 centroids), so
+// each rotated-domain product q_k x'_k is off by at most 2^-7 + 2^-10 of its
+// size; for dense activations the errors average out to about
 // 2^-9 * ||w o x||_2, inside 1e-3 * sum|w x| once K is in the hundreds.  With
 // float32 activations each operand is split into bf16 hi + lo (hi by
 // truncation, lo = bf16(v - hi)) and three MFMAs (hi*hi + hi*lo + lo*hi) leave
@@ -85,6 +86,36 @@ __device__ __forceinline__ void dequant8(uint32_t w, float d, const uint8_t* lut
     const float2 c = *reinterpret_cast<const float2*>(lut + pair_addr(w, laneoff, k));
     v[2 * k] = c.x * d;
     v[2 * k + 1] = c.y * d;
+  }
+}
+
+// The persistent kernel's pair table holds fp16 pairs: entry e (the byte of
+// two nibbles, low nibble = even element) is the dword f16(c[e % 16]) |
+// f16(c[e / 16]) << 16, in 64 copies (entry e, copy l at byte 256 e + 4 l),
+// so one ds_read_b32 per lane serves all 64 lanes without bank conflicts and
+// reads half the bytes of the float32 table.  The centroids in fp16 carry
+// 11 significant bits; their product with an fp16 scale is exact in float32
+// and is rounded once, to the bf16 operand.
+constexpr int kLut16Bytes = 256 * 64 * 4;
+
+__device__ __forceinline__ void fill_pair_lut16(uint8_t* lut, int tid, int nthreads) {
+  const int lane = tid & 63, g = lane >> 4;
+  for (int w = tid >> 6; w < 16; w += nthreads >> 6) {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    float hi = centroid(0);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) hi = wu == k ? centroid(k) : hi;
+    const uint32_t hb = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)hi) << 16;
+    uint8_t* base = lut + ((16 * wu + g) << 8) + 16 * (lane & 15);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float lo = g == 0   ? centroid(4 * u)
+                       : g == 1 ? centroid(4 * u + 1)
+                       : g == 2 ? centroid(4 * u + 2)
+                                : centroid(4 * u + 3);
+      const uint32_t v = hb | __builtin_bit_cast(unsigned short, (_Float16)lo);
+      *reinterpret_cast<uint4*>(base + (u << 10)) = make_uint4(v, v, v, v);
+    }
   }
 }
 
@@ -354,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 // ---------------------------------------------------------------------------
 
 // TQ4_1S: 16 bytes of nibbles and the fp16 scale pair per block; each weight
-// is the centroid pair lookup times its fp16 scale, rounded to bf16.
+// is the fp16 centroid pair lookup times its fp16 scale, rounded to bf16.
 struct GemmTQ4 {
   static constexpr bool kLut = true, kByBlock = true, kTensorScale = false;
   static constexpr int kLoads = 2;
@@ -385,9 +416,9 @@ struct GemmTQ4 {
     float v[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float2 c = *reinterpret_cast<const float2*>(lut + pair_addr(d.w[s], laneoff, k));
-      v[2 * k] = __builtin_fmaf(c.x, sc, 0.0f);
-      v[2 * k + 1] = __builtin_fmaf(c.y, sc, 0.0f);
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(lut + pair_addr(d.w[s], laneoff, k));
+      v[2 * k] = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (unsigned short)(c & 0xffffu)), sc, 0.0f);
+      v[2 * k + 1] = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (unsigned short)(c >> 16)), sc, 0.0f);
     }
     return as_bf16x8(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                      pack_bf16x2(v[6], v[7]));
@@ -498,7 +529,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   // LDS: pair table (TQ4_1S only) | partial-tile ring | pass accumulator.
   // While a pass's activations are staged, the ring's space holds a part of
   // them at a time.
-  constexpr int kLutSpace = Fmt::kLut ? kLutBytes : 0;
+  constexpr int kLutSpace = Fmt::kLut ? kLut16Bytes : 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLutSpace + kRingBytes + kAccFloats * 4];
   uint8_t* const lut = smem;
   f32x4 (*const ring)[kWide][MT][64] = reinterpret_cast<f32x4 (*)[kWide][MT][64]>(smem + kLutSpace);
@@ -510,7 +541,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15;
   const uint32_t g = (uint32_t)(lane >> 4);
-  const uint32_t laneoff = (uint32_t)(lane & (kCopies - 1)) * 8u;
+  const uint32_t laneoff = (uint32_t)lane * 4u;          // this lane's copy in the fp16 pair table
   const uint32_t ngroups = (nb + 3u) / 4u;
   constexpr uint32_t kPassGroups = (uint32_t)(kWide * NQ);
   const uint32_t passes = (ngroups + kPassGroups - 1u) / kPassGroups;
@@ -668,7 +699,7 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     // LDS stores wait for any DMA into LDS still in flight.)
     load_w(pa, t0, pass);
     if constexpr (Fmt::kLut) {
-      if (pass == pass_begin) fill_pair_lut(lut, tid, 64 * kWide);
+      if (pass == pass_begin) fill_pair_lut16(lut, tid, 64 * kWide);
     }
     dma_x(pass, 0);
     __syncthreads();                        // first part staged (and the table filled)

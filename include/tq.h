@@ -170,8 +170,9 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  * activations, three hi/lo-split passes for float32 activations.
  * Precision of the MFMA path: the products are formed in the rotated domain,
  * so what is guaranteed is a bound on sum_k |q_k x'_k| (q = d * c[idx]):
- * per product at most 2^-7 of |q x'| with bf16 x' (bf16 x' and the bf16
- * weight round by up to 2^-8 each), at most 2^-13 with float32 x' (hi/lo
+ * per product at most 2^-7 + 2^-10 of |q x'| with bf16 x' (x' rounds by up
+ * to 2^-8; the weight, the fp16-rounded centroid times the scale rounded
+ * once to bf16, by up to 2^-8 + 2^-11), at most 2^-13 with float32 x' (hi/lo
  * split without the lo*lo term), plus float32 accumulation over K.  The
  * original-domain bound 1e-3 * sum_k |W_deq[n,k] x_k| is only statistical:
  * it holds for dense activations (bf16 once K is in the hundreds, float32 at
