@@ -507,10 +507,10 @@ struct GemmMXFP6 {
 // an LDS accumulator (32 KiB, one float per output of the workgroup; the
 // host splits taller launches) and Y is written once, by the last pass: a
 // global read of Y in the loop would also wait for the weight prefetch,
-// since vector loads complete in issue order.  The activation operands are requested before
-// the pair table is filled and the weights after it: a workgroup that issued
-// everything at once (a few hundred KiB per CU) stalled its wavefronts on
-// load issue for several microseconds before computing anything.
+// since vector loads complete in issue order.  Each wavefront loads its own
+// activation operands from X (no LDS staging, no workgroup barrier), then
+// its first two weight tiles, and fills its part of the pair table while
+// they are in flight.
 // ---------------------------------------------------------------------------
 constexpr int kWide = 16;
 constexpr int kRingBytes = 65536;
@@ -527,14 +527,11 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   constexpr int kRing = kRingBytes / (kWide * 64 * 16 * MT);        // weight tiles per ring
   static_assert(kRing * 256 * MT == 64 * kWide, "one output per thread per flush");
   // LDS: pair table (TQ4_1S only) | partial-tile ring | pass accumulator.
-  // While a pass's activations are staged, the ring's space holds a part of
-  // them at a time.
   constexpr int kLutSpace = Fmt::kLut ? kLut16Bytes : 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLutSpace + kRingBytes + kAccFloats * 4];
   uint8_t* const lut = smem;
   f32x4 (*const ring)[kWide][MT][64] = reinterpret_cast<f32x4 (*)[kWide][MT][64]>(smem + kLutSpace);
   float* const accum = reinterpret_cast<float*>(smem + kLutSpace + kRingBytes);
-  uint8_t* const stage = smem + kLutSpace;
   const float ts = Fmt::kTensorScale ? *tscale : 1.0f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -600,61 +597,60 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Activation operands of a pass: 16 MT rows x (16 NQ * 128) elements of
-  // X, staged through LDS one 64 KiB part along K at a time by direct-to-LDS loads
-  // (global_load_lds_dwordx4: no registers held, and every instruction
-  // moves 1 KiB of one row, coalesced).  Piece c of row r is stored at
-  // chunk c ^ (r % 16), so that the operand reads (16 rows x four 16-byte
-  // chunks per instruction) spread over the banks; a lane of a DMA
-  // instruction writes the LDS chunk at its own position, so it reads the
-  // global piece that belongs there.  Rows past M are not staged (their
-  // LDS holds stale bytes) and elements past K are clamped: both only feed
-  // outputs that are not written (an MFMA output row depends on its own
-  // activation row alone) or steps that are skipped.  (Loading the operands straight
-  // from X in the MFMA layout, 16 rows x 64 bytes per instruction, took
-  // about twice as long.)
+  // Activation operands of a pass, straight from X into registers: for
+  // group j, step s and m tile mt, lane (n, g) needs the 8 elements of
+  // activation row 16 mt + n that meet its weights (by block: elements
+  // 32 s + 8 g of the group; by element: 32 g + 8 s).  They are loaded in
+  // row-major lane order, lane 4 n + g reading elements 32 s + 8 g, so that
+  // four neighbouring lanes read 64 contiguous bytes of one row, and handed
+  // to lane n + 16 g by the same ds_bpermute as the weights; the by-element
+  // order then swaps s and g across the lane groups.  No LDS staging and no
+  // workgroup barrier: each wavefront loads only its own operands (an
+  // earlier version staged a pass's activations through LDS in 64 KiB parts,
+  // with two barriers per part).  Rows past M are clamped to row M - 1 and
+  // elements past K to the last block: both only feed outputs that are not
+  // written (an MFMA output row depends on its own activation row alone) or
+  // steps that are skipped.
   constexpr uint32_t kPassK = 16u * NQ * 128u;               // elements of K per pass
-  constexpr int kParts = (int)(16u * MT * kPassK * 2u) / kRingBytes;   // staged one ring-full at a time
-  constexpr uint32_t kPartK = kPassK / (uint32_t)kParts;
-  constexpr uint32_t kRowBytes = kPartK * 2u;                // bytes of one staged row
-  constexpr int kDma = (int)(16u * MT * kRowBytes) / (1024 * kWide);   // 1 KiB DMA instructions per wavefront
-  static_assert(kParts >= 2 && 16u * MT * kRowBytes == (uint32_t)kRingBytes && kRowBytes % 1024u == 0u,
-                "staging layout");
   const uint32_t K = nb * 32u;
-  auto dma_x = [&](uint32_t pass, uint32_t h) {
+  auto load_a = [&](uint32_t pass) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      const uint32_t base = 1024u * (uint32_t)(i * kWide + wave);          // wavefront-uniform LDS offset
-      if (base / kRowBytes >= M) continue;   // an instruction covers part of one row; rows past M are not staged
-      const uint32_t off = base + 16u * (uint32_t)lane;
-      const uint32_t r = off / kRowBytes, c = ((off % kRowBytes) / 16u) ^ (r & 15u);
-      const uint32_t k = min(pass * kPassK + h * kPartK + 8u * c, K - 8u);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(X + ((size_t)r * ldx + k) * 2),
-                                       (__attribute__((address_space(3))) void*)(stage + base), 16, 0, 0);
+    for (int j = 0; j < NQ; ++j) {
+      const uint32_t kg = pass * kPassK + 128u * ((uint32_t)wave + (uint32_t)(kWide * j));   // wavefront-uniform
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t k = min(kg + 32u * (uint32_t)s + 8u * lblk, K - 8u);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint32_t r = min((uint32_t)(16 * mt) + lrow, M - 1u);
+          A[j][s][mt] = *reinterpret_cast<const uint4*>(X + ((size_t)r * ldx + k) * 2);
+        }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // Wait for this wavefront's LDS reads, then for the workgroup.
-  auto lds_done_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt and expcnt left alone
-    __builtin_amdgcn_s_barrier();
-  };
-  // The operands of part h: the groups j of this wavefront that lie in it
-  // (a part holds whole groups), step s in the format's element order.
-  static_assert(kPartK % 128u == 0u, "a part holds whole groups");
-  auto read_ops = [&](uint32_t h) {
+  auto place_a = [&]() {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t kg = 128u * ((uint32_t)wave + (uint32_t)(kWide * j));   // wavefront-uniform
-        if (kg / kPartK == h) {
-          const uint32_t kin = Fmt::kByBlock ? 32u * (uint32_t)s + 8u * g : 32u * g + 8u * (uint32_t)s;
-          const uint32_t c = (kg - h * kPartK + kin) / 8u;
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const uint32_t r = (uint32_t)(16 * mt + nl);
-            A[j][s][mt] = *reinterpret_cast<const uint4*>(stage + r * kRowBytes + 16u * (c ^ (r & 15u)));
-          }
+        for (int s = 0; s < 4; ++s) {
+          uint4& a = A[j][s][mt];
+          a.x = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.x);
+          a.y = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.y);
+          a.z = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.z);
+          a.w = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.w);
+        }
+        if constexpr (!Fmt::kByBlock) {
+          uint32_t t[4][4];
+          transpose_groups(make_uint4(A[j][0][mt].x, A[j][1][mt].x, A[j][2][mt].x, A[j][3][mt].x), t[0]);
+          transpose_groups(make_uint4(A[j][0][mt].y, A[j][1][mt].y, A[j][2][mt].y, A[j][3][mt].y), t[1]);
+          transpose_groups(make_uint4(A[j][0][mt].z, A[j][1][mt].z, A[j][2][mt].z, A[j][3][mt].z), t[2]);
+          transpose_groups(make_uint4(A[j][0][mt].w, A[j][1][mt].w, A[j][2][mt].w, A[j][3][mt].w), t[3]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) A[j][s][mt] = make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]);
         }
       }
     }
@@ -692,36 +688,21 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
 
   WSet pa, pb;
   for (uint32_t pass = pass_begin; pass < pass_end; ++pass) {
-    // The pass's activations and first weights, in the same order on every
-    // pass (the table is filled while the first pass's are in flight); the
-    // waits for the activations leave the weights in flight.
-    // (The table is filled before the first DMA is issued: the compiler makes
-    // LDS stores wait for any DMA into LDS still in flight.)
+    // The pass's activation operands, then its first two weight tiles, in
+    // the same order on every pass; the table is filled while they are in
+    // flight.  Vector loads complete in issue order, so the wait for the
+    // activations (at their first use) leaves the weights in flight.
+    load_a(pass);
     load_w(pa, t0, pass);
+    load_w(pb, min(t0 + G, last), pass);
     if constexpr (Fmt::kLut) {
-      if (pass == pass_begin) fill_pair_lut16(lut, tid, 64 * kWide);
-    }
-    dma_x(pass, 0);
-    __syncthreads();                        // first part staged (and the table filled)
-    read_ops(0);
-    lds_done_barrier();                     // every wavefront has its first-part operands
-    static_for<kParts - 1>([&](auto pc) {
-      constexpr int part = decltype(pc)::value + 1;
-      dma_x(pass, (uint32_t)part);
-      if constexpr (part == 1) {
-        load_w(pb, min(t0 + G, last), pass);
-        // Wait for this wavefront's DMA, issued just before the kLoads NQ
-        // loads of pb (vector loads complete in order), so pb stays in
-        // flight; then for the workgroup.
-        static_assert(Fmt::kLoads * NQ < 16, "vmcnt field");
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (Fmt::kLoads * NQ));
-      } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+      if (pass == pass_begin) {
+        fill_pair_lut16(lut, tid, 64 * kWide);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's table stores; loads left in flight
+        __builtin_amdgcn_s_barrier();         // the whole table
       }
-      __builtin_amdgcn_s_barrier();
-      read_ops((uint32_t)part);
-      lds_done_barrier();                   // the ring's space is free again
-    });
+    }
+    place_a();
 
     uint32_t ti = 0;                        // tiles of this pass done
     // Tile tt from register set w; w is refilled with tile `next` as soon
