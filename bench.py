@@ -538,7 +538,8 @@ BF_BYTES = {"nvfp4": 0.5625, "mxfp6": 0.78125}
 
 def bench_blockfp(torch, tqa, wl, dev, stream, layers, no_graph):
     """27B-shaped layers (all 64 by default): per-tensor NVFP4 or MXFP6 (seeded, ~10% MXFP6); quantize, and
-    the fused decode at M = 1 (VALU GEMV), 8, 16 and 64 (bf16 MFMA), one launch per tensor, graph-replayed."""
+    the fused decode at M = 1 (VALU GEMV), 8, 16 and 64 (bf16 MFMA), graph-replayed, over the loader's
+    layout (same-format q|k|v and gate|up members concatenated) and over one launch per tensor."""
     names = ["q", "k", "v", "o", "gate", "up", "down"]
     fmt_count = {"nvfp4": 0, "mxfp6": 0}
     src = []
@@ -596,34 +597,26 @@ def bench_blockfp(torch, tqa, wl, dev, stream, layers, no_graph):
            "quantize_ms": round(q_ms, 2), "quantize_rsf_GB_s": round(q_bytes / (rsf_ms * 1e-3) / 1e9, 1),
            "quantize_bytes": "NVFP4 reads the bf16 weights twice (amax, encode); MXFP6 once",
            "quantize_launches": "NVFP4: amax + encode; MXFP6: encode"}
+    # gemv_M{m}: the layout a loader produces (same-format members of q|k|v and of gate|up
+    # row-concatenated, one launch each); gemv_M{m}_per_tensor: one launch per tensor, for contrast.
+    res["layout"] = "gemv_M*: same-format members of q|k|v and of gate|up row-concatenated; o and down alone"
     for m in (1, 8, 16, 64):
         xsv = {}
         for (fmt, codes, bs, ts, n, k) in store:
             if k not in xsv:
                 g = wl.generator(wl.seed_of(4, m, k), dev)
                 xsv[k] = wl.activation(m, k, g, dev, torch.bfloat16)
-        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for (_, _, _, _, n, _) in store]
+        for key, tensors in ((f"gemv_M{m}", fused), (f"gemv_M{m}_per_tensor", store)):
+            ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for (_, _, _, _, n, _) in tensors]
 
-        def run():
-            for i, (fmt, codes, bs, ts, n, k) in enumerate(store):
-                tqa.blockfp_gemm(fmt, codes, bs, ts, xsv[k], out=ys[i])
+            def run(tensors=tensors, ys=ys):
+                for i, (fmt, codes, bs, ts, n, k) in enumerate(tensors):
+                    tqa.blockfp_gemm(fmt, codes, bs, ts, xsv[k], out=ys[i])
 
-        ms = _time_graph(torch, stream, run, 3, no_graph)
-        byts = sum((BF_BYTES[f] * n * k + 2 * m * k + 4 * m * n) for (f, _, _, _, n, k) in store)
-        res[f"gemv_M{m}"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
-                             "launches": len(store)}
-        if m in (1, 8):
-            yf = [torch.empty((m, n), dtype=torch.float32, device=dev) for (_, _, _, _, n, _) in fused]
-
-            def run_fused():
-                for i, (fmt, codes, bs, ts, n, k) in enumerate(fused):
-                    tqa.blockfp_gemm(fmt, codes, bs, ts, xsv[k], out=yf[i])
-
-            ms = _time_graph(torch, stream, run_fused, 3, no_graph)
-            byts = sum((BF_BYTES[f] * n * k + 2 * m * k + 4 * m * n) for (f, _, _, _, n, k) in fused)
-            res[f"gemv_M{m}_fused"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
-                                       "launches": len(fused),
-                                       "layout": "same-format members of q|k|v and of gate|up row-concatenated"}
+            ms = _time_graph(torch, stream, run, 3, no_graph)
+            byts = sum((BF_BYTES[f] * n * k + 2 * m * k + 4 * m * n) for (f, _, _, _, n, k) in tensors)
+            res[key] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1), "launches": len(tensors)}
+            del ys
     del store, fused
     torch.cuda.empty_cache()
     return res

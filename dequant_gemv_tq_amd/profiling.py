@@ -120,13 +120,17 @@ def gemm_run() -> None:
     print("gemm counter run done", flush=True)
 
 
-def gemm_summarize(db: str) -> None:
-    """MFMA utilisation and bf16 MFMA flops per GEMM dispatch from a --pmc MfmaUtil MfmaFlopsBF16 run."""
+GEMM_SQ = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY",
+           "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES")
+
+
+def _gemm_dispatches(db: str, counters) -> list:
     con = sqlite3.connect(db)
+    marks = ", ".join("?" for _ in counters)
     rows = con.execute(
         "select dispatch_id, kernel_name, counter_name, sum(value) from counters_collection "
-        "where counter_name in ('MfmaUtil', 'MfmaFlopsBF16') group by dispatch_id, kernel_name, counter_name "
-        "order by dispatch_id").fetchall()
+        f"where counter_name in ({marks}) group by dispatch_id, kernel_name, counter_name "
+        "order by dispatch_id", tuple(counters)).fetchall()
     con.close()
     per = {}
     for d, name, cname, v in rows:
@@ -137,11 +141,21 @@ def gemm_summarize(db: str) -> None:
     expect = len(GROUPS) * len(GEMM_BATCHES) * COPIES
     if len(disp) != expect:
         raise RuntimeError(f"expected {expect} GEMM dispatches, found {len(disp)}")
+    return disp
+
+
+def gemm_summarize(db: str, sq_db: str | None = None) -> None:
+    """MFMA utilisation and bf16 MFMA flops per GEMM dispatch from a --pmc MfmaUtil MfmaFlopsBF16 run, and
+    (with a second database from a --pmc run of GEMM_SQ) the wavefronts' instruction counts and waits."""
+    disp = _gemm_dispatches(db, ("MfmaUtil", "MfmaFlopsBF16"))
     lines = ["# Small-batch GEMM: MFMA utilisation (Llama-3-8B groups, bf16 pre-rotated activations)", "",
              "Commands (repository root on the GPU host; OUT is any scratch folder):", "", "```",
              "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 -d OUT/mfma -o mfma -- python3 -m dequant_gemv_tq_amd.profiling "
              "gemm_run",
-             "python3 -m dequant_gemv_tq_amd.profiling gemm_summarize OUT/mfma/mfma_results.db", "```", "",
+             "rocprofv3 --pmc " + " ".join(GEMM_SQ) + " -d OUT/sq -o sq -- python3 -m "
+             "dequant_gemv_tq_amd.profiling gemm_run",
+             "python3 -m dequant_gemv_tq_amd.profiling gemm_summarize OUT/mfma/mfma_results.db OUT/sq/sq_results.db",
+             "```", "",
              "MfmaUtil is rocprofv3's derived counter (MFMA busy cycles over GPU-active cycles times SIMD count, "
              "in %); MfmaFlopsBF16 counts the bf16 MFMA work issued, against 2 * 16 * ceil(M / 16) * N * K for "
              "the padded activation tiles.", "",
@@ -155,9 +169,29 @@ def gemm_summarize(db: str) -> None:
             util = statistics.median(c.get("MfmaUtil", 0.0) for c in chunk)
             fl = statistics.median(c.get("MfmaFlopsBF16", 0.0) for c in chunk)
             import re
-            kn = re.search(r"gemm_small_kernel<[^>]*>", chunk[0]["name"])
+            kn = re.search(r"gemm_small_kernel<[^>]*>", chunk[0]["name"].replace("tq::(anonymous namespace)::", ""))
             lines.append(f"| {gname} | {n} x {k} | {m} | `{kn.group(0) if kn else chunk[0]['name']}` | {util:.1f} | "
                          f"{fl / 1e9:.3f} | {2 * 16 * ((m + 15) // 16) * n * k / 1e9:.3f} |")
+    if sq_db:
+        sq = _gemm_dispatches(sq_db, GEMM_SQ)
+        lines += ["", "Wavefront counters (median over the launches; SQ_WAVE_CYCLES is the summed lifetime of the "
+                  "wavefronts, so the wait columns are shares of it):", "",
+                  "| group | M | VALU instr per wavefront | LDS instr per wavefront | waiting (SQ_WAIT_ANY) % | "
+                  "waiting on LDS (SQ_WAIT_INST_LDS) % | issuing VALU (SQ_ACTIVE_INST_VALU) % |",
+                  "|---|---|---|---|---|---|---|"]
+        i = 0
+        for gname, (n, k) in GROUPS.items():
+            for m in GEMM_BATCHES:
+                chunk = sq[i:i + COPIES]
+                i += COPIES
+
+                def med(key, chunk=chunk):
+                    return statistics.median(c.get(key, 0.0) for c in chunk)
+                waves, cyc = max(med("SQ_WAVES"), 1.0), max(med("SQ_WAVE_CYCLES"), 1.0)
+                lines.append(f"| {gname} | {m} | {med('SQ_INSTS_VALU') / waves:.0f} | "
+                             f"{med('SQ_INSTS_LDS') / waves:.0f} | {100 * med('SQ_WAIT_ANY') / cyc:.1f} | "
+                             f"{100 * med('SQ_WAIT_INST_LDS') / cyc:.1f} | "
+                             f"{100 * med('SQ_ACTIVE_INST_VALU') / cyc:.1f} |")
     print("\n".join(lines + [""]))
 
 
@@ -411,8 +445,8 @@ if __name__ == "__main__":
         stats(sys.argv[2])
     elif len(sys.argv) >= 2 and sys.argv[1] == "gemm_run":
         gemm_run()
-    elif len(sys.argv) == 3 and sys.argv[1] == "gemm_summarize":
-        gemm_summarize(sys.argv[2])
+    elif len(sys.argv) in (3, 4) and sys.argv[1] == "gemm_summarize":
+        gemm_summarize(sys.argv[2], sys.argv[3] if len(sys.argv) == 4 else None)
     elif len(sys.argv) >= 2 and sys.argv[1] == "kv_run":
         kv_run()
     elif len(sys.argv) == 4 and sys.argv[1] == "kv_summarize":
