@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
     L.tq_dequantize.argtypes = [p, p, i64, i64, u32, p, c_int, i64, p]
     L.tq_rotate.argtypes = [p, c_int, i64, i64, i64, u32, p, c_int, i64, p]
     L.tq_gemv.argtypes = [p, p, i64, i64, u32, p, c_int, c_int, p, p]
-    L.tq_gemm.argtypes = [p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
+    L.tq_gemm.argtypes = [p, p, i64, i64, i64, p, c_int, i64, p, i64, p, ctypes.c_size_t, p]
     L.tq_blockfp_quantize.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p, ctypes.c_size_t, p]
     L.tq_blockfp_quantize_rsf.argtypes = [c_int, p, c_int, i64, i64, p, p, p, p, ctypes.c_size_t, p]
     L.tq_workspace_bytes.argtypes = [c_int, i64, i64, i64]
@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L.tq_attn_decode_noalloc.restype = c_int
     L.tq_stream_read.argtypes = [p, ctypes.c_size_t, p, p]
     L.tq_stream_read.restype = c_int
-    L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p]
+    L.tq_blockfp_gemm.argtypes = [c_int, p, p, p, i64, i64, i64, p, c_int, i64, p, i64, p, ctypes.c_size_t, p]
     L.tq_transcode_q8.argtypes = [p, p, i64, i64, u32, p, p, p]
     L.tq_q8_gemv.argtypes = [p, p, i64, i64, p, c_int, p, p]
     L.tq_kv_sign_from_seed.argtypes = [ctypes.c_uint64, p]
@@ -257,8 +257,38 @@ def gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, rotated: b
     return y
 
 
-def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=None):
-    """Y [M, N] float32 = X' Q^T with pre-rotated activations x_rot [M, K] (bf16 or fp32)."""
+_GEMM_WS = {}      # (device index, stream) -> zero-filled split-K workspace
+
+
+def _gemm_workspace(op: str, N: int, K: int, M: int, xbf16: bool, device, workspace):
+    """The split-K workspace of a GEMM call: the caller's, checked, or one kept per device and stream.
+
+    The library's contract: zero-filled before its first use, left fit for the next call by every
+    call, and never used by two calls at once -- hence one buffer per stream.
+    """
+    need = workspace_bytes(op, N, K, M) if (xbf16 and M > 4) else 0
+    if workspace is not None:
+        _need(isinstance(workspace, torch.Tensor) and workspace.dtype == torch.uint8 and workspace.is_contiguous()
+              and workspace.numel() >= need, f"workspace must be a contiguous uint8 buffer of at least {need} bytes")
+        _need(workspace.device == device, "workspace must be on the weights' device")
+        _need(workspace.data_ptr() % 256 == 0, "workspace must be 256-byte aligned")
+        return workspace
+    if need == 0:
+        return None
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _GEMM_WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _GEMM_WS[key] = ws
+    return ws
+
+
+def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=None, workspace=None):
+    """Y [M, N] float32 = X' Q^T with pre-rotated activations x_rot [M, K] (bf16 or fp32).
+
+    workspace: optional uint8 device buffer for the split-K sums (see tq_gemm); by default one
+    zero-filled buffer per device and stream is kept and reused.
+    """
     N, K = _tq4_weights(packed, scales)
     _dev(x_rot, "x_rot")
     M = x_rot.shape[0]
@@ -267,8 +297,9 @@ def gemm(packed: torch.Tensor, scales: torch.Tensor, x_rot: torch.Tensor, out=No
     y = torch.empty((M, N), dtype=torch.float32, device=packed.device) if out is None else out
     _rows(y, "out", (torch.float32,), M, N)
     _same_device(packed, (x_rot, "x_rot"), (y, "out"))
+    ws = _gemm_workspace("gemm", N, K, M, x_rot.dtype == torch.bfloat16, packed.device, workspace)
     st = lib().tq_gemm(_ptr(packed), _ptr(scales), N, K, M, _ptr(x_rot), _dtype_code(x_rot, "x_rot"),
-                       x_rot.stride(0), _ptr(y), y.stride(0), _stream())
+                       x_rot.stride(0), _ptr(y), y.stride(0), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     _check("tq_gemm", st)
     return y
 
@@ -327,8 +358,8 @@ def blockfp_quantize(fmt: str, W: torch.Tensor, rsf: bool = False, workspace=Non
 
 
 def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tensor_scale, x: torch.Tensor,
-                 out=None):
-    """Y [M, N] float32 = X W_deq^T (x: [M, K] or [K], fp32/bf16)."""
+                 out=None, workspace=None):
+    """Y [M, N] float32 = X W_deq^T (x: [M, K] or [K], fp32/bf16); workspace as for gemm()."""
     f = FORMATS[fmt]
     _need(isinstance(codes, torch.Tensor) and codes.dim() == 2, "codes must be a 2-D uint8 tensor")
     N = codes.shape[0]
@@ -349,8 +380,10 @@ def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tens
     _rows(y2, "out", (torch.float32,), M, N)
     _same_device(codes, (x2, "x"), (y2, "out"))
     y = y2 if y.dim() == 2 else y
+    ws = _gemm_workspace("blockfp_gemm", N, K, M, x2.dtype == torch.bfloat16, codes.device, workspace)
     st = lib().tq_blockfp_gemm(f, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), N, K, M, _ptr(x2),
-                               _dtype_code(x2, "x"), x2.stride(0), _ptr(y2), y2.stride(0), _stream())
+                               _dtype_code(x2, "x"), x2.stride(0), _ptr(y2), y2.stride(0), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream())
     _check("tq_blockfp_gemm", st)
     return y if x.dim() == 2 else y.reshape(-1)
 

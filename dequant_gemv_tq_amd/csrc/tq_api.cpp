@@ -101,14 +101,18 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
 }
 
 tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
-                  const void* x_rot, tq_dtype xt, int64_t ldx, float* y, int64_t ldy, hipStream_t stream) {
+                  const void* x_rot, tq_dtype xt, int64_t ldx, float* y, int64_t ldy, void* workspace,
+                  size_t ws_bytes, hipStream_t stream) {
   if (!x_rot || !y || M <= 0) return TQ_EINVAL;
   if (tq_status st = check_weights(packed, scales, N, K)) return st;
   if (ldx < K || ldy < N) return TQ_EINVAL;
   if (M > 256 || K > 131072 || N > 0x7fffffff) return TQ_ESHAPE;
   if (!float_or_bf16(xt)) return TQ_EDTYPE;
   if (!aligned(x_rot, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4)) return TQ_EALIGN;
-  return from_hip(tq::launch_gemm(packed, scales, N, K, M, x_rot, xt == TQ_BF16, ldx, y, ldy, stream));
+  const size_t need = tq::gemm_workspace_bytes(N, K, M, xt == TQ_BF16);
+  if (need && (!workspace || ws_bytes < need)) return TQ_EINVAL;
+  if (need && !aligned(workspace, 256)) return TQ_EALIGN;
+  return from_hip(tq::launch_gemm(packed, scales, N, K, M, x_rot, xt == TQ_BF16, ldx, y, ldy, workspace, stream));
 }
 
 static tq_status blockfp_quantize(tq_format f, const void* W, tq_dtype wt, int64_t N, int64_t K, uint8_t* codes,
@@ -140,9 +144,12 @@ tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64
 
 size_t tq_workspace_bytes(int op, int64_t N, int64_t K, int64_t M) {
   switch (op) {
-    case TQ_OP_QUANTIZE: case TQ_OP_DEQUANTIZE: case TQ_OP_ROTATE: case TQ_OP_GEMV: case TQ_OP_GEMM:
-    case TQ_OP_MXFP6_QUANTIZE: case TQ_OP_BLOCKFP_GEMM: case TQ_OP_TRANSCODE_Q8: case TQ_OP_Q8_GEMV:
+    case TQ_OP_QUANTIZE: case TQ_OP_DEQUANTIZE: case TQ_OP_ROTATE: case TQ_OP_GEMV:
+    case TQ_OP_MXFP6_QUANTIZE: case TQ_OP_TRANSCODE_Q8: case TQ_OP_Q8_GEMV:
       return 0;
+    case TQ_OP_GEMM: case TQ_OP_BLOCKFP_GEMM:
+      if (N <= 0 || K <= 0 || M <= 0) return SIZE_MAX;
+      return tq::gemm_workspace_bytes(N, K, M, true);
     case TQ_OP_NVFP4_QUANTIZE:
       return TQ_NVFP4_WORKSPACE_BYTES;
     case TQ_OP_ATTN_DECODE:
@@ -154,7 +161,7 @@ size_t tq_workspace_bytes(int op, int64_t N, int64_t K, int64_t M) {
 
 tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale,
                           int64_t N, int64_t K, int64_t M, const void* x, tq_dtype xt, int64_t ldx, float* y,
-                          int64_t ldy, hipStream_t stream) {
+                          int64_t ldy, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (f != TQ_FMT_NVFP4 && f != TQ_FMT_MXFP6) return TQ_EINVAL;
   if (!codes || !block_scales || !x || !y || N <= 0 || K <= 0 || M <= 0) return TQ_EINVAL;
   if (f == TQ_FMT_NVFP4 && !tensor_scale) return TQ_EINVAL;
@@ -165,8 +172,11 @@ tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* bloc
   if (!aligned(codes, f == TQ_FMT_NVFP4 ? 16 : 8) || !aligned(x, 16) || (ldx * dtype_size(xt)) % 16 || !aligned(y, 4))
     return TQ_EALIGN;
   if (f == TQ_FMT_NVFP4 && (!aligned(block_scales, 2) || !aligned(tensor_scale, 4))) return TQ_EALIGN;
+  const size_t need = tq::gemm_workspace_bytes(N, K, M, xt == TQ_BF16);
+  if (need && (!workspace || ws_bytes < need)) return TQ_EINVAL;
+  if (need && !aligned(workspace, 256)) return TQ_EALIGN;
   return from_hip(tq::launch_blockfp_gemm((int)f, codes, block_scales, tensor_scale, N, K, M, x, xt == TQ_BF16, ldx,
-                                          y, ldy, stream));
+                                          y, ldy, workspace, stream));
 }
 
 tq_status tq_transcode_q8(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, uint32_t sign_mask,

@@ -507,7 +507,15 @@ struct GemmMXFP6 {
 // an LDS accumulator (32 KiB, one float per output of the workgroup; the
 // host splits taller launches) and Y is written once, by the last pass: a
 // global read of Y in the loop would also wait for the weight prefetch,
-// since vector loads complete in issue order.  Each wavefront loads its own
+// since vector loads complete in issue order.
+//
+// Few row tiles and K in several passes: the passes are split over S sets
+// of workgroups (one pass each), so every workgroup takes several tiles and
+// reads the activations of one pass only.  Each set stores its sums to a
+// workspace; once a workgroup has stored all of its tiles it counts them on
+// per-tile counters, and the workgroup that brings a count to S adds the S
+// stored sums in split order and writes Y (so Y does not depend on which
+// set finishes last), then returns the counter to zero.  Each wavefront loads its own
 // activation operands from X (no LDS staging, no workgroup barrier), then
 // its first two weight tiles, and fills its part of the pair table while
 // they are in flight.
@@ -523,7 +531,8 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
                                                                 uint32_t nb, const uint8_t* __restrict__ X,
                                                                 int64_t ldx, uint32_t M, float* __restrict__ Y,
                                                                 int64_t ldy, uint32_t G, uint32_t tq, uint32_t tr,
-                                                                uint32_t halves) {
+                                                                uint32_t S, float* __restrict__ part,
+                                                                uint32_t* __restrict__ counters) {
   constexpr int kRing = kRingBytes / (kWide * 64 * 16 * MT);        // weight tiles per ring
   static_assert(kRing * 256 * MT == 64 * kWide, "one output per thread per flush");
   // LDS: pair table (TQ4_1S only) | partial-tile ring | pass accumulator.
@@ -543,15 +552,14 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   constexpr uint32_t kPassGroups = (uint32_t)(kWide * NQ);
   const uint32_t passes = (ngroups + kPassGroups - 1u) / kPassGroups;
 
-  // K split in two (halves == 2, few row tiles): workgroups G.. 2G - 1 take
-  // the same tiles as 0 .. G - 1 over the second half of the passes, and
-  // both halves add their sums into Y, which the launch zeroed first; with
-  // two addends onto zero the result does not depend on their order.
-  const uint32_t half = blockIdx.x / G;
-  const uint32_t t0 = blockIdx.x - half * G;
-  const uint32_t mid = (passes + 1u) / 2u;
-  const uint32_t pass_begin = halves == 2u ? half * mid : 0u;
-  const uint32_t pass_end = halves == 2u && half == 0u ? mid : passes;
+  // Workgroups sG .. sG + G - 1 take the same tiles over split s of the
+  // passes (S == 1: all of them).
+  const uint32_t split = blockIdx.x / G;
+  const uint32_t t0 = blockIdx.x - split * G;
+  const uint32_t per_split = (passes + S - 1u) / S;
+  const uint32_t pass_begin = split * per_split;
+  const uint32_t pass_end = min(pass_begin + per_split, passes);
+  const uint32_t T = (N + 15u) / 16u;                    // row tiles
   const uint32_t n = tq + (t0 < tr ? 1u : 0u);          // this workgroup's tiles
   const uint32_t last = t0 + (n - 1u) * G;
 
@@ -676,10 +684,11 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
         const uint32_t tt = t0 + (first + slot) * G;
         const uint32_t row = tt * 16u + (uint32_t)(l & 15);
         const uint32_t m = (uint32_t)mt * 16u + 4u * (uint32_t)(l >> 4) + (uint32_t)r;
-        if (m < M && row < N) {
-          const float v = Fmt::kTensorScale ? sum * ts : sum;
-          if (halves == 2u) unsafeAtomicAdd(Y + (size_t)m * ldy + row, v);
-          else Y[(size_t)m * ldy + row] = v;
+        if (S == 1u) {
+          if (m < M && row < N) Y[(size_t)m * ldy + row] = Fmt::kTensorScale ? sum * ts : sum;
+        } else {
+          __hip_atomic_store(part + ((size_t)split * T + tt) * (256u * MT) + o, sum, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
@@ -764,6 +773,98 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     else run_tiles(std::false_type{});
     if (ti % (uint32_t)kRing != 0u) flush(ti - ti % (uint32_t)kRing, ti % (uint32_t)kRing, pass);
   }
+
+  if (S > 1u) {
+    // Every tile's sums of this split are stored: count the tiles, and add
+    // up those whose count this workgroup completes, in split order.  The
+    // sums are stored and loaded as device-scope atomics, which the L2
+    // caches of the chip keep coherent without a cache writeback or
+    // invalidation (a __threadfence() here cost more than the whole GEMM);
+    // each wavefront waits for its stores to complete before the barrier,
+    // and the counting atomics are issued after it.  The ring, no longer
+    // needed, holds the per-tile "last split" flags.
+    uint32_t* const flags = reinterpret_cast<uint32_t*>(&ring[0][0][0][0]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (uint32_t i = (uint32_t)tid; i < n; i += 64u * kWide)
+      flags[i] = __hip_atomic_fetch_add(counters + t0 + i * G, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                         S - 1u ? 1u : 0u;
+    __syncthreads();
+    constexpr uint32_t kOut = 256u * MT;
+    for (uint32_t e = (uint32_t)tid; e < n * kOut; e += 64u * kWide) {
+      const uint32_t i = e / kOut, o = e - i * kOut;
+      if (!flags[i]) continue;
+      const uint32_t tt = t0 + i * G;
+      // Eight loads in flight at a time, added in split order.
+      float sum = 0.f;
+      for (uint32_t s0 = 0; s0 < S; s0 += 8u) {
+        float v[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u)
+          v[u] = __hip_atomic_load(part + ((size_t)min(s0 + u, S - 1u) * T + tt) * kOut + o, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (uint32_t u = 0; u < 8u; ++u)
+          if (s0 + u < S) sum += v[u];
+      }
+      const uint32_t l = (o % 256u) >> 2;
+      const uint32_t row = tt * 16u + (l & 15u);
+      const uint32_t m = (o / 256u) * 16u + 4u * (l >> 4) + (o & 3u);
+      if (m < M && row < N) Y[(size_t)m * ldy + row] = Fmt::kTensorScale ? sum * ts : sum;
+      if (o == 0u) __hip_atomic_store(counters + tt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Workspace layout: a fixed region of per-tile counters (one launch that
+// splits K covers at most kSplitTiles row tiles; taller matrices are
+// launched in row chunks), then the sums of every split.  The counters sit
+// at the same place for every shape, so the sums of one call never land
+// where another call's counters are, and every call leaves them at zero.
+constexpr uint32_t kSplitTiles = 16384;
+constexpr size_t kCounterBytes = kSplitTiles * 4;
+
+// Launch shape of the persistent kernel for Nc rows: S sets of workgroups
+// (one pass of K each when the tiles are few, else one set over all
+// passes), G workgroups per set with the tiles spread evenly.
+struct SmallPlan {
+  uint32_t S, G, tq, tr;
+};
+SmallPlan small_plan(uint32_t Nc, uint32_t nb, int NQ, uint32_t cap) {
+  const uint32_t passes = ((nb + 3u) / 4u + kWide * NQ - 1u) / (kWide * NQ);
+  const uint32_t tiles = (Nc + 15u) / 16u;
+  SmallPlan p;
+  // Fewer than four row tiles per compute unit and K in several passes:
+  // each set takes one pass, so that a workgroup works through more tiles
+  // per pass instead of paying a pass's operand loads and flushes for one.
+  p.S = passes >= 2u && tiles < 4u * cap ? passes : 1u;
+  const uint32_t wgs = std::max(1u, cap / p.S);
+  const uint32_t per_wg = (tiles + wgs - 1u) / wgs;
+  p.G = (tiles + per_wg - 1u) / per_wg;
+  p.tq = tiles / p.G;
+  p.tr = tiles % p.G;
+  return p;
+}
+
+// Rows per launch: with several passes per workgroup its outputs (16 * 16 *
+// MT per tile) must fit the pass accumulator, and with several sets the
+// tiles must fit the counters.
+uint64_t small_chunk_rows(uint32_t N, uint32_t nb, int MT, int NQ, uint32_t cap) {
+  const uint32_t passes = ((nb + 3u) / 4u + kWide * NQ - 1u) / (kWide * NQ);
+  uint64_t rows = N;
+  if (passes > 1u) rows = std::min<uint64_t>(rows, 16ull * (kAccFloats / (256u * MT)) * cap);
+  return std::min<uint64_t>(rows, 16ull * kSplitTiles);
+}
+
+size_t small_workspace(uint32_t N, uint32_t nb, int MT, int NQ, uint32_t cap) {
+  size_t need = 0;
+  const uint64_t chunk = small_chunk_rows(N, nb, MT, NQ, cap);
+  for (uint64_t r0 = 0; r0 < N; r0 += chunk) {
+    const uint32_t Nc = (uint32_t)std::min<uint64_t>(N - r0, chunk);
+    const SmallPlan p = small_plan(Nc, nb, NQ, cap);
+    if (p.S > 1u) need = std::max(need, kCounterBytes + (size_t)p.S * ((Nc + 15u) / 16u) * 256u * (size_t)MT * 4u);
+  }
+  return need;
 }
 
 // Bytes of codes and of scales per 32-element block.
@@ -772,33 +873,19 @@ template <class Fmt> constexpr size_t scale_bytes() {
   return std::is_same<Fmt, GemmTQ4>::value ? 4 : std::is_same<Fmt, GemmNVFP4>::value ? 2 : 1;
 }
 
-__global__ void zero_rows(float* __restrict__ Y, int64_t ldy, uint32_t N) {
-  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-  if (i < N) Y[(size_t)blockIdx.y * ldy + i] = 0.f;
-}
-
 template <class Fmt, int MT, int NQ>
 void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb, const uint8_t* X,
-                  int64_t ldx, uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
+                  int64_t ldx, uint32_t M, float* Y, int64_t ldy, void* ws, hipStream_t s) {
   const uint32_t cap = (uint32_t)device_cu_count();
-  const uint32_t passes = ((nb + 3u) / 4u + kWide * NQ - 1u) / (kWide * NQ);
-  // With several passes a workgroup's outputs (16 * 16 * MT per tile) must
-  // fit the pass accumulator: taller matrices are launched in row chunks.
-  const uint64_t max_tiles = passes > 1 ? (uint64_t)(kAccFloats / (256 * MT)) * cap : ~0ull;
-  for (uint64_t r0 = 0; r0 < N; r0 += 16u * max_tiles) {
-    const uint32_t Nc = (uint32_t)std::min<uint64_t>(N - r0, 16u * max_tiles);
-    const uint32_t tiles = (Nc + 15u) / 16u;
-    // Fewer than four row tiles per compute unit and K in several passes:
-    // split K in two, so that each workgroup works through more tiles per
-    // pass instead of paying a pass's staging and flush for one tile.
-    const uint32_t halves = passes >= 2u && tiles < 4u * cap ? 2u : 1u;
-    const uint32_t wgs = std::max(1u, cap / halves);
-    const uint32_t per_wg = (tiles + wgs - 1u) / wgs;
-    const uint32_t grid = (tiles + per_wg - 1u) / per_wg;
-    if (halves == 2u) hipLaunchKernelGGL(zero_rows, dim3((Nc + 255u) / 256u, M), dim3(256), 0, s, Y + r0, ldy, Nc);
-    hipLaunchKernelGGL((gemm_small_kernel<Fmt, MT, NQ>), dim3(grid * halves), dim3(64 * kWide), 0, s,
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* part = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
+  const uint64_t chunk = small_chunk_rows(N, nb, MT, NQ, cap);
+  for (uint64_t r0 = 0; r0 < N; r0 += chunk) {
+    const uint32_t Nc = (uint32_t)std::min<uint64_t>(N - r0, chunk);
+    const SmallPlan p = small_plan(Nc, nb, NQ, cap);
+    hipLaunchKernelGGL((gemm_small_kernel<Fmt, MT, NQ>), dim3(p.G * p.S), dim3(64 * kWide), 0, s,
                        pk + r0 * nb * code_bytes<Fmt>(), sc + r0 * nb * scale_bytes<Fmt>(), ts, Nc, nb, X, ldx, M,
-                       Y + r0, ldy, grid, tiles / grid, tiles % grid, halves);
+                       Y + r0, ldy, p.G, p.tq, p.tr, p.S, part, counters);
   }
 }
 
@@ -806,10 +893,10 @@ void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_
 // per wavefront and pass), 2 or 4 tiles of 16 activation rows.
 template <class Fmt>
 void launch_small_mt(int mt, const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb,
-                     const uint8_t* X, int64_t ldx, uint32_t M, float* Y, int64_t ldy, hipStream_t s) {
-  if (mt == 1) launch_small<Fmt, 1, 2>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, s);
-  else if (mt == 2) launch_small<Fmt, 2, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, s);
-  else launch_small<Fmt, 4, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, s);
+                     const uint8_t* X, int64_t ldx, uint32_t M, float* Y, int64_t ldy, void* ws, hipStream_t s) {
+  if (mt == 1) launch_small<Fmt, 1, 2>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
+  else if (mt == 2) launch_small<Fmt, 2, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
+  else launch_small<Fmt, 4, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
 }
 
 // Weight groups in flight per wavefront: three where the registers allow.
@@ -841,8 +928,24 @@ void launch_mt(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, con
 
 }  // namespace
 
+// Workspace bytes of the persistent kernel for an [N, K] weight and M bf16
+// activation rows (the largest of its 64-row launches); 0 when no launch
+// splits K or the call runs another kernel.
+size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M, bool xbf16) {
+  if (M <= 4 || !xbf16 || N <= 0 || K <= 0) return 0;
+  const uint32_t nb = (uint32_t)(K / kBlock), cap = (uint32_t)device_cu_count();
+  size_t need = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += 64) {
+    const int64_t mc = (M - m0 < 64) ? M - m0 : 64;
+    const int mt = (int)((mc + 15) / 16);
+    need = std::max(need, mt == 1 ? small_workspace((uint32_t)N, nb, 1, 2, cap)
+                                  : small_workspace((uint32_t)N, nb, mt == 2 ? 2 : 4, 1, cap));
+  }
+  return need;
+}
+
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
-                       const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+                       const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, void* ws, hipStream_t s) {
   // Up to four rows (or float32 activations below 16 rows) the VALU kernel
   // keeps the rows in registers; from five bf16 rows on, one padded 16-row
   // MFMA tile is faster (measured: 8 rows take about twice as long on the
@@ -866,7 +969,7 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
     const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
       launch_small_mt<GemmTQ4>(mt, packed, reinterpret_cast<const uint8_t*>(scales), nullptr, n, nb, Xm, ldx, mm, Ym,
-                               ldy, s);   // the persistent kernel
+                               ldy, ws, s);   // the persistent kernel
     } else {
       if (mt == 1) launch_mt<1, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
       else launch_mt<2, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
@@ -877,7 +980,7 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
 
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y,
-                               int64_t ldy, hipStream_t s) {
+                               int64_t ldy, void* ws, hipStream_t s) {
   // Up to four rows, and float32 activations, on the VALU kernel (rows in
   // registers, any M); from five bf16 rows on, 16-row MFMA tiles with
   // exactly converted bf16 weights.
@@ -890,9 +993,9 @@ hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bsc
     float* Ym = y + m0 * ldy;
     const int mt = (int)((mc + 15) / 16);
     if (fmt == TQ_FMT_NVFP4)
-      launch_small_mt<GemmNVFP4>(mt, codes, bscales, tscale, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, s);
+      launch_small_mt<GemmNVFP4>(mt, codes, bscales, tscale, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, ws, s);
     else
-      launch_small_mt<GemmMXFP6>(mt, codes, bscales, nullptr, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, s);
+      launch_small_mt<GemmMXFP6>(mt, codes, bscales, nullptr, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, ws, s);
   }
   return hipGetLastError();
 }

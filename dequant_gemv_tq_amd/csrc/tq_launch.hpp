@@ -24,7 +24,8 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N,
 hipError_t launch_gemm_valu(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
                             const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
-                       const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+                       const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, void* ws, hipStream_t s);
+size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M, bool xbf16);
 hipError_t launch_blockfp_quantize(int fmt, const void* W, bool bf16, int64_t N, int64_t K,
                                    uint8_t* codes, uint8_t* bscales, float* tscale, void* workspace,
                                    hipStream_t s, bool rsf = false);
@@ -37,7 +38,7 @@ hipError_t launch_q8_gemv(const int8_t* codes, const uint16_t* qscales, int64_t 
                           bool xbf16, float* y, hipStream_t s);
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx,
-                               float* y, int64_t ldy, hipStream_t s);
+                               float* y, int64_t ldy, void* ws, hipStream_t s);
 
 // plain streaming read (tq_measure.hip).
 hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);

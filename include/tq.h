@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -180,18 +180,22 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  * per block cancel down to a single weight.  Callers with such activations
  * who need that bound pass float32 x' in launches of at most 15 rows, which
  * run float32 FMAs.
- * With bf16 activations, M >= 5, fewer than four 16-row tiles of N per
- * compute unit and K longer than one pass of the kernel (4096 elements for
- * launches of up to 16 rows, 2048 for 17-64; M is launched 64 rows at a
- * time), the call zeroes y's
- * M x N elements in a kernel of its own and two sets of workgroups then add
- * the sums of the two halves of K into them: y must not overlap x, and the
- * result is still the same on every run (two addends onto zero).
- * Limits: M <= 256, K <= 131072.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN,
- * TQ_EDTYPE. */
+ * Workspace (bf16 activations, M >= 5): the MFMA kernel splits K into
+ * several ranges when K is long (more than 4096 elements for launches of up
+ * to 16 rows, 2048 for 17-64; M is launched 64 rows at a time) or when N
+ * has few 16-row tiles per compute unit.  Each range's sums then go to the
+ * workspace, and the last workgroup to finish a tile adds the ranges in
+ * their fixed order, so y is the same on every run.  `workspace` is device
+ * memory of at least tq_workspace_bytes(TQ_OP_GEMM, N, K, M) bytes,
+ * 256-byte aligned, zero-filled before the first call that uses it; every
+ * call leaves it fit for the next one.  Calls that share a workspace must
+ * not run at the same time (one stream, or ordered streams).  When that
+ * size is 0 the workspace may be NULL.
+ * Limits: M <= 256, K <= 131072.  Errors: TQ_EINVAL (also: a workspace
+ * missing or smaller than needed), TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
                   const void* x_rot, tq_dtype xt, int64_t ldx, float* y, int64_t ldy,
-                  hipStream_t stream);
+                  void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes of NVFP4 quantization: the amax pass leaves one partial
  * maximum per workgroup (at most 1024) for the encode pass. */
@@ -203,10 +207,10 @@ typedef enum tq_op {
   TQ_OP_DEQUANTIZE = 2,        /* none                                          */
   TQ_OP_ROTATE = 3,            /* none                                          */
   TQ_OP_GEMV = 4,              /* none                                          */
-  TQ_OP_GEMM = 5,              /* none (split K writes into y itself)           */
+  TQ_OP_GEMM = 5,              /* split-K sums and per-tile counters            */
   TQ_OP_NVFP4_QUANTIZE = 6,    /* tq_blockfp_quantize(_rsf) with TQ_FMT_NVFP4   */
   TQ_OP_MXFP6_QUANTIZE = 7,    /* tq_blockfp_quantize(_rsf) with TQ_FMT_MXFP6: none */
-  TQ_OP_BLOCKFP_GEMM = 8,      /* none                                          */
+  TQ_OP_BLOCKFP_GEMM = 8,      /* as TQ_OP_GEMM                                 */
   TQ_OP_TRANSCODE_Q8 = 9,      /* none                                          */
   TQ_OP_Q8_GEMV = 10,          /* none                                          */
   TQ_OP_ATTN_DECODE = 11       /* N = B, K = Hq, M = T_max: as tq_attn_workspace_bytes */
@@ -270,17 +274,20 @@ tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64
  *   M >= 5 with bf16 X: bf16 MFMA in 16-row tiles (up to 64 rows per
  *     launch), every weight converted once to an exact bf16 operand
  *     (e2m1 * e4m3 for NVFP4, the tensor scale applied to the finished sums;
- *     e3m2 * 2^(e8m0 - 127) for MXFP6), float32 accumulation.  Few row
- *     tiles and K in several passes: Y zeroed first and K split in two, as
- *     for tq_gemm (Y must not overlap X; the result does not vary by run).
+ *     e3m2 * 2^(e8m0 - 127) for MXFP6), float32 accumulation.  Long K or
+ *     few row tiles: K split into ranges through the workspace, with the
+ *     contract of tq_gemm's (tq_workspace_bytes(TQ_OP_BLOCKFP_GEMM, N, K,
+ *     M) bytes, 256-byte aligned, zero-filled before first use; the result
+ *     does not vary by run).
  * X [M, K] row stride ldx, TQ_F32 or TQ_BF16, 16-byte aligned; Y [M, N]
  * float32, row stride ldy.  K % 32 == 0, K <= 32768, M <= 4096; NVFP4 codes
  * 16-byte aligned (MXFP6 codes 8-byte), NVFP4 block_scales 2-byte aligned.
- * Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
+ * Errors: TQ_EINVAL (also: a workspace missing or smaller than needed),
+ * TQ_ESHAPE, TQ_EALIGN, TQ_EDTYPE. */
 tq_status tq_blockfp_gemm(tq_format f, const uint8_t* codes, const uint8_t* block_scales,
                           const float* tensor_scale, int64_t N, int64_t K, int64_t M,
                           const void* x, tq_dtype xt, int64_t ldx, float* y, int64_t ldy,
-                          hipStream_t stream);
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Load-time transcode of TQ4_1S weights to int8 blocks (TQ4 page, the note
  * under the decode-speed summary and the backend item of "适用前提与边界":

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = tqa.lib()
-    assert L.tq_abi_version() == 2
+    assert L.tq_abi_version() == 3
     for s in range(6):
         assert L.tq_status_str(s)
     assert b"unknown" in L.tq_status_str(99)
@@ -96,11 +96,18 @@ def test_other_calls_reject_before_launch():
     assert L.tq_gemv(g, g, 8, 64, 0, _p(GOOD + 4), F32, 1, g, None) == EALIGN
     assert L.tq_gemv(g, g, 8, 64, 0, g, F32, 1, _p(GOOD + 2), None) == EALIGN
     # gemm
-    assert L.tq_gemm(g, g, 8, 64, 0, g, BF16, 64, g, 8, None) == EINVAL
-    assert L.tq_gemm(g, g, 8, 64, 257, g, BF16, 64, g, 8, None) == ESHAPE
-    assert L.tq_gemm(g, g, 8, 64, 16, g, F16, 64, g, 8, None) == EDTYPE
-    assert L.tq_gemm(g, g, 8, 64, 4, g, BF16, 60, g, 8, None) == EINVAL     # ldx < K
-    assert L.tq_gemm(g, g, 8, 64, 4, g, BF16, 64, g, 4, None) == EINVAL     # ldy < N
+    assert L.tq_gemm(g, g, 8, 64, 0, g, BF16, 64, g, 8, None, 0, None) == EINVAL
+    assert L.tq_gemm(g, g, 8, 64, 257, g, BF16, 64, g, 8, None, 0, None) == ESHAPE
+    assert L.tq_gemm(g, g, 8, 64, 16, g, F16, 64, g, 8, None, 0, None) == EDTYPE
+    assert L.tq_gemm(g, g, 8, 64, 4, g, BF16, 60, g, 8, None, 0, None) == EINVAL     # ldx < K
+    assert L.tq_gemm(g, g, 8, 64, 4, g, BF16, 64, g, 4, None, 0, None) == EINVAL     # ldy < N
+    # a launch that splits K needs its workspace: missing, short or misaligned is rejected
+    need = L.tq_workspace_bytes(5, 4096, 14336, 16)
+    assert need > 0
+    assert L.tq_gemm(g, g, 4096, 14336, 16, g, BF16, 14336, g, 4096, None, 0, None) == EINVAL
+    assert L.tq_gemm(g, g, 4096, 14336, 16, g, BF16, 14336, g, 4096, g, need - 4, None) == EINVAL
+    assert L.tq_gemm(g, g, 4096, 14336, 16, g, BF16, 14336, g, 4096, _p(GOOD + 16), need, None) == EALIGN
+    assert L.tq_blockfp_gemm(1, g, g, g, 4096, 14336, 16, g, BF16, 14336, g, 4096, None, 0, None) == EINVAL
     # rotate / dequantize
     assert L.tq_rotate(g, F32, 2, 40, 40, 0, g, F32, 40, None) == ESHAPE
     assert L.tq_rotate(g, F16, 2, 64, 64, 0, g, F32, 64, None) == EDTYPE
@@ -116,11 +123,15 @@ def test_other_calls_reject_before_launch():
     assert L.tq_blockfp_quantize(1, g, F32, 2, 40, g, g, g, g, W4, None) == ESHAPE
     assert L.tq_blockfp_quantize(2, g, F32, 2, 48, g, g, None, None, 0, None) == ESHAPE   # MXFP6 needs K % 32
     assert L.tq_blockfp_quantize(2, g, F16, 2, 64, g, g, None, None, 0, None) == EDTYPE
-    # workspace sizes: only NVFP4 quantization and decode attention take one
+    # workspace sizes: NVFP4 quantization, the split-K GEMMs and decode attention take one
     smax = ctypes.c_size_t(-1).value
     assert L.tq_workspace_bytes(6, 17408, 5120, 0) == W4
-    for op in (1, 2, 3, 4, 5, 7, 8, 9, 10):
+    for op in (1, 2, 3, 4, 7, 9, 10):
         assert L.tq_workspace_bytes(op, 4096, 4096, 16) == 0
+    for op in (5, 8):
+        assert L.tq_workspace_bytes(op, 4096, 4096, 4) == 0                   # M <= 4: the VALU kernel
+        assert L.tq_workspace_bytes(op, 4096, 14336, 64) > 0                  # K in several ranges
+        assert L.tq_workspace_bytes(op, 4096, 14336, 0) == smax
     assert L.tq_workspace_bytes(11, 2, 32, 1000) == L.tq_attn_workspace_bytes(2, 32, 1000)
     assert L.tq_workspace_bytes(11, 0, 32, 1000) == smax
     assert L.tq_workspace_bytes(99, 1, 1, 1) == smax
@@ -140,12 +151,12 @@ def test_other_calls_reject_before_launch():
         assert fn(2, g, F16, 2, 64, g, g, None, None, 0, None) == EDTYPE
         assert fn(2, _p(GOOD + 4), F32, 2, 64, g, g, None, None, 0, None) == EALIGN     # W: 16 B
         assert fn(1, g, F32, 2, 64, _p(GOOD + 4), g, g, g, W4, None) == EALIGN        # codes: 8 B
-    assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 4097, g, F32, 64, g, 8, None) == ESHAPE   # M <= 4096
-    assert L.tq_blockfp_gemm(1, g, g, g, 8, 32800, 1, g, F32, 32800, g, 8, None) == ESHAPE  # K <= 32768
-    assert L.tq_blockfp_gemm(2, g, g, None, 8, 48, 1, g, F32, 64, g, 8, None) == ESHAPE     # K % 32
-    assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None) == EDTYPE
-    assert L.tq_blockfp_gemm(1, _p(GOOD + 8), g, g, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN   # NVFP4 codes: 16 B
-    assert L.tq_blockfp_gemm(2, _p(GOOD + 4), g, None, 8, 64, 1, g, F32, 64, g, 8, None) == EALIGN  # MXFP6 codes: 8 B
+    assert L.tq_blockfp_gemm(1, g, g, g, 8, 64, 4097, g, F32, 64, g, 8, None, 0, None) == ESHAPE   # M <= 4096
+    assert L.tq_blockfp_gemm(1, g, g, g, 8, 32800, 1, g, F32, 32800, g, 8, None, 0, None) == ESHAPE  # K <= 32768
+    assert L.tq_blockfp_gemm(2, g, g, None, 8, 48, 1, g, F32, 64, g, 8, None, 0, None) == ESHAPE     # K % 32
+    assert L.tq_blockfp_gemm(2, g, g, None, 8, 64, 1, g, F16, 64, g, 8, None, 0, None) == EDTYPE
+    assert L.tq_blockfp_gemm(1, _p(GOOD + 8), g, g, 8, 64, 1, g, F32, 64, g, 8, None, 0, None) == EALIGN   # NVFP4 codes: 16 B
+    assert L.tq_blockfp_gemm(2, _p(GOOD + 4), g, None, 8, 64, 1, g, F32, 64, g, 8, None, 0, None) == EALIGN  # MXFP6 codes: 8 B
     # int8 transcode and GEMV
     assert L.tq_transcode_q8(g, g, 8, 64, 0, None, g, None) == EINVAL
     assert L.tq_transcode_q8(g, g, 8, 48, 0, g, g, None) == ESHAPE

@@ -294,3 +294,22 @@ def test_gemm_one_hot_rows_rotated_domain_bound(k, xdtype):
     assert not bad.any(), (f"{bad.sum()} outside the rotated-domain bound; worst ratio "
                            f"{float((err / np.maximum(rot, 1e-300)).max())!r}")
     assert np.all(rot >= a * (1 - 1e-12))                  # the rotated sum dominates the original one
+
+
+@pytest.mark.gpu
+def test_gemm_workspace_reused_across_shapes():
+    """One workspace serves split-K calls of different shapes in turn: a call with few row tiles writes its
+    partial sums where a later, taller call keeps per-tile counters only if the layout let them overlap, so
+    the taller call must still be exact (and the shorter one after it)."""
+    m = 16
+    ws = torch.zeros(tqa.workspace_bytes("gemm", 8192, 14336, 64), dtype=torch.uint8, device=DEV)
+    for n, k in ((517, 4096), (4100, 4096), (300, 8192), (8192, 14336), (517, 4096)):
+        g = workloads.generator(n + k, DEV)
+        W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+        X = workloads.activation(m, k, g, DEV, torch.bfloat16)
+        packed, scales = tqa.quantize(W)
+        say(f"[gemm] shared workspace M={m} {n}x{k}")
+        Y = tqa.gemm(packed, scales, tqa.rotate(X, dtype=torch.bfloat16), workspace=ws)
+        rows = np.unique(np.linspace(0, n - 1, 256).astype(int))
+        yr, a = otq.gemm_o64(packed.cpu().numpy()[rows], u16(scales)[rows], X.float().cpu().numpy())
+        assert_within(f32np(Y)[:, rows], yr, a, what=f"gemm shared workspace {n}x{k}")
