@@ -480,7 +480,7 @@ def bench_gemm(torch, tqa, wl, model, groups, dev, stream, no_graph):
         flops = sum(L * 2.0 * m * n * k for n, k in groups.values())
         res[f"M{m}"] = {"ms_32_layers": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1),
                         "TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 2),
-                        "path": "VALU fp32" if m <= 4 else "MFMA bf16"}
+                        "path": "VALU fp32" if m <= 2 else "MFMA bf16"}
     return res
 
 

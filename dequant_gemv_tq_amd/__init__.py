@@ -266,7 +266,7 @@ def _gemm_workspace(op: str, N: int, K: int, M: int, xbf16: bool, device, worksp
     The library's contract: zero-filled before its first use, left fit for the next call by every
     call, and never used by two calls at once -- hence one buffer per stream.
     """
-    need = workspace_bytes(op, N, K, M) if (xbf16 and M > 4) else 0
+    need = workspace_bytes(op, N, K, M) if xbf16 else 0
     if workspace is not None:
         _need(isinstance(workspace, torch.Tensor) and workspace.dtype == torch.uint8 and workspace.is_contiguous()
               and workspace.numel() >= need, f"workspace must be a contiguous uint8 buffer of at least {need} bytes")

@@ -874,7 +874,7 @@ template <class Fmt> constexpr size_t scale_bytes() {
 }
 
 template <class Fmt, int MT, int NQ>
-void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb, const uint8_t* X,
+hipError_t launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb, const uint8_t* X,
                   int64_t ldx, uint32_t M, float* Y, int64_t ldy, void* ws, hipStream_t s) {
   const uint32_t cap = (uint32_t)device_cu_count();
   uint32_t* counters = static_cast<uint32_t*>(ws);
@@ -883,20 +883,23 @@ void launch_small(const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_
   for (uint64_t r0 = 0; r0 < N; r0 += chunk) {
     const uint32_t Nc = (uint32_t)std::min<uint64_t>(N - r0, chunk);
     const SmallPlan p = small_plan(Nc, nb, NQ, cap);
+    if (p.S > 1u && !ws) return hipErrorInvalidValue;   // the entry points size and check it; never reached
     hipLaunchKernelGGL((gemm_small_kernel<Fmt, MT, NQ>), dim3(p.G * p.S), dim3(64 * kWide), 0, s,
                        pk + r0 * nb * code_bytes<Fmt>(), sc + r0 * nb * scale_bytes<Fmt>(), ts, Nc, nb, X, ldx, M,
                        Y + r0, ldy, p.G, p.tq, p.tr, p.S, part, counters);
   }
+  return hipSuccess;
 }
 
 // The persistent kernel for one chunk of up to 64 rows: MT = 1 (two groups
 // per wavefront and pass), 2 or 4 tiles of 16 activation rows.
 template <class Fmt>
-void launch_small_mt(int mt, const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb,
-                     const uint8_t* X, int64_t ldx, uint32_t M, float* Y, int64_t ldy, void* ws, hipStream_t s) {
-  if (mt == 1) launch_small<Fmt, 1, 2>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
-  else if (mt == 2) launch_small<Fmt, 2, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
-  else launch_small<Fmt, 4, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
+hipError_t launch_small_mt(int mt, const uint8_t* pk, const uint8_t* sc, const float* ts, uint32_t N, uint32_t nb,
+                           const uint8_t* X, int64_t ldx, uint32_t M, float* Y, int64_t ldy, void* ws,
+                           hipStream_t s) {
+  if (mt == 1) return launch_small<Fmt, 1, 2>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
+  if (mt == 2) return launch_small<Fmt, 2, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
+  return launch_small<Fmt, 4, 1>(pk, sc, ts, N, nb, X, ldx, M, Y, ldy, ws, s);
 }
 
 // Weight groups in flight per wavefront: three where the registers allow.
@@ -928,11 +931,19 @@ void launch_mt(const uint4* pk, const uint32_t* sc, uint32_t N, uint32_t nb, con
 
 }  // namespace
 
+// Activation rows up to which the GEMMs run the VALU kernel (float32 FMAs);
+// larger bf16 batches take the MFMA kernel, whose split-K launches need the
+// workspace.  The dispatch and the workspace size both read this.  Measured
+// over a Llama-3-8B layer: 2 rows 45 us on the VALU kernel against 56 us
+// for one padded 16-row MFMA tile; 3 rows 81 against 56 us, 4 rows 72
+// against 57 us.
+constexpr int kValuRows = 2;
+
 // Workspace bytes of the persistent kernel for an [N, K] weight and M bf16
 // activation rows (the largest of its 64-row launches); 0 when no launch
 // splits K or the call runs another kernel.
 size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M, bool xbf16) {
-  if (M <= 4 || !xbf16 || N <= 0 || K <= 0) return 0;
+  if (M <= kValuRows || !xbf16 || N <= 0 || K <= 0) return 0;
   const uint32_t nb = (uint32_t)(K / kBlock), cap = (uint32_t)device_cu_count();
   size_t need = 0;
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
@@ -946,11 +957,10 @@ size_t gemm_workspace_bytes(int64_t N, int64_t K, int64_t M, bool xbf16) {
 
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N, int64_t K, int64_t M,
                        const void* xr, bool xbf16, int64_t ldx, float* y, int64_t ldy, void* ws, hipStream_t s) {
-  // Up to four rows (or float32 activations below 16 rows) the VALU kernel
-  // keeps the rows in registers; from five bf16 rows on, one padded 16-row
-  // MFMA tile is faster (measured: 8 rows take about twice as long on the
-  // VALU kernel as 16 on the MFMA one).
-  if (M <= 4 || (M < 16 && !xbf16)) return launch_gemm_valu(packed, scales, N, K, M, xr, xbf16, ldx, y, ldy, s);
+  // Up to two rows (or float32 activations below 16 rows) the VALU kernel
+  // keeps the rows in registers; from three bf16 rows on, one padded 16-row
+  // MFMA tile is faster (kValuRows).
+  if (M <= kValuRows || (M < 16 && !xbf16)) return launch_gemm_valu(packed, scales, N, K, M, xr, xbf16, ldx, y, ldy, s);
   const uint32_t nb = (uint32_t)(K / kBlock);
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(scales);
@@ -968,8 +978,9 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
     const int mt = (int)((mc + 15) / 16);
     const uint32_t n = (uint32_t)N, mm = (uint32_t)mc;
     if (xbf16) {
-      launch_small_mt<GemmTQ4>(mt, packed, reinterpret_cast<const uint8_t*>(scales), nullptr, n, nb, Xm, ldx, mm, Ym,
-                               ldy, ws, s);   // the persistent kernel
+      const hipError_t e = launch_small_mt<GemmTQ4>(mt, packed, reinterpret_cast<const uint8_t*>(scales), nullptr, n,
+                                                    nb, Xm, ldx, mm, Ym, ldy, ws, s);   // the persistent kernel
+      if (e != hipSuccess) return e;
     } else {
       if (mt == 1) launch_mt<1, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
       else launch_mt<2, true>(pk, sc, n, nb, Xm, ldx, mm, Ym, ldy, s);
@@ -981,10 +992,10 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int64_t N,
 hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bscales, const float* tscale,
                                int64_t N, int64_t K, int64_t M, const void* x, bool xbf16, int64_t ldx, float* y,
                                int64_t ldy, void* ws, hipStream_t s) {
-  // Up to four rows, and float32 activations, on the VALU kernel (rows in
-  // registers, any M); from five bf16 rows on, 16-row MFMA tiles with
+  // Up to two rows, and float32 activations, on the VALU kernel (rows in
+  // registers, any M); from three bf16 rows on, 16-row MFMA tiles with
   // exactly converted bf16 weights.
-  if (M <= 4 || !xbf16) return launch_blockfp_gemv(fmt, codes, bscales, tscale, N, K, M, x, xbf16, ldx, y, ldy, s);
+  if (M <= kValuRows || !xbf16) return launch_blockfp_gemv(fmt, codes, bscales, tscale, N, K, M, x, xbf16, ldx, y, ldy, s);
   const uint32_t nb = (uint32_t)(K / kBlock);
   const uint8_t* X = static_cast<const uint8_t*>(x);
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
@@ -992,10 +1003,13 @@ hipError_t launch_blockfp_gemm(int fmt, const uint8_t* codes, const uint8_t* bsc
     const uint8_t* Xm = X + m0 * ldx * 2;
     float* Ym = y + m0 * ldy;
     const int mt = (int)((mc + 15) / 16);
-    if (fmt == TQ_FMT_NVFP4)
-      launch_small_mt<GemmNVFP4>(mt, codes, bscales, tscale, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, ws, s);
-    else
-      launch_small_mt<GemmMXFP6>(mt, codes, bscales, nullptr, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy, ws, s);
+    const hipError_t e =
+        fmt == TQ_FMT_NVFP4
+            ? launch_small_mt<GemmNVFP4>(mt, codes, bscales, tscale, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy,
+                                         ws, s)
+            : launch_small_mt<GemmMXFP6>(mt, codes, bscales, nullptr, (uint32_t)N, nb, Xm, ldx, (uint32_t)mc, Ym, ldy,
+                                         ws, s);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -394,7 +394,7 @@ def stats(csv_path: str) -> None:
               f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 1, 1, 1>`; down "
               "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 4>`.  "
               "Other kernels: the quantizer (`quantize_kernel<bf16, rsf>`, the second flag for the RSF-lite "
-              "scale search), the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M <= 4, and float32 "
+              "scale search), the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M <= 2, and float32 "
               "activations below 16 rows; above, the persistent MFMA `gemm_small_kernel<format, MT, NQ>` with bf16 "
               "activations, MT = 1, 2, 4 "
               "tiles of 16 activation rows, and `gemm_mfma_kernel` with float32 activations), dequantization, "

@@ -164,7 +164,7 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  *   x_rot   [M, K] pre-rotated activations (tq_rotate), row stride ldx,
  *           TQ_BF16 or TQ_F32, 16-byte aligned.
  *   y       [M, N] float32, row stride ldy (output).
- * M <= 4 (and float32 activations with M < 16) run a VALU kernel with
+ * M <= 2 (and float32 activations with M < 16) run a VALU kernel with
  * float32 FMAs.  Larger M runs bf16 MFMA in 16-row tiles with float32
  * accumulation, dequantizing each weight once: one pass for bf16
  * activations, three hi/lo-split passes for float32 activations.
@@ -180,7 +180,7 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
  * per block cancel down to a single weight.  Callers with such activations
  * who need that bound pass float32 x' in launches of at most 15 rows, which
  * run float32 FMAs.
- * Workspace (bf16 activations, M >= 5): the MFMA kernel splits K into
+ * Workspace (bf16 activations, M >= 3): the MFMA kernel splits K into
  * several ranges when K is long (more than 4096 elements for launches of up
  * to 16 rows, 2048 for 17-64; M is launched 64 rows at a time) or when N
  * has few 16-row tiles per compute unit.  Each range's sums then go to the
@@ -266,12 +266,12 @@ tq_status tq_blockfp_quantize_rsf(tq_format f, const void* W, tq_dtype wt, int64
 /* Y[m, n] = sum_k W_deq[n, k] X[m, k] for a block-float weight (fused
  * decode, float32 accumulation; the activation is used as given, there is
  * no rotation).  Codes are decoded by gfx950's scaled-convert instructions.
- *   M <= 4, or float32 X (any M): VALU kernel.  E2M1 two at a time, E3M2 a
+ *   M <= 2, or float32 X (any M): VALU kernel.  E2M1 two at a time, E3M2 a
  *     whole 32-element block at a time, scale 1, exact; each 16- (NVFP4) or
  *     32-element (MXFP6) partial sum is multiplied once by its scale:
  *     float32(e4m3 * tensor_scale) for NVFP4, 2^(e8m0 - 127) (ldexp,
  *     exact) for MXFP6.
- *   M >= 5 with bf16 X: bf16 MFMA in 16-row tiles (up to 64 rows per
+ *   M >= 3 with bf16 X: bf16 MFMA in 16-row tiles (up to 64 rows per
  *     launch), every weight converted once to an exact bf16 operand
  *     (e2m1 * e4m3 for NVFP4, the tensor scale applied to the finished sums;
  *     e3m2 * 2^(e8m0 - 127) for MXFP6), float32 accumulation.  Long K or

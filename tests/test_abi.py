@@ -129,7 +129,7 @@ def test_other_calls_reject_before_launch():
     for op in (1, 2, 3, 4, 7, 9, 10):
         assert L.tq_workspace_bytes(op, 4096, 4096, 16) == 0
     for op in (5, 8):
-        assert L.tq_workspace_bytes(op, 4096, 4096, 4) == 0                   # M <= 4: the VALU kernel
+        assert L.tq_workspace_bytes(op, 4096, 14336, 2) == 0                  # M <= 2: the VALU kernel
         assert L.tq_workspace_bytes(op, 4096, 14336, 64) > 0                  # K in several ranges
         assert L.tq_workspace_bytes(op, 4096, 14336, 0) == smax
     assert L.tq_workspace_bytes(11, 2, 32, 1000) == L.tq_attn_workspace_bytes(2, 32, 1000)
