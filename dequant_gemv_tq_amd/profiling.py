@@ -392,7 +392,7 @@ def stats(csv_path: str) -> None:
     lines += ["", "Decode GEMV instantiations `gemv_kernel<format, J, R, MC, mode, threads, depth, early, stage>`: "
               "q|k|v and gate|up (K = 4096, bf16 activation, rotation fused, one row per wavefront) run "
               f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 1, 1, 1>`; down "
-              "(K = 14336) stages its activation in four passes, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 4>`.  "
+              "(K = 14336, two row slots per workgroup) rotates its activation per lane, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 0>`.  "
               "Other kernels: the quantizer (`quantize_kernel<bf16, rsf>`, the second flag for the RSF-lite "
               "scale search), the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M <= 2, and float32 "
               "activations below 16 rows; above, the persistent MFMA `gemm_small_kernel<format, MT, NQ>` with bf16 "
