@@ -400,7 +400,7 @@ def stats(csv_path: str) -> None:
               "tiles of 16 activation rows, and `gemm_mfma_kernel` with float32 activations), dequantization, "
               "the NVFP4 / MXFP6 rows (`gemv_kernel<FmtNVFP4, ...>`, `gemv_kernel<FmtMXFP6, ...>` up to four "
               "activation rows, `gemm_small_kernel<GemmNVFP4, ...>`, `gemm_small_kernel<GemmMXFP6, ...>` from "
-              "five) and the "
+              "three) and the "
               "load-time int8 rows (`q8_transcode_kernel`, `q8_gemv_kernel<bf16 activation, passes>`), the turbo4 KV "
               "cache (`q8_rows_kernel` keys, `turbo4_encode_kernel` values, `attn_split_kernel<G, bf16 q>` + "
               "`attn_combine_kernel` for decode attention), `stream_read_kernel` (the read envelope); the "
