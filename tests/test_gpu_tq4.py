@@ -313,3 +313,6 @@ def test_gemm_workspace_reused_across_shapes():
         rows = np.unique(np.linspace(0, n - 1, 256).astype(int))
         yr, a = otq.gemm_o64(packed.cpu().numpy()[rows], u16(scales)[rows], X.float().cpu().numpy())
         assert_within(f32np(Y)[:, rows], yr, a, what=f"gemm shared workspace {n}x{k}")
+        # every call leaves the per-tile counters (the first 64 KiB) at zero for the next one
+        torch.cuda.synchronize()
+        assert int(ws[:65536].view(torch.int32).count_nonzero()) == 0
