@@ -376,19 +376,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(const uint4* __r
 //                     8 g .. 8 g + 7 (the raw dwords are transposed across
 //                     the lane groups first);
 //   kByBlock = false: step s covers elements 8 s .. 8 s + 7 of every lane
-//                     group's own block (no transpose; the activation
-//                     operands are read from LDS in the same order).
-// kLoads is the number of vector loads a group's weights take (the exact
-// wait in the prologue counts them); kLut says whether the pair table is
-// needed; kTensorScale whether the finished sums are multiplied by a
-// float32 tensor scale.
+//                     group's own block (no transpose of the weights; the
+//                     activation operands are transposed across the lane
+//                     groups instead).
+// kLut says whether the pair table is needed; kTensorScale whether the
+// finished sums are multiplied by a float32 tensor scale.
 // ---------------------------------------------------------------------------
 
 // TQ4_1S: 16 bytes of nibbles and the fp16 scale pair per block; each weight
 // is the fp16 centroid pair lookup times its fp16 scale, rounded to bf16.
 struct GemmTQ4 {
   static constexpr bool kLut = true, kByBlock = true, kTensorScale = false;
-  static constexpr int kLoads = 2;
   struct Raw {
     uint4 p;
     uint32_t sc;
@@ -432,7 +430,6 @@ struct GemmTQ4 {
 // is exact.  The tensor scale multiplies the finished sums.
 struct GemmNVFP4 {
   static constexpr bool kLut = false, kByBlock = false, kTensorScale = true;
-  static constexpr int kLoads = 2;
   struct Raw {
     uint4 p;
     uint32_t sc;
@@ -460,7 +457,6 @@ struct GemmNVFP4 {
 // scale is a power of two, which the conversion applies exactly.
 struct GemmMXFP6 {
   static constexpr bool kLut = false, kByBlock = false, kTensorScale = false;
-  static constexpr int kLoads = 3;          // 16 + 8 bytes of codes, the scale byte
   struct Raw {
     uint4 a;
     uint2 b;
@@ -545,7 +541,6 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nl = lane & 15;
   const uint32_t g = (uint32_t)(lane >> 4);
   const uint32_t laneoff = (uint32_t)lane * 4u;          // this lane's copy in the fp16 pair table
   const uint32_t ngroups = (nb + 3u) / 4u;
@@ -590,11 +585,10 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     __builtin_memcpy(&out, wd, sizeof(wd));
     return out;
   };
-  // The scheduling barriers keep each register set's loads together, and a
-  // workgroup barrier separates the two sets before the tile loop (the
-  // compiler interleaved them otherwise), so every path into the loop
-  // carries the same load order and the wait for a set never covers the set
-  // loaded after it.
+  // The scheduling barriers keep each register set's loads together (the
+  // compiler interleaved the two sets otherwise), so every path into the
+  // loop carries the same load order and the wait for a set never covers
+  // the set loaded after it.
   auto load_w = [&](WSet& w, uint32_t tile, uint32_t pass) {
     const uint32_t row = min(tile * 16u + lrow, N - 1u);
     __builtin_amdgcn_sched_barrier(0);
