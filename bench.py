@@ -383,10 +383,10 @@ def main():
                             "read_envelope_GB_s": round(nbytes / (rms * 1e-3) / 1e9, 1),
                             "gemv_over_read": round(ms / rms, 3)}
     torch.cuda.empty_cache()
-    # Roofline of the dominant kernel: the instantiation that serves q|k|v and
-    # gate|up (K = 4096, one row per wavefront; 64 of the 128 launches of a
-    # step and 57% of its bytes).  o (one two-row tile per workgroup) and down
-    # (K = 14336, activation staged in four passes) are other instantiations.
+    # Roofline of the dominant kernel: the instantiation that serves q|k|v, o
+    # and gate|up (K = 4096, one row per wavefront; 96 of the 128 launches of
+    # a step and 73% of its bytes).  down (K = 14336, activation rotated per
+    # lane) is another instantiation.
     dom = list(tq_profiling.DOMINANT)
     dom_bytes = sum(gemv_bytes(groups[g][0], groups[g][1], xb) for g in dom)
     dom_ms = sum(group_ms[g] for g in dom)

@@ -728,16 +728,16 @@ void launch_cfg(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const ui
 
 // Decode GEMV shape, measured on MI355X over the Llama-3-8B and 70B decode
 // layers: x' staged in LDS (when a workgroup holds more than two row slots),
-// the fewest K-blocks per lane that fit a row into
-// a 1024-thread workgroup, and one row per wavefront per tile with two
-// register sets of tile loads, only the first requested before the
-// activation has arrived -- except when a single round of two-row tiles
-// already covers the matrix (one tile per workgroup, nothing to pipeline),
-// where two rows per wavefront and one register set are used.  Graph-timed
+// the fewest K-blocks per lane that fit a row into a 1024-thread workgroup,
+// and one row per wavefront per tile with two register sets of tile loads,
+// only the first requested before the activation has arrived.  Graph-timed
 // 32-layer Llama-3-8B step on two boxes: 1.215 / 1.206 ms with both sets
 // requested at the start, 1.164 / 1.147 ms with one; four sets (one early)
 // measured 1.317 / 1.140 ms -- deeper queues help on some boxes and cost 8%
-// on others, so two are kept.
+// on others, so two are kept.  Matrices that one round of two-row tiles
+// covers (Llama-3-8B o: one tile per workgroup) used to take two rows per
+// wavefront and one register set; two one-row tiles, the first computed
+// while the second arrives, run o in 5.17-5.23 instead of 5.58-5.62 us.
 constexpr bool kGemvStage = true;
 constexpr int kGemvMinJ = 1;
 
@@ -772,10 +772,7 @@ template <typename Fmt, int J>
 void launch_gemv_j(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, const uint8_t* x, int mode, float* y,
                    hipStream_t s) {
   const Plan pl = plan_for(nb, 1024, J);
-  const uint32_t slots = (uint32_t)(pl.threads / pl.TK);
-  const uint32_t tiles2 = (N + 2u * slots - 1u) / (2u * slots);
-  if (tiles2 <= grid_cap(pl.threads)) launch_gemv_jr<Fmt, J, 2>(fmt, N, nb, mask, x, mode, y, pl, s);
-  else launch_gemv_jr<Fmt, J, 1>(fmt, N, nb, mask, x, mode, y, pl, s);
+  launch_gemv_jr<Fmt, J, 1>(fmt, N, nb, mask, x, mode, y, pl, s);
 }
 
 template <typename Fmt>

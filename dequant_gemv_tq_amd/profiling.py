@@ -46,7 +46,7 @@ GROUPS = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "dow
 MEMBERS = {"qkv": ["q", "k", "v"], "o": ["o"], "gate_up": ["gate", "up"], "down": ["down"]}
 COPIES = 8
 COPY_BYTES = 1 << 30
-DOMINANT = ("qkv", "gate_up")               # groups served by the dominant instantiation
+DOMINANT = ("qkv", "o", "gate_up")          # groups served by the dominant instantiation
 DOMINANT_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 1>"   # K = 4096, one row per wavefront
 SOURCES = ("csrc/tq_gemv.hip", "csrc/tq_internal.hpp")
 
@@ -256,7 +256,7 @@ def summarize(fetch_db: str, write_db: str) -> None:
            "algorithmic_bytes_per_launch": round(dom_a / len(DOMINANT)),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "source_sha256": source_hash()}
-    lines += ["", "Per launch of the dominant instantiation (mean over q|k|v and gate|up):", "",
+    lines += ["", "Per launch of the dominant instantiation (mean over q|k|v, o and gate|up):", "",
               f"traffic-json: {json.dumps(rec)}", ""]
     print("\n".join(lines))
 
@@ -390,8 +390,8 @@ def stats(csv_path: str) -> None:
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.2f}% |")
     lines += ["", "Decode GEMV instantiations `gemv_kernel<format, J, R, MC, mode, threads, depth, early, stage>`: "
-              "q|k|v and gate|up (K = 4096, bf16 activation, rotation fused, one row per wavefront) run "
-              f"`{DOMINANT_KERNEL}`; o runs the two-row `gemv_kernel<FmtTQ4, 1, 2, 1, 3, 1024, 1, 1, 1>`; down "
+              "q|k|v, o and gate|up (K = 4096, bf16 activation, rotation fused, one row per wavefront) run "
+              f"`{DOMINANT_KERNEL}`; down "
               "(K = 14336, two row slots per workgroup) rotates its activation per lane, `gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 0>`.  "
               "Other kernels: the quantizer (`quantize_kernel<bf16, rsf>`, the second flag for the RSF-lite "
               "scale search), the small-batch GEMM (VALU `gemv_kernel<..., MC, ...>` for M <= 2, and float32 "
