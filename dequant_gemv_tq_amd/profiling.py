@@ -19,6 +19,11 @@ Kernel durations of a benchmark run:
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- \\
         python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
     python3 -m dequant_gemv_tq_amd.profiling stats OUT/trace/bench_kernel_stats.csv > profiles/...md
+    python3 -m dequant_gemv_tq_amd.profiling groups OUT/trace/bench_kernel_trace.csv > profiles/...md
+
+``groups`` takes the same run's kernel trace: the duration of every GEMV of the
+graph-replayed decode steps by group, against the plain-read kernel over the
+same bytes (the benchmark's read envelope, launched in group order).
 
 ``run`` launches, in this order: a plain elementwise copy (negation) of
 1 GiB (calibration: it reads and writes exactly 1 GiB), then for each Llama-3-8B decode group
@@ -436,6 +441,78 @@ def read_record(path: str) -> dict | None:
     return None
 
 
+DOWN_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 0>"   # K = 14336, activation rotated per lane
+
+
+def groups(csv_path: str) -> None:
+    """Per-group GEMV kernel durations of the decode steps in a rocprofv3 kernel trace, and the plain read."""
+    import csv
+    import re
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if "tq::" not in r["Kernel_Name"]:
+                continue                   # the library's kernels only (not PyTorch's input generation)
+            name = r["Kernel_Name"].replace("tq::(anonymous namespace)::", "")
+            m = re.search(r"([A-Za-z0-9_]+(<[^()]*>)?)\(", name)
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), m.group(1) if m else name))
+    rows.sort()
+    names = [r[2] for r in rows]
+    order = list(GROUPS)
+    kern = {"qkv": DOMINANT_KERNEL, "o": DOMINANT_KERNEL, "gate_up": DOMINANT_KERNEL, "down": DOWN_KERNEL}
+    layer = [kern[g] for g in order]
+    # A decode step: 32 layers of the four group launches back to back.
+    step = layer * 32
+    per = {g: [] for g in order}
+    spans = []
+    i = 0
+    while i + len(step) <= len(rows):
+        if names[i:i + len(step)] == step:
+            for j in range(len(step)):
+                per[order[j % 4]].append((rows[i + j][1] - rows[i + j][0]) / 1e3)
+            spans.append((rows[i + len(step) - 1][1] - rows[i][0]) / 1e3)
+            i += len(step)
+        else:
+            i += 1
+    # The read envelope: runs of consecutive plain reads, one run per group in group order.
+    reads, run = [], []
+    for k, n in enumerate(names):
+        if n == "stream_read_kernel":
+            if run and k != run[-1] + 1:
+                reads.append(run)
+                run = []
+            run.append(k)
+    if run:
+        reads.append(run)
+    env = {}
+    if len(reads) == len(order):
+        for g, r in zip(order, reads):
+            env[g] = statistics.median((rows[k][1] - rows[k][0]) / 1e3 for k in r)
+    lines = ["# Decode GEMV durations by group (Llama-3-8B layer shapes, rocprofv3 kernel trace)", "",
+             "Command (repository root on the GPU host; OUT is any scratch folder):", "", "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o bench -- "
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "python3 -m dequant_gemv_tq_amd.profiling groups OUT/trace/bench_kernel_trace.csv", "```", "",
+             f"{len(spans)} graph-replayed decode steps of 128 launches found in the trace (the first replays "
+             "include the profiler's warm-up). Kernel execution time per launch, median over every layer of "
+             "every step; the plain read is `stream_read_kernel` over the same bytes with the same launch "
+             "shape (the benchmark's read envelope).", "",
+             "| group | N x K | kernel | GEMV median us | plain read median us | GEMV / read |",
+             "|---|---|---|---|---|---|"]
+    rec = {}
+    for g in order:
+        n, k = GROUPS[g]
+        gm = statistics.median(per[g]) if per[g] else float("nan")
+        rm = env.get(g, float("nan"))
+        rec[g] = {"gemv_us": round(gm, 2), "read_us": round(rm, 2), "ratio": round(gm / rm, 3)}
+        lines.append(f"| {g} | {n} x {k} | `{kern[g]}` | {gm:.2f} | {rm:.2f} | {gm / rm:.3f} |")
+    if spans:
+        lines += ["", f"Step span (first launch start to last launch end), median: {statistics.median(spans):.1f} us.",
+                  ""]
+    lines += ["groups-json: " + json.dumps({"groups": rec, "source_sha256": stats_source_hash()}), ""]
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "run":
         run()
@@ -443,6 +520,8 @@ if __name__ == "__main__":
         summarize(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 3 and sys.argv[1] == "stats":
         stats(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "groups":
+        groups(sys.argv[2])
     elif len(sys.argv) >= 2 and sys.argv[1] == "gemm_run":
         gemm_run()
     elif len(sys.argv) in (3, 4) and sys.argv[1] == "gemm_summarize":
