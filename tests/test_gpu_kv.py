@@ -162,3 +162,14 @@ def test_attn_decode_llama8b_heads_8k():
     lengths = torch.tensor([8192, 3001], dtype=torch.int32, device=DEV)
     _, worst = _check_attn(q, lengths, cache, "llama8b 8K")
     assert worst < 1e-4
+
+
+def test_attn_decode_many_splits_32k():
+    """32768 cached tokens: 128 splits per sequence in the combine (its split loop in groups of eight), with a
+    ragged second sequence (20001 tokens: a partial last split)."""
+    B, T, Hq, Hkv = 2, 32768, 8, 2
+    cache = _cache(B, T, Hkv, 80)
+    q = _rand((B, Hq, D), 81, torch.bfloat16, 1.5)
+    lengths = torch.tensor([32768, 20001], dtype=torch.int32, device=DEV)
+    _, worst = _check_attn(q, lengths, cache, "32K tokens")
+    assert worst < 1e-4
