@@ -123,3 +123,25 @@ def test_blockfp_gemm_fp32_many_rows(fmt):
     torch.cuda.synchronize()
     yr, a = obf.gemm_deq_o64(Wd, X.cpu().numpy())
     assert assert_within(f32np(Y), yr, a, what=f"{fmt} fp32 M={m}") < 1e-4
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp6"])
+@pytest.mark.parametrize("m", [2, 16, 64])
+def test_blockfp_gemm_padded_row_strides(fmt, m):
+    """Block-float products through activation and output row strides above K and N (VALU rows at M = 2,
+    the MFMA kernel with K split over workgroups at K = 8192 above); the output's padding stays untouched."""
+    n, k = 80, 8192
+    W = _outlier_weight(n, k, 1200 + m, torch.bfloat16)
+    codes, bs, ts, Wd = _check(fmt, W)
+    X = workloads.activation(m, k, workloads.generator(1300 + m, DEV), DEV, torch.bfloat16)
+    x_full = torch.zeros((m, k + 64), dtype=torch.bfloat16, device=DEV)
+    x = x_full[:, :k]
+    x.copy_(X)
+    y_full = torch.full((m, n + 24), -7.0, dtype=torch.float32, device=DEV)
+    y = y_full[:, :n]
+    say(f"[{fmt} gemm] padded strides M={m} ldx={x.stride(0)} ldy={y.stride(0)}")
+    tqa.blockfp_gemm(fmt, codes, bs, ts, x, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y_full[:, n:] == -7.0)
+    yr, a = obf.gemm_deq_o64(Wd, X.float().cpu().numpy())
+    assert assert_within(f32np(y), yr, a, what=f"{fmt} padded M={m}") < 1e-4

@@ -316,3 +316,27 @@ def test_gemm_workspace_reused_across_shapes():
         # every call leaves the per-tile counters (the first 64 KiB) at zero for the next one
         torch.cuda.synchronize()
         assert int(ws[:65536].view(torch.int32).count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 16, 17, 64])
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float32])
+def test_gemm_padded_row_strides(m, xdtype):
+    """Activation rows and output rows with leading dimensions above K and N (slices of wider buffers): every
+    path (VALU rows, the persistent MFMA kernel with K split over workgroups at K = 8192, the float32 hi/lo
+    MFMA kernel) reads and writes through them, and the padding columns of the output stay untouched."""
+    n, k = 96, 8192
+    g = workloads.generator(3000 + m, DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    X = workloads.activation(m, k, g, DEV, torch.bfloat16)
+    packed, scales = tqa.quantize(W)
+    xr_full = torch.zeros((m, k + 64), dtype=xdtype, device=DEV)
+    xr = xr_full[:, :k]
+    xr.copy_(tqa.rotate(X, dtype=xdtype))
+    y_full = torch.full((m, n + 40), 12345.0, dtype=torch.float32, device=DEV)
+    y = y_full[:, :n]
+    say(f"[gemm] padded strides M={m} x'={xdtype} ldx={xr.stride(0)} ldy={y.stride(0)}")
+    tqa.gemm(packed, scales, xr, out=y)
+    torch.cuda.synchronize()
+    assert torch.all(y_full[:, n:] == 12345.0)
+    yr, a = otq.gemm_o64(packed.cpu().numpy(), u16(scales), X.float().cpu().numpy())
+    assert_within(f32np(y), yr, a, what=f"gemm padded M={m} {xdtype}")
