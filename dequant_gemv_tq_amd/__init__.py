@@ -230,11 +230,20 @@ def dequantize(packed: torch.Tensor, scales: torch.Tensor, sign_mask: int = DEFA
 
 
 def rotate(x: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, dtype=torch.float32, out=None):
-    """x [M, K] or [K] -> x' of the same shape (dtype fp32 or bf16)."""
+    """x [M, K] or [K] -> x' of the same shape (dtype fp32 or bf16); rows may be strided (unit column
+    stride), and ``out`` is written in place (a view of it, never a copy)."""
     _dev(x, "x")
     x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    _need(x2.dim() == 2 and x2.stride(1) == 1, "x must be [M, K] or [K] with unit column stride")
     M, K = x2.shape
-    xr = torch.empty((M, K), dtype=dtype, device=x.device) if out is None else out.reshape(M, K)
+    if out is None:
+        xr = torch.empty((M, K), dtype=dtype, device=x.device)
+    else:
+        _need(isinstance(out, torch.Tensor) and out.dim() == x.dim(), "out must have the shape of x")
+        _need(out.dim() == 2 or out.is_contiguous(), "a 1-D out must be contiguous")
+        xr = out if out.dim() == 2 else out.view(1, -1)
+        _rows(xr, "out", (torch.float32, torch.bfloat16), M, K)
+        _same_device(x2, (xr, "out"))
     st = lib().tq_rotate(_ptr(x2), _dtype_code(x2, "x"), M, K, x2.stride(0), sign_mask & 0xFFFFFFFF,
                          _ptr(xr), _dtype_code(xr, "out"), xr.stride(0), _stream())
     _check("tq_rotate", st)
@@ -376,7 +385,8 @@ def blockfp_gemm(fmt: str, codes: torch.Tensor, block_scales: torch.Tensor, tens
     _need(x2.shape[1] == K and x2.stride(1) == 1, f"x must be [M, {K}] or [{K}] with unit column stride")
     M = x2.shape[0]
     y = torch.empty((M, N), dtype=torch.float32, device=codes.device) if out is None else out
-    y2 = y if y.dim() == 2 else y.reshape(1, -1)
+    _need(isinstance(y, torch.Tensor) and (y.dim() == 2 or y.is_contiguous()), "a 1-D out must be contiguous")
+    y2 = y if y.dim() == 2 else y.view(1, -1)              # a view: the call writes into ``out``
     _rows(y2, "out", (torch.float32,), M, N)
     _same_device(codes, (x2, "x"), (y2, "out"))
     y = y2 if y.dim() == 2 else y

@@ -340,3 +340,25 @@ def test_gemm_padded_row_strides(m, xdtype):
     assert torch.all(y_full[:, n:] == 12345.0)
     yr, a = otq.gemm_o64(packed.cpu().numpy(), u16(scales), X.float().cpu().numpy())
     assert_within(f32np(y), yr, a, what=f"gemm padded M={m} {xdtype}")
+
+
+def test_rotate_padded_rows_and_given_outputs():
+    """Rotation through padded input and output row strides, into a given output (written in place), and of
+    a single vector into a given 1-D output: bit-exact against the oracle."""
+    g = workloads.generator(6, DEV)
+    x = workloads.activation(5, 2048, g, DEV, torch.bfloat16)
+    ref = otq.rotate_f32(x.float().cpu().numpy().reshape(5, -1, 32), otq.DEFAULT_SIGN_MASK).reshape(5, -1)
+    x_full = torch.zeros((5, 2048 + 96), dtype=torch.bfloat16, device=DEV)
+    x_full[:, :2048] = x
+    out_full = torch.full((5, 2048 + 32), 9.0, dtype=torch.float32, device=DEV)
+    say("[rotate] padded rows into a given output")
+    r = tqa.rotate(x_full[:, :2048], out=out_full[:, :2048])
+    torch.cuda.synchronize()
+    assert r.data_ptr() == out_full.data_ptr()
+    np.testing.assert_array_equal(out_full[:, :2048].cpu().numpy(), ref)
+    assert torch.all(out_full[:, 2048:] == 9.0)
+    v_out = torch.empty(2048, dtype=torch.float32, device=DEV)
+    r1 = tqa.rotate(x[2].contiguous(), out=v_out)
+    torch.cuda.synchronize()
+    assert r1.data_ptr() == v_out.data_ptr()
+    np.testing.assert_array_equal(v_out.cpu().numpy(), ref[2])
