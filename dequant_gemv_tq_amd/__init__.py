@@ -462,8 +462,9 @@ def kv_quantize_k(K: torch.Tensor, out=None):
         scales = torch.empty(K.shape[:-1] + (d // 32,), dtype=torch.int16, device=K.device)
     else:
         codes, scales = out
-        if codes.shape != K.shape or scales.shape != K.shape[:-1] + (d // 32,):
-            raise ValueError("out shapes do not match K")
+        _dense(codes, "out[0]", (torch.int8,), tuple(K.shape))
+        _dense(scales, "out[1]", _SCALE16, tuple(K.shape[:-1]) + (d // 32,))
+        _same_device(K, (codes, "out[0]"), (scales, "out[1]"))
     st = lib().tq_kv_quantize_k(_ptr(K), _dtype_code(K, "K"), n, d, _ptr(codes), _ptr(scales), _stream())
     _check("tq_kv_quantize_k", st)
     return codes, scales
@@ -483,8 +484,9 @@ def kv_quantize_v(V: torch.Tensor, sign=None, out=None):
         norms = torch.empty(V.shape[:-1], dtype=torch.int16, device=V.device)
     else:
         packed, norms = out
-        if packed.shape != V.shape[:-1] + (d // 2,) or norms.shape != V.shape[:-1]:
-            raise ValueError("out shapes do not match V")
+        _dense(packed, "out[0]", (torch.uint8,), tuple(V.shape[:-1]) + (d // 2,))
+        _dense(norms, "out[1]", _SCALE16, tuple(V.shape[:-1]))
+        _same_device(V, (packed, "out[0]"), (norms, "out[1]"))
     st = lib().tq_kv_quantize_v(_ptr(V), _dtype_code(V, "V"), n, d, sign, _ptr(packed), _ptr(norms), _stream())
     _check("tq_kv_quantize_v", st)
     return packed, norms

@@ -173,3 +173,24 @@ def test_attn_decode_many_splits_32k():
     lengths = torch.tensor([32768, 20001], dtype=torch.int32, device=DEV)
     _, worst = _check_attn(q, lengths, cache, "32K tokens")
     assert worst < 1e-4
+
+
+def test_kv_encode_rejects_malformed_outputs():
+    """Given outputs of the wrong dtype, shape or layout are refused before anything launches (a strided
+    view would otherwise be written as if dense)."""
+    K = _rand((2, 3, 40, D), 16, torch.bfloat16)
+    kc, ks = tqa.kv_quantize_k(K)
+    vp, vn = tqa.kv_quantize_v(K)
+    with pytest.raises(ValueError, match="dtype"):
+        tqa.kv_quantize_k(K, out=(kc.to(torch.int16), ks))
+    with pytest.raises(ValueError, match="contiguous"):
+        wide = torch.empty((2, 3, 40, 2 * D), dtype=torch.int8, device=DEV)
+        tqa.kv_quantize_k(K, out=(wide[..., :D], ks))
+    with pytest.raises(ValueError, match="shape"):
+        tqa.kv_quantize_k(K, out=(kc, ks[..., :2].contiguous()))
+    with pytest.raises(ValueError, match="contiguous"):
+        wide = torch.empty((2, 3, 40, D), dtype=torch.uint8, device=DEV)
+        tqa.kv_quantize_v(K, out=(wide[..., :D // 2], vn))
+    with pytest.raises(ValueError, match="dtype"):
+        tqa.kv_quantize_v(K, out=(vp, vn.to(torch.float32)))
+    torch.cuda.synchronize()
