@@ -599,60 +599,116 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Activation operands of a pass, straight from X into registers: for
-  // group j, step s and m tile mt, lane (n, g) needs the 8 elements of
-  // activation row 16 mt + n that meet its weights (by block: elements
-  // 32 s + 8 g of the group; by element: 32 g + 8 s).  They are loaded in
-  // row-major lane order, lane 4 n + g reading elements 32 s + 8 g, so that
-  // four neighbouring lanes read 64 contiguous bytes of one row, and handed
-  // to lane n + 16 g by the same ds_bpermute as the weights; the by-element
-  // order then swaps s and g across the lane groups.  No LDS staging and no
-  // workgroup barrier: each wavefront loads only its own operands (an
-  // earlier version staged a pass's activations through LDS in 64 KiB parts,
-  // with two barriers per part).  Rows past M are clamped to row M - 1 and
-  // elements past K to the last block: both only feed outputs that are not
-  // written (an MFMA output row depends on its own activation row alone) or
-  // steps that are skipped.
+  // Activation operands of a pass.  For group j and m tile mt, lane (n, g)
+  // needs, for step s, eight elements of activation row 16 mt + n: by block
+  // the elements 32 s + 8 g of the group, by element 32 g + 8 s.  Rows past
+  // M are clamped to row M - 1 and elements past K to the last block: both
+  // only feed outputs that are not written (an MFMA output row depends on
+  // its own activation row alone) or steps that are skipped.  Each
+  // wavefront loads only its own operands (an earlier version staged a
+  // pass's activations for the whole workgroup through LDS in 64 KiB parts,
+  // with two barriers per part).
+  //
+  // Two m tiles (kStageA): each 4 KiB piece (one m tile: 16 rows x 128
+  // elements) is loaded with 256 contiguous bytes of a row per 16 lanes
+  // (four rows per load) and passed through this wavefront's 4 KiB of the
+  // partial-tile ring, which is idle until the pass's first tile; row n keeps
+  // its 16-byte chunk c at position c ^ n, so both the stores (one row, 16
+  // chunks) and the loads (16 rows, one chunk each) of 16 lanes fall on
+  // distinct banks; one workgroup barrier per pass then frees the ring for
+  // the tiles.  8B layer at M = 32: 76.3-76.9 -> 72.1 us.  With one or
+  // four m tiles, or MXFP6's larger register sets, the round trip costs
+  // registers the kernel does not have (it spilled and ran slower), and the
+  // operands are loaded in row-major
+  // lane order, lane 4 n + g reading elements 32 s + 8 g of row n (64
+  // contiguous bytes per row over four lanes), and handed to lane n + 16 g
+  // by the same ds_bpermute as the weights; the by-element order then swaps
+  // s and g across the lane groups.
+  constexpr bool kStageA = MT == 2 && !std::is_same<Fmt, GemmMXFP6>::value;   // MXFP6: spills
   constexpr uint32_t kPassK = 16u * NQ * 128u;               // elements of K per pass
   const uint32_t K = nb * 32u;
   auto load_a = [&](uint32_t pass) {
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kStageA) {
+      const uint32_t rq = (uint32_t)lane >> 4, e8 = 8u * ((uint32_t)lane & 15u);
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const uint32_t kg = pass * kPassK + 128u * ((uint32_t)wave + (uint32_t)(kWide * j));   // wavefront-uniform
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t k = min(kg + 32u * (uint32_t)s + 8u * lblk, K - 8u);
+      for (int j = 0; j < NQ; ++j) {
+        const uint32_t k = min(pass * kPassK + 128u * ((uint32_t)wave + (uint32_t)(kWide * j)) + e8, K - 8u);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const uint32_t r = min((uint32_t)(16 * mt) + lrow, M - 1u);
-          A[j][s][mt] = *reinterpret_cast<const uint4*>(X + ((size_t)r * ldx + k) * 2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t r = min((uint32_t)(16 * mt + 4 * i) + rq, M - 1u);
+            A[j][i][mt] = *reinterpret_cast<const uint4*>(X + ((size_t)r * ldx + k) * 2);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const uint32_t kg = pass * kPassK + 128u * ((uint32_t)wave + (uint32_t)(kWide * j));   // wavefront-uniform
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t k = min(kg + 32u * (uint32_t)s + 8u * lblk, K - 8u);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const uint32_t r = min((uint32_t)(16 * mt) + lrow, M - 1u);
+            A[j][s][mt] = *reinterpret_cast<const uint4*>(X + ((size_t)r * ldx + k) * 2);
+          }
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   auto place_a = [&]() {
+    if constexpr (kStageA) {
+      uint8_t* const st = smem + kLutSpace + (size_t)wave * 4096u;
+      const uint32_t wn = (uint32_t)lane >> 4, wc = (uint32_t)lane & 15u;   // store: row 4 i + wn, chunk wc
+      const uint32_t nl = (uint32_t)lane & 15u, gl = (uint32_t)lane >> 4;   // load: row nl, lane group gl
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
+      for (int j = 0; j < NQ; ++j) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint4& a = A[j][s][mt];
-          a.x = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.x);
-          a.y = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.y);
-          a.z = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.z);
-          a.w = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.w);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t n = 4u * (uint32_t)i + wn;
+            *reinterpret_cast<uint4*>(st + 256u * n + 16u * (wc ^ n)) = A[j][i][mt];
+          }
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): the piece is in LDS
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t c = Fmt::kByBlock ? 4u * (uint32_t)s + gl : 4u * gl + (uint32_t)s;
+            A[j][s][mt] = *reinterpret_cast<const uint4*>(st + 256u * nl + 16u * (c ^ nl));
+          }
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): read before the next piece is stored
+          __builtin_amdgcn_wave_barrier();
         }
-        if constexpr (!Fmt::kByBlock) {
-          uint32_t t[4][4];
-          transpose_groups(make_uint4(A[j][0][mt].x, A[j][1][mt].x, A[j][2][mt].x, A[j][3][mt].x), t[0]);
-          transpose_groups(make_uint4(A[j][0][mt].y, A[j][1][mt].y, A[j][2][mt].y, A[j][3][mt].y), t[1]);
-          transpose_groups(make_uint4(A[j][0][mt].z, A[j][1][mt].z, A[j][2][mt].z, A[j][3][mt].z), t[2]);
-          transpose_groups(make_uint4(A[j][0][mt].w, A[j][1][mt].w, A[j][2][mt].w, A[j][3][mt].w), t[3]);
+      }
+    } else {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) A[j][s][mt] = make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]);
+      for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            uint4& a = A[j][s][mt];
+            a.x = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.x);
+            a.y = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.y);
+            a.z = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.z);
+            a.w = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_addr, (int)a.w);
+          }
+          if constexpr (!Fmt::kByBlock) {
+            uint32_t t[4][4];
+            transpose_groups(make_uint4(A[j][0][mt].x, A[j][1][mt].x, A[j][2][mt].x, A[j][3][mt].x), t[0]);
+            transpose_groups(make_uint4(A[j][0][mt].y, A[j][1][mt].y, A[j][2][mt].y, A[j][3][mt].y), t[1]);
+            transpose_groups(make_uint4(A[j][0][mt].z, A[j][1][mt].z, A[j][2][mt].z, A[j][3][mt].z), t[2]);
+            transpose_groups(make_uint4(A[j][0][mt].w, A[j][1][mt].w, A[j][2][mt].w, A[j][3][mt].w), t[3]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) A[j][s][mt] = make_uint4(t[0][s], t[1][s], t[2][s], t[3][s]);
+          }
         }
       }
     }
@@ -698,14 +754,25 @@ __global__ __launch_bounds__(64 * kWide) void gemm_small_kernel(const uint8_t* _
     load_a(pass);
     load_w(pa, t0, pass);
     load_w(pb, min(t0 + G, last), pass);
-    if constexpr (Fmt::kLut) {
-      if (pass == pass_begin) {
-        fill_pair_lut16(lut, tid, 64 * kWide);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's table stores; loads left in flight
-        __builtin_amdgcn_s_barrier();         // the whole table
+    if constexpr (kStageA) {
+      // Every wavefront's operands out of the ring (and the table complete)
+      // before any tile writes to the ring; the weight loads stay in flight.
+      if constexpr (Fmt::kLut) {
+        if (pass == pass_begin) fill_pair_lut16(lut, tid, 64 * kWide);
       }
+      place_a();
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      if constexpr (Fmt::kLut) {
+        if (pass == pass_begin) {
+          fill_pair_lut16(lut, tid, 64 * kWide);
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's table stores; loads left in flight
+          __builtin_amdgcn_s_barrier();         // the whole table
+        }
+      }
+      place_a();
     }
-    place_a();
 
     uint32_t ti = 0;                        // tiles of this pass done
     // Tile tt from register set w; w is refilled with tile `next` as soon
