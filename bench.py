@@ -137,7 +137,7 @@ def cpu_baseline(seconds):
         for t in gtasks:
             otq.gemv_rows_o64(t[1], t[2], t[3])
         g1 = time.perf_counter() - t0
-    reps = max(1, int(min(seconds / 6, 5.0) / max(g1, 1e-3)))
+    reps = max(1, int(min(seconds / 3, 8.0) / max(g1, 1e-3)))
     with threadpool_limits(1):
         t0 = time.perf_counter()
         for _ in range(reps):
