@@ -362,3 +362,64 @@ def test_rotate_padded_rows_and_given_outputs():
     torch.cuda.synchronize()
     assert r1.data_ptr() == v_out.data_ptr()
     np.testing.assert_array_equal(v_out.cpu().numpy(), ref[2])
+
+
+def test_gemm_split_k_graph_replays():
+    """Split-K GEMMs (M = 16 and M = 32 at K = 14336: sums and per-tile counters in the workspace) captured in
+    a HIP graph and replayed several times, with other library work between the replays: every replay equals
+    the eager result bit for bit, since each call leaves the counters at zero for the next."""
+    n, k = 1024, 14336
+    g = workloads.generator(4242, DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    packed, scales = tqa.quantize(W)
+    xs = [tqa.rotate(workloads.activation(m, k, g, DEV, torch.bfloat16), dtype=torch.bfloat16) for m in (16, 32)]
+    ys = [torch.empty((x.shape[0], n), dtype=torch.float32, device=DEV) for x in xs]
+    ws = torch.zeros(tqa.workspace_bytes("gemm", n, k, 32), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > 65536                                   # the split path is taken
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ref = [tqa.gemm(packed, scales, x, workspace=ws).clone() for x in xs]
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            for x, y in zip(xs, ys):
+                tqa.gemm(packed, scales, x, out=y, workspace=ws)
+        for rep in range(4):
+            say(f"[gemm] split-K graph replay {rep}")
+            for y in ys:
+                y.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            for y, r in zip(ys, ref):
+                assert torch.equal(y, r), f"replay {rep}"
+            tqa.gemm(packed, scales, xs[1], workspace=ws)       # eager work on the same workspace between replays
+            torch.cuda.synchronize()
+    assert int(ws[:65536].view(torch.int32).count_nonzero()) == 0
+    X0 = xs[0].float().cpu().numpy()                            # x' itself: the oracle's product of rotated rows
+    q = otq.rotated_weights_f64(packed.cpu().numpy()[:64], u16(scales)[:64])
+    yr = X0.astype(np.float64) @ q.T
+    a = np.abs(X0.astype(np.float64)) @ np.abs(q).T
+    assert np.all(np.abs(f32np(ref[0])[:, :64] - yr) <= 1e-2 * a)   # bf16 operands: within 2^-7 of sum |q x'|
+
+
+def test_gemm_split_k_on_two_streams():
+    """The binding keeps one zero-filled workspace per stream: split-K GEMMs issued on two streams without
+    synchronizing between them give the results of the same calls made one after the other."""
+    n, k, m = 2048, 14336, 16
+    g = workloads.generator(4343, DEV)
+    Ws = [workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16) for _ in range(2)]
+    qs = [tqa.quantize(W) for W in Ws]
+    x = tqa.rotate(workloads.activation(m, k, g, DEV, torch.bfloat16), dtype=torch.bfloat16)
+    ref = [tqa.gemm(p, sc, x) for p, sc in qs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    say("[gemm] split-K on two streams")
+    for it in range(3):
+        for i, (st, (p, sc)) in enumerate(zip(streams, qs)):
+            with torch.cuda.stream(st):
+                outs[i].append(tqa.gemm(p, sc, x))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for y in outs[i]:
+            assert torch.equal(y, ref[i])
