@@ -66,3 +66,42 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     st = L.tq_attn_decode_noalloc(g, BF16, 64, 32, 8, 128, 32768, g, g, g, g, g, sign, g,
                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 2                     # TQ_ESHAPE, before anything launches
+
+
+def test_noalloc_under_graph_capture():
+    """The allocation-free call captured in a HIP graph (what it is for) and replayed several times, with an
+    eager call of another shape on the same device between the replays: every replay gives the result of the
+    workspace entry point."""
+    L = tqa.lib()
+    B, Hq, Hkv, T = 4, 16, 4, 1500
+    kc, ks, vp, vn = _cache(B, Hkv, T, 21)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(22)
+    q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    lens = torch.tensor([1500, 3, 700, 257], dtype=torch.int32, device="cuda")
+    sign = tqa.kv_sign_from_seed(0)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    ws_bytes = L.tq_attn_workspace_bytes(B, Hq, T)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    o_ref = torch.empty((B, Hq, 128), device="cuda")
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.tq_attn_decode(P(q), BF16, B, Hq, Hkv, 128, T, P(lens), P(kc), P(ks), P(vp), P(vn), sign, P(o_ref),
+                            P(ws), ws_bytes, cur()) == 0
+    o = torch.empty_like(o_ref)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        # one eager call first: the array's device address is looked up outside the capture
+        assert L.tq_attn_decode_noalloc(P(q), BF16, B, Hq, Hkv, 128, T, P(lens), P(kc), P(ks), P(vp), P(vn), sign,
+                                        P(o), cur()) == 0
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            assert L.tq_attn_decode_noalloc(P(q), BF16, B, Hq, Hkv, 128, T, P(lens), P(kc), P(ks), P(vp), P(vn),
+                                            sign, P(o), cur()) == 0
+        for rep in range(3):
+            o.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref), f"replay {rep}"
+            o_ref2, o_new2 = _both(2, 8, 2, 400, [400, 99], seed=30 + rep)   # other shapes, same array
+            assert torch.equal(o_new2, o_ref2)
