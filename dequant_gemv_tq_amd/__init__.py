@@ -252,7 +252,7 @@ def rotate(x: torch.Tensor, sign_mask: int = DEFAULT_SIGN_MASK, dtype=torch.floa
 
 def gemv(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, rotated: bool = False,
          sign_mask: int = DEFAULT_SIGN_MASK, out=None):
-    """y [N] float32 = W_deq x.  x: [K] raw (fp32/bf16) or, with rotated=True, x' fp32."""
+    """y [N] float32 = W_deq x.  x: [K] raw (fp32/bf16) or, with rotated=True, x' (fp32 or bf16) from rotate()."""
     N, K = _tq4_weights(packed, scales)
     _dev(x, "x")
     if x.numel() != K or not x.is_contiguous():

@@ -95,7 +95,7 @@ tq_status tq_gemv(const uint8_t* packed, const uint16_t* scales, int64_t N, int6
   if (!x || !y) return TQ_EINVAL;
   if (tq_status st = check_weights(packed, scales, N, K)) return st;
   if (K > 131072 || N > 0x7fffffff) return TQ_ESHAPE;
-  if (x_is_rotated ? xt != TQ_F32 : !float_or_bf16(xt)) return TQ_EDTYPE;
+  if (!float_or_bf16(xt)) return TQ_EDTYPE;
   if (!aligned(x, 16) || !aligned(y, 4)) return TQ_EALIGN;
   return from_hip(tq::launch_gemv(packed, scales, N, K, sign_mask, x, xt == TQ_BF16, x_is_rotated != 0, y, stream));
 }

@@ -149,9 +149,11 @@ tq_status tq_rotate(const void* x, tq_dtype xt, int64_t M, int64_t K, int64_t ld
 /* Fused batch-1 GEMV y = W_deq x on TQ4_1S weights, computed in the rotated
  * domain: y_n = sum_b [ d0 * sum_{i<16} c[idx_i] x'_i + d1 * sum_{i>=16} ... ]
  * with float32 accumulation (TQ4 page, decode-speed section).
- *   x            [K]; if x_is_rotated != 0 it is x' from tq_rotate and must
- *                be TQ_F32; otherwise it is the raw activation (TQ_F32 or
- *                TQ_BF16) and the kernel rotates it itself (sign_mask used).
+ *   x            [K]; if x_is_rotated != 0 it is x' from tq_rotate (TQ_F32,
+ *                or TQ_BF16 as tq_rotate rounds it: the product is then
+ *                exact for that rounded x'); otherwise it is the raw
+ *                activation (TQ_F32 or TQ_BF16) and the kernel rotates it
+ *                itself (sign_mask used).
  *   y            [N] float32 (output).
  * Limits: K <= 131072.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN (x 16-byte
  * aligned, y 4-byte aligned), TQ_EDTYPE. */

@@ -91,7 +91,7 @@ def test_other_calls_reject_before_launch():
     assert L.tq_gemv(g, g, 8, 64, 0, None, F32, 1, g, None) == EINVAL
     assert L.tq_gemv(g, g, 8, 50, 0, g, F32, 1, g, None) == ESHAPE
     assert L.tq_gemv(g, g, 8, 131072 + 32, 0, g, F32, 1, g, None) == ESHAPE
-    assert L.tq_gemv(g, g, 8, 64, 0, g, BF16, 1, g, None) == EDTYPE          # rotated x must be fp32
+    assert L.tq_gemv(g, g, 8, 64, 0, g, F16, 1, g, None) == EDTYPE           # rotated x: fp32 or bf16
     assert L.tq_gemv(g, g, 8, 64, 0, g, F16, 0, g, None) == EDTYPE
     assert L.tq_gemv(g, g, 8, 64, 0, _p(GOOD + 4), F32, 1, g, None) == EALIGN
     assert L.tq_gemv(g, g, 8, 64, 0, g, F32, 1, _p(GOOD + 2), None) == EALIGN

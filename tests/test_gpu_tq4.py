@@ -423,3 +423,26 @@ def test_gemm_split_k_on_two_streams():
     for i in range(2):
         for y in outs[i]:
             assert torch.equal(y, ref[i])
+
+
+@pytest.mark.parametrize("n,k", [(300, 4096), (1000, 14336)])
+def test_gemv_prerotated_bf16(n, k):
+    """A pre-rotated activation in bf16 (as tq_rotate rounds it): the product is exact for that x', so it is
+    checked in the rotated domain against the float64 q . x' within 1e-3 of sum |q x'|."""
+    g = workloads.generator(5100 + n, DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    x = workloads.activation(1, k, g, DEV, torch.bfloat16)[0].contiguous()
+    packed, scales = tqa.quantize(W)
+    xr = tqa.rotate(x, dtype=torch.bfloat16)
+    say(f"[gemv] pre-rotated bf16 x' {n}x{k}")
+    y = tqa.gemv(packed, scales, xr, rotated=True)
+    torch.cuda.synchronize()
+    q = otq.rotated_weights_f64(packed.cpu().numpy(), u16(scales))
+    xv = xr.float().cpu().numpy().astype(np.float64)
+    yr = q @ xv
+    a = np.abs(q) @ np.abs(xv)
+    assert np.all(np.abs(f32np(y) - yr) <= 1e-3 * a)
+    # the same x' as float32 gives the same product up to float32 rounding
+    y32 = tqa.gemv(packed, scales, xr.float().contiguous(), rotated=True)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(f32np(y32) - f32np(y)) <= 1e-5 * a)
