@@ -469,16 +469,21 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 }
 
 // Combine the splits of (sequence b, head h) and rotate back:
-// o = (1/128) D H (Z / L_total).  Thread i computes output element i.  The
-// split maxima and sums are read by all threads at once (thread t takes
-// splits t, t + 128, ...) and reduced in LDS; the z sums are then read eight
-// splits at a time, so the loads are in flight together.
+// o = (1/128) D H (Z / L_total).  Thread i computes output element i: up to
+// 16 splits it requests every split's maximum, sum and z_i at once (one
+// round trip of loads) and merges them in split order, M = max_j m_j, then
+// l and z_i weighted by 2^(m_j - M).  With more splits the 128 threads first
+// reduce the (m_j, l_j) pairs together, then each reads its z_i 32 splits at
+// a time.  H is then applied in butterflies: stride 64 through LDS (the two
+// wavefronts), strides 32 .. 1 by shuffles.
 __global__ __launch_bounds__(kD) void attn_combine_kernel(const float* __restrict__ part,
                                                           const int32_t* __restrict__ lengths, uint32_t Tmax,
                                                           uint32_t Hq, uint32_t S, Signs sg, float* __restrict__ out) {
+  constexpr uint32_t kIn = 16;            // splits merged in one round trip of loads
+  constexpr uint32_t kZ = 32;             // z values a thread requests at once beyond that
   __shared__ float zs[kD];
   __shared__ float red[2][2];
-  const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
+  const int i = threadIdx.x, lane = i & 63;
   const uint32_t h = blockIdx.x, b = blockIdx.y;
   const uint32_t L = (uint32_t)min(max(lengths[b], 0), (int32_t)Tmax);
   float* o = out + ((size_t)b * Hq + h) * kD;
@@ -488,42 +493,71 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(const float* __restric
   }
   const uint32_t ns = (L + kChunk - 1) / kChunk;
   const float* p = part + ((size_t)b * Hq + h) * S * kPart;
-  float M = -__builtin_inff();
-  for (uint32_t s = i; s < ns; s += kD) M = fmaxf(M, p[s * kPart]);
+  float M = -__builtin_inff(), l = 0.f, z = 0.f;
+  if (ns <= kIn) {
+    float mv[kIn], lv[kIn], zv[kIn];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, xor_f(M, m));
-  if (lane == 0) red[0][wave] = M;
-  __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
-  float l = 0.f;
-  for (uint32_t s = i; s < ns; s += kD) l += p[s * kPart + 1] * __builtin_amdgcn_exp2f(p[s * kPart] - M);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) l += xor_f(l, m);
-  if (lane == 0) red[1][wave] = l;
-  __syncthreads();
-  l = red[1][0] + red[1][1];
-  float z = 0.f;
-  uint32_t s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    float zv[8], mv[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      zv[k] = p[(s + k) * kPart + 2 + i];
-      mv[k] = p[(s + k) * kPart];
+    for (uint32_t u = 0; u < kIn; ++u) {
+      const float* q = p + (size_t)min(u, ns - 1u) * kPart;     // repeats of the last split: no effect on M
+      mv[u] = q[0];
+      lv[u] = q[1];
+      zv[u] = q[2 + i];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) z += zv[k] * __builtin_amdgcn_exp2f(mv[k] - M);
+    for (uint32_t u = 0; u < kIn; ++u) M = fmaxf(M, mv[u]);
+#pragma unroll
+    for (uint32_t u = 0; u < kIn; ++u) {   // no branch: a branch per split would hold its load back
+      const float w = u < ns ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f;
+      l += lv[u] * w;
+      z += zv[u] * w;
+    }
+  } else {
+    // Thread t reduces splits t, t + 128, ... to (m_t, l_t); each wavefront
+    // merges its threads' pairs and the two wavefronts meet in LDS.
+    float mt = -__builtin_inff(), lt = 0.f;
+    for (uint32_t j = i; j < ns; j += kD) {
+      const float mj = p[(size_t)j * kPart], lj = p[(size_t)j * kPart + 1];
+      const float mn = fmaxf(mt, mj);
+      lt = lt * __builtin_amdgcn_exp2f(mt - mn) + lj * __builtin_amdgcn_exp2f(mj - mn);
+      mt = mn;
+    }
+    float Mw = mt;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) Mw = fmaxf(Mw, xor_f(Mw, m));
+    float lw = mt == -__builtin_inff() ? 0.f : lt * __builtin_amdgcn_exp2f(mt - Mw);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lw += xor_f(lw, m);
+    if (lane == 0) {
+      red[i >> 6][0] = Mw;
+      red[i >> 6][1] = lw;
+    }
+    __syncthreads();
+    M = fmaxf(red[0][0], red[1][0]);       // finite: wavefront 0 holds split 0
+    l = red[0][1] * __builtin_amdgcn_exp2f(red[0][0] - M) + red[1][1] * __builtin_amdgcn_exp2f(red[1][0] - M);
+    for (uint32_t j0 = 0; j0 < ns; j0 += kZ) {
+      float mv[kZ], zv[kZ];
+#pragma unroll
+      for (uint32_t u = 0; u < kZ; ++u) {
+        const float* q = p + (size_t)min(j0 + u, ns - 1u) * kPart;
+        mv[u] = q[0];
+        zv[u] = q[2 + i];
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < kZ; ++u) z += zv[u] * (j0 + u < ns ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f);
+    }
   }
-  for (; s < ns; ++s) z += p[s * kPart + 2 + i] * __builtin_amdgcn_exp2f(p[s * kPart] - M);
   zs[i] = z / l;
   __syncthreads();
-  float acc = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < kD; ++j) {
-    const float v = zs[j];
-    acc += (__builtin_popcount(i & j) & 1) ? -v : v;
+  // (a, b) at indices (j, j + s), j without bit s: a + b at j, a - b at j + s.
+  const float pv = zs[i ^ 64];
+  float v = zs[i];
+  v = (i & 64) ? pv - v : v + pv;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float pm = xor_f(v, m);
+    v = (lane & m) ? pm - v : v + pm;
   }
-  const float r = acc * (1.0f / kD);
+  const float r = v * (1.0f / kD);
   o[i] = ((sg.w[i >> 5] >> (i & 31)) & 1u) ? -r : r;
 }
 
