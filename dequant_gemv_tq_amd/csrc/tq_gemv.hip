@@ -259,6 +259,57 @@ struct FmtMXFP6 {
   }
 };
 
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Bit e of kHadPar[i & 7] (byte i & 7 of the constant) is the parity of
+// (i & e): the sign pattern of Sylvester Hadamard entries H[i][8 b + e].
+constexpr unsigned long long kHadPar = 0x963C5AF066CCAA00ull;
+
+// x' = H D x for the 64 blocks of one wavefront (lane l owns block l of the
+// wavefront's range) on the matrix cores.  (H D)[i][k] = (-1)^(popcount(i & k)
+// + mask_k) is +-1, exact in bf16, and so is a bf16 activation, so every
+// product is exact and only the float32 accumulation rounds.  Per 32 blocks
+// and half block h, one v_mfma_f32_32x32x16_bf16: the A operand is the
+// matrix (lane l: row i = l % 32, columns k = 16 h + 8 (l / 32) + e), the B
+// operand eight consecutive activation elements (lane l: block l % 32 of the
+// tile, elements k = 16 h + 8 (l / 32) + e), xq[T][h] for tile T.  Lane l,
+// register r of tile T's result holds element 8 (r / 4) + 4 (l / 32) + r % 4
+// of block 32 T + l % 32; one permlane32 swap per register pair gives each
+// lane the other half of its own block, so v[i] = x'_i on return.
+__device__ __forceinline__ void rotate_blocks_mfma(const uint4 (&xq)[2][2], uint32_t mask, int lane,
+                                                   float (&v)[32]) {
+  const uint32_t i = (uint32_t)lane & 31u, kb = 8u * ((uint32_t)lane >> 5);
+  const uint32_t par = (uint32_t)(kHadPar >> (8u * (i & 7u))) & 0xffu;
+  bf16x8 A[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t base = 16u * (uint32_t)h + kb;                  // bits 3 and 4 only
+    const uint32_t hi = (uint32_t)__builtin_popcount(i & base) & 1u;
+    const uint32_t s8 = (par ^ (mask >> base) ^ (0u - hi)) & 0xffu;   // sign of element base + e at bit e
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      w[t] = 0x3F803F80u | (((s8 >> (2 * t)) & 1u) << 15) | (((s8 >> (2 * t + 1)) & 1u) << 31);
+    A[h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  f32x16 c[2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    c[T] = f32x16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      c[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[h], __builtin_bit_cast(bf16x8, xq[T][h]), c[T], 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float a = c[0][r], b = c[1][r];
+    swap32(a, b);
+    v[8 * (r / 4) + r % 4] = a;
+    v[8 * (r / 4) + 4 + r % 4] = b;
+  }
+}
+
 // One cross-lane stage of the 32-point FWHT when 8 consecutive lanes hold a
 // block, 4 consecutive elements each: elements i and i + 4d sit in lanes
 // l and l ^ d at the same position.  The lower lane forms a + b, the upper
@@ -456,8 +507,22 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
   // anything else so that their latency overlaps the table fill.
   float xr[J][MC][32];
   ActivationStage<kMode, kStage ? kStage : 1> xst;
+  // A raw bf16 activation row with one block per lane is rotated on the
+  // matrix cores: lane l loads the 16 bytes of blocks 32 T + l % 32 of the
+  // wavefront's range that the MFMA B operand takes (rotate_blocks_mfma).
+  constexpr bool kRotMfma = kMode == 3 && J == 1 && MC == 1 && !kStage;
+  uint4 xq[2][2];
   if constexpr (kStage) {
     xst.load(x, nb * 32, tid, nthreads);
+  } else if constexpr (kRotMfma) {
+    const uint32_t wbase = (uint32_t)(lk - lane);           // 64 wk: the wavefront's first block
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t blk = min(wbase + 32u * (uint32_t)T + ((uint32_t)lane & 31u), nb - 1);
+        xq[T][h] = *reinterpret_cast<const uint4*>(x + (size_t)blk * 64 + 32 * h + 16 * (lane >> 5));
+      }
   } else {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -495,17 +560,24 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
     // Unrotated activations are rotated per lane while the first tile's
     // loads are in flight: x' = FWHT32(D x); the 1/sqrt(32) is applied once
     // to each finished row sum instead of to every element.
+    if constexpr (kRotMfma) {
+      rotate_blocks_mfma(xq, mask, lane, xr[0][0]);
+      const bool inside = (uint32_t)lk < nb;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const bool inside = (uint32_t)(lk + j * TK) < nb;
+      for (int i = 0; i < 32; ++i) xr[0][0][i] = inside ? xr[0][0][i] : 0.f;
+    } else {
 #pragma unroll
-      for (int m = 0; m < MC; ++m) {
-        if constexpr (kMode >= 2) {
-          apply_signs(xr[j][m], mask);
-          fwht32(xr[j][m]);
+      for (int j = 0; j < J; ++j) {
+        const bool inside = (uint32_t)(lk + j * TK) < nb;
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+          if constexpr (kMode >= 2) {
+            apply_signs(xr[j][m], mask);
+            fwht32(xr[j][m]);
+          }
+#pragma unroll
+          for (int i = 0; i < 32; ++i) xr[j][m][i] = inside ? xr[j][m][i] : 0.f;
         }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) xr[j][m][i] = inside ? xr[j][m][i] : 0.f;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
