@@ -121,6 +121,30 @@ def test_gemv_shapes(n, k, mode):
     assert worst < 1e-4
 
 
+@pytest.mark.parametrize("k", [11296, 22400, 32000])
+def test_gemv_bf16_rotation_on_matrix_cores(k):
+    """A raw bf16 activation with one block per lane and at most two row slots per workgroup (K above
+    10240, at most 1024 blocks) is rotated on the matrix cores.  Block counts that leave the last
+    wavefront of a row part-filled (353, 700 and 1000 blocks), three sign masks, and one-hot activations
+    (x' of a one-hot x is exactly +-1, so y is a column of W_deq)."""
+    n = 37
+    g = workloads.generator(k, DEV)
+    W = workloads.normal_weight(n, k, k ** -0.5, g, DEV, torch.bfloat16)
+    x = workloads.activation(1, k, g, DEV, torch.bfloat16)[0].contiguous()
+    for mask in (0, 0xFFFFFFFF, otq.sign_mask_from_seed(k)):
+        say(f"[gemv mfma rotation] {n}x{k} mask={mask:#x}")
+        packed, scales = tqa.quantize(W, sign_mask=mask)
+        y = tqa.gemv(packed, scales, x, sign_mask=mask)
+        yr, a = otq.gemv_rows_o64(packed.cpu().numpy(), u16(scales), x.float().cpu().numpy(), mask)
+        assert assert_within(f32np(y), yr, a, what=f"gemv {n}x{k} mask {mask:#x}") < 1e-4
+    Wd = otq.dequantize_o64(packed.cpu().numpy(), u16(scales), mask)
+    for j in (0, 31, k // 2 + 5, k - 1):
+        e = torch.zeros(k, dtype=torch.bfloat16, device=DEV)
+        e[j] = 1.0
+        np.testing.assert_allclose(f32np(tqa.gemv(packed, scales, e, sign_mask=mask)), Wd[:, j], rtol=1e-5,
+                                   atol=1e-7)
+
+
 def test_gemv_tiny_config_and_special_vectors():
     W, x = workloads.tiny_tq(DEV)
     packed, scales = tqa.quantize(W)
