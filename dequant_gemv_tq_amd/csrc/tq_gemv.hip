@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
       load_tile(min(t + (uint32_t)(kEarly + ic.value) * G, last), ps[kEarly + ic.value]);
     });
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    if constexpr (Fmt::kLut) __syncthreads();   // the pair table (the only thing shared so far)
   }
   constexpr float kOutScale = kMode >= 2 ? kInvSqrt32 : 1.0f;
 
@@ -825,8 +825,12 @@ void launch_gemv_jr(const Fmt& fmt, uint32_t N, uint32_t nb, uint32_t mask, cons
     // slots; with one or two slots (K above 8192) every lane rotates its own
     // blocks instead, which saves the staging barrier and the LDS round trip
     // (Llama-3-8B down 11.2-11.5 -> 11.0 us, 5120 x 17408 16.3-16.6 -> 13.8-14.5 us).
+    // The block-float formats rotate nothing and need no pair table, so
+    // per-lane loads leave their workgroups with no barrier before the
+    // first tile at all: 27B-shaped NVFP4 layer, o 6.4-6.6 -> 5.6 us,
+    // 16-layer stream 0.800 -> 0.764-0.773 ms.
     const bool shared = pl.threads / pl.TK > 2;
-    if (kGemvStage && shared && K <= (uint32_t)kStageFloats && passes <= 8) {
+    if (kGemvStage && Fmt::kLut && shared && K <= (uint32_t)kStageFloats && passes <= 8) {
       if (passes <= 1) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 1>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
       else if (passes <= 2) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 2>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
       else if (passes <= 4) launch_cfg<Fmt, J, R, 1, 1024, D, 1, 4>(fmt, N, nb, mask, x, 0, mode, y, 0, pl, s);
