@@ -557,6 +557,7 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
       }
     }
   } else {
+    if constexpr (Fmt::kLut) __syncthreads();   // the pair table: before this wavefront waits for its x
     // Unrotated activations are rotated per lane while the first tile's
     // loads are in flight: x' = FWHT32(D x); the 1/sqrt(32) is applied once
     // to each finished row sum instead of to every element.
@@ -585,7 +586,6 @@ __global__ __launch_bounds__(kMaxT) void gemv_kernel(Fmt fmt, uint32_t N, uint32
       load_tile(min(t + (uint32_t)(kEarly + ic.value) * G, last), ps[kEarly + ic.value]);
     });
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (Fmt::kLut) __syncthreads();   // the pair table (the only thing shared so far)
   }
   constexpr float kOutScale = kMode >= 2 ? kInvSqrt32 : 1.0f;
 
