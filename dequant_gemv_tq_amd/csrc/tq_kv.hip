@@ -238,6 +238,12 @@ __global__ __launch_bounds__(kThreads) void turbo4_decode_kernel(const uint2* __
 // sum z = sum_t 2^(s_t - m) nn_t c[idx_t] (128 floats) to the workspace.
 // --------------------------------------------------------------------------
 constexpr int kPart = kD + 2;           // floats per (sequence, head, split): m, l, z[128]
+// Query heads per cache head from which the value sums run on the matrix
+// cores (16 rows per MFMA whatever G is).  16 sequences x 4096 tokens, 32
+// query heads, per layer: G = 4 45.3 -> 39.7 us, G = 8 42.1 -> 31.8 us;
+// G = 2 55.4 against 55.8 us, and G = 1 83.6 -> 91.4 us, where most of the
+// 16 rows are padding.
+constexpr int kMfmaValueHeads = 4;
 
 template <int G, bool kBf16Q>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
@@ -408,9 +414,75 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   }
   __syncthreads();
 
-  // Values: 4 tokens per wavefront step, 16 lanes per token, 8 elements
-  // (4 bytes of nibbles) per lane.
-  {
+  // Values on the matrix cores (G >= kMfmaValueHeads): z[h][j] =
+  // sum_t w[h][t] c[idx_t][j] with w = 2^(s_t - m) nn_t is a (heads x
+  // tokens) by (tokens x 128) product, one
+  // v_mfma_f32_16x16x16f16 per 16 tokens and 16 elements (heads padded to
+  // 16 rows; the matrix cores cost the same for every G up to 16).  Lane l
+  // keeps the value loads it has: word e16 = l % 16 (elements 8 e16 .. 8 e16
+  // + 7) of tokens it * 16 + 4 wave + slot, slot = l / 16, it = 0 .. 15.  So
+  // k-group q (q = 0 .. 3) takes, from lane l, its tokens it = 4 q + e as
+  // k = 4 slot + e: the A operand (row h = l % 16, k = 4 (l / 16) + e) is
+  // w[h] of those tokens and the B operand (column n = l % 16, the same k) is
+  // centroid nibble dt of their words, so output column n of tile dt is
+  // element 8 n + dt.  Both operands are fp16: a centroid carries 11
+  // significant bits, and w is scaled by 2^sw so that the wavefront's
+  // largest norm lands just below 2^15 (w = p nn 2^sw < 2^15, no overflow;
+  // only weights more than 2^29 below the largest become fp16 subnormals);
+  // the float32 sums are scaled back by 2^-sw (exact) before they are stored.
+  if constexpr (G >= kMfmaValueHeads) {
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int copy = lane & 31;
+    const int hrow = lane & 15;
+    float nmax = 0.f;
+#pragma unroll
+    for (int it = 0; it < kChunk / 16; ++it) {
+      const uint32_t tl = (uint32_t)(it * 16 + wave * 4 + slot);
+      nmax = fmaxf(nmax, tl < n ? f16_bits_to_f32(vnr[it]) : 0.f);
+    }
+    nmax = fmaxf(nmax, xor_f(nmax, 16));
+    nmax = fmaxf(nmax, xor_f(nmax, 32));
+    int ex = 0;
+    (void)__builtin_frexpf(nmax, &ex);                       // nmax < 2^ex (0 for nmax = 0)
+    const int sw = nmax > 0.f ? 15 - ex : 0;
+    const float up = __builtin_ldexpf(1.0f, sw), down = __builtin_ldexpf(1.0f, -sw);
+    f32x4 acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int it = 4 * q + e;
+        const uint32_t tl = (uint32_t)(it * 16 + wave * 4 + slot);
+        const uint32_t tc = min(tl, n - 1u);
+        const float nn = tl < n ? f16_bits_to_f32(vnr[it]) : 0.f;
+        const float w = hrow < G ? sc[hrow < G ? hrow : 0][tc] * nn * up : 0.f;
+        a[e] = (_Float16)w;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        half4 bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = (_Float16)lut[__builtin_amdgcn_ubfe(vb[4 * q + e], 4 * dt, 4)][copy];
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bv, acc[dt], 0, 0, 0);
+      }
+    }
+    // Lane l holds heads 4 (l / 16) + r, element 8 (l % 16) + dt.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * slot + r;
+      if (h < G) {
+        float4* dst = reinterpret_cast<float4*>(&red[wave][h][8 * e16]);
+        dst[0] = make_float4(acc[0][r] * down, acc[1][r] * down, acc[2][r] * down, acc[3][r] * down);
+        dst[1] = make_float4(acc[4][r] * down, acc[5][r] * down, acc[6][r] * down, acc[7][r] * down);
+      }
+    }
+  } else {
+    // Values on the VALU: 4 tokens per wavefront step, 16 lanes per token,
+    // 8 elements (4 bytes of nibbles) per lane.
     const int copy = lane & 31;
     float z[G][8];
 #pragma unroll
