@@ -141,6 +141,31 @@ def test_attn_decode_groups_and_lengths(Hq, Hkv, qdtype):
     assert worst < 1e-4
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 4)])
+@pytest.mark.parametrize("spread", ["tiny", "large", "mixed"])
+def test_attn_decode_value_norm_range(Hq, Hkv, spread):
+    """Value sums on the matrix cores (four or more query heads per cache head) take fp16 weights scaled per
+    wavefront by a power of two: value norms of about 1e-4 everywhere, about 1e4 everywhere, and spread
+    over ten decades within one 256-token chunk stay within the bound."""
+    B, T = 2, 700
+    V = _rand((B, Hkv, T, D), 91, torch.float32)
+    if spread == "tiny":
+        V = V * 1e-5
+    elif spread == "large":
+        V = V * 1e3
+    else:
+        g = torch.Generator(device=DEV)
+        g.manual_seed(92)
+        V = V * torch.pow(10.0, torch.rand((B, Hkv, T, 1), generator=g, device=DEV) * 10.0 - 7.0)
+    K = _rand((B, Hkv, T, D), 90, torch.bfloat16)
+    kc, ks = tqa.kv_quantize_k(K)
+    vp, vn = tqa.kv_quantize_v(V.to(torch.bfloat16).contiguous())
+    q = _rand((B, Hq, D), 93, torch.bfloat16, 1.5)
+    lengths = torch.tensor([700, 301], dtype=torch.int32, device=DEV)
+    _, worst = _check_attn(q, lengths, (kc, ks, vp, vn), f"norms {spread} Hq={Hq} Hkv={Hkv}")
+    assert worst < 1e-4
+
+
 def test_attn_decode_zero_length_and_peaked_scores():
     B, T, Hq, Hkv = 3, 300, 32, 8
     kc, ks, vp, vn = _cache(B, T, Hkv, 60)
