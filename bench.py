@@ -726,6 +726,15 @@ def bench_70b(torch, tqa, wl, dev, stream, no_graph, gemv_layers=3):
         ms = _time_graph(torch, stream, lambda g=g: [tqa.gemv(*keep[i][g], xs[i][g], out=ys[g])
                                                      for i in range(len(keep))], 10, no_graph) / len(keep)
         per[g] = {"N": n, "K": k, "us": round(ms * 1e3, 2), "GB_s": round(gemv_bytes(n, k) / (ms * 1e-3) / 1e9, 1)}
+    # Kernel execution time of gate|up from the committed rocprofv3 kernel statistics (None when they were
+    # taken from other sources): in this benchmark the K = 8192 instantiation serves this matrix alone.
+    from dequant_gemv_tq_amd import profiling as tq_profiling
+    srec = tq_profiling.read_stats_record(os.path.join(ROOT, "profiles", "kernels_bench_llama8b.md"))
+    rp = srec["kernels"].get(tq_profiling.GATE_UP_70B_KERNEL) if srec else None
+    n, k = shapes["gate_up"]
+    per["gate_up"]["rocprof_kernel"] = tq_profiling.GATE_UP_70B_KERNEL
+    per["gate_up"]["rocprof_us"] = rp
+    per["gate_up"]["rocprof_frac"] = (round(gemv_bytes(n, k) / (rp * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if rp else None)
     trio_ms = _time_graph(torch, stream, lambda: [tqa.gemv(*keep[i][g], xs[i][g], out=ys[g]) for i in range(len(keep))
                                                   for g in shapes], 10, no_graph) / len(keep)
     trio_bytes = sum(gemv_bytes(n, k) for n, k in shapes.values())

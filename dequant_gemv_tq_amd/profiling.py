@@ -53,6 +53,7 @@ COPIES = 8
 COPY_BYTES = 1 << 30
 DOMINANT = ("qkv", "o", "gate_up")          # groups served by the dominant instantiation
 DOMINANT_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 1>"   # K = 4096, one row per wavefront
+GATE_UP_70B_KERNEL = "gemv_kernel<FmtTQ4, 1, 1, 1, 3, 1024, 2, 1, 2>"  # K = 8192 (Llama-3-70B gate|up in the benchmark)
 SOURCES = ("csrc/tq_gemv.hip", "csrc/tq_internal.hpp")
 
 
