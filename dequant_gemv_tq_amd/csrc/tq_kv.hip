@@ -244,6 +244,11 @@ constexpr int kPart = kD + 2;           // floats per (sequence, head, split): m
 // G = 2 55.4 against 55.8 us, and G = 1 83.6 -> 91.4 us, where most of the
 // 16 rows are padding.
 constexpr int kMfmaValueHeads = 4;
+// And from which the key scores do (v_mfma_i32_16x16x32_i8, bit-identical
+// scores): same layout, G = 8 31.9 -> 27.9 us per layer, but G = 4 39.6 ->
+// 41.6 us; the B operand needs twice the key load instructions (8-byte
+// pieces of four blocks per lane instead of 16-byte halves of one).
+constexpr int kMfmaScoreHeads = 8;
 
 template <int G, bool kBf16Q>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
@@ -256,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   __shared__ float sc[G][kChunk];                                  // scores, then 2^(s - m)
   __shared__ float red[4][G][kD];                                  // per-wavefront z partials
   __shared__ float stat[G][2];
+  __shared__ __attribute__((aligned(8))) uint16_t ksl[G >= kMfmaScoreHeads ? kChunk * 4 : 1];   // key block scales
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -282,9 +288,27 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
   const uint16_t* vnb = vnorms + kv0;
   const bool full = n == (uint32_t)kChunk;
   const uint32_t ck = (uint32_t)(wave * 8 + (lane >> 3)), cv = (uint32_t)(wave * 4 + slot);
-  uint4 kq[kChunk / 32];
-  uint32_t kscl[kChunk / 32], vb[kChunk / 16], vnr[kChunk / 16];
-  if (full) {
+  // Scores on the int8 matrix cores (G >= kMfmaScoreHeads): wavefront w takes
+  // tokens 64 w + 16 tg + l % 16 (tg = 0 .. 3); lane l loads bytes 8 (l / 16)
+  // .. + 7 of each of the token's four q8_0 blocks (the MFMA B operand), and
+  // the chunk's block scales go through LDS (they are only 2-byte aligned).
+  constexpr bool kMS = G >= kMfmaScoreHeads;
+  constexpr int kKq = kMS ? 1 : kChunk / 32;
+  uint4 kq[kKq];
+  uint32_t kscl[kKq], vb[kChunk / 16], vnr[kChunk / 16];
+  uint2 km[kMS ? 16 : 1];
+  uint32_t ksr[kMS ? 4 : 1];
+  if constexpr (kMS) {
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const uint32_t tl = min((uint32_t)(wave * 64 + tg * 16 + e16), n - 1u);
+      const uint2* kr = reinterpret_cast<const uint2*>(kb + tl * 8);
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) km[tg * 4 + bk] = kr[4 * bk + slot];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ksr[j] = ksb[min((uint32_t)(tid + kThreads * j), 4u * n - 1u)];
+  } else if (full) {
 #pragma unroll
     for (int it = 0; it < kChunk / 32; ++it) {
       const uint32_t tl = (uint32_t)(it * 32) + ck;
@@ -352,10 +376,51 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     if ((tid & 3) == 0) dq[h][(tid & 15) >> 2] = d;
   }
   for (int i = tid; i < 16 * 32; i += kThreads) lut[i >> 5][i & 31] = cb.c[i >> 5];
+  if constexpr (kMS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ksl[tid + kThreads * j] = (uint16_t)ksr[j];
+  }
   __syncthreads();
 
-  // Scores: 8 lanes per token, 16 key bytes per lane (half a q8_0 block).
-  {
+  if constexpr (kMS) {
+    // One v_mfma_i32_16x16x32_i8 per q8_0 block and 16 tokens: A = the
+    // quantized query (row h = l % 16, zero past G; bytes 32 b + 8 (l / 16)
+    // .. + 7), B = the keys; the exact integer dot of block b for head
+    // 4 (l / 16) + r and token l % 16 lands in lane l, register r, and is
+    // scaled and summed over the blocks as ((f0 + f1) + (f2 + f3)), the
+    // order of the VALU version, so the scores are the same bit for bit.
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const float scale = kLog2e * 0.08838834764831845f;     // log2(e) / sqrt(128), float32
+    const int hrow = lane & 15;
+    long qa[4];
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk)
+      qa[bk] = hrow < G ? *reinterpret_cast<const long*>(&qs[hrow < G ? hrow : 0][32 * bk + 8 * slot]) : 0l;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const uint32_t tl = (uint32_t)(wave * 64 + tg * 16 + e16);
+      const uint2 sr = *reinterpret_cast<const uint2*>(&ksl[4 * tl]);
+      const float dk[4] = {f16_bits_to_f32(sr.x & 0xffffu), f16_bits_to_f32(sr.x >> 16),
+                           f16_bits_to_f32(sr.y & 0xffffu), f16_bits_to_f32(sr.y >> 16)};
+      i32x4 c[4];
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+        c[bk] = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa[bk], __builtin_bit_cast(long, km[tg * 4 + bk]),
+                                                      i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * slot + r;
+        if (h < G) {
+          float f[4];
+#pragma unroll
+          for (int bk = 0; bk < 4; ++bk) f[bk] = (float)c[bk][r] * (dk[bk] * dq[h][bk]);
+          sc[h][tl] = ((f[0] + f[1]) + (f[2] + f[3])) * scale;
+        }
+      }
+    }
+  } else {
+    // Scores on the VALU: 8 lanes per token, 16 key bytes per lane (half a
+    // q8_0 block).
     const float scale = kLog2e * 0.08838834764831845f;     // log2(e) / sqrt(128), float32
     uint4 qc[G];
     float dqs[G];
