@@ -153,7 +153,10 @@ tq_status tq_rotate(const void* x, tq_dtype xt, int64_t M, int64_t K, int64_t ld
  *                or TQ_BF16 as tq_rotate rounds it: the product is then
  *                exact for that rounded x'); otherwise it is the raw
  *                activation (TQ_F32 or TQ_BF16) and the kernel rotates it
- *                itself (sign_mask used).
+ *                itself (sign_mask used; the +-1 products are exact and only
+ *                the float32 sums of the rotation round, whether they run as
+ *                butterflies or, for a bf16 x with K in (10240, 32768], on
+ *                the matrix cores).
  *   y            [N] float32 (output).
  * Limits: K <= 131072.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EALIGN (x 16-byte
  * aligned, y 4-byte aligned), TQ_EDTYPE. */
@@ -367,7 +370,10 @@ size_t tq_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t T_max);
  * The query is quantized per 32-element block (scale fl(amax / 127) in
  * float32, codes as tq_kv_quantize_k) so each key block's dot product is an
  * exact integer; values are summed in the rotated domain and rotated back
- * once per head.
+ * once per head.  With G >= 4 the value sums run on the matrix cores with
+ * fp16 operands (the centroid, and the weight 2^(s - m) * norm scaled by a
+ * power of two per wavefront so that it cannot overflow): each product
+ * carries at most about 2^-11 relative error before the float32 sums.
  *   q        [B, Hq, 128] TQ_BF16 or TQ_F32, 16-byte aligned.
  *   lengths  int32 [B] device, each clamped to [0, T_max] (0 gives o = 0).
  *   k_codes  int8 [B, Hkv, T_max, 128], k_scales fp16 [B, Hkv, T_max, 4]
